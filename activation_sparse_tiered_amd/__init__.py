@@ -1,0 +1,176 @@
+"""Python binding of libspax: three-tier activation-sparse decoding GEMV on MI355X (gfx950).
+
+Thin argument marshalling over the C ABI in ``include/spax.h``: every step of the path
+(packing, tier masks, tiered GEMV, decode step) runs in the HIP kernels of libspax.so.
+torch is used only for device memory (tensors are passed by ``data_ptr()``) and streams
+(``torch.cuda.current_stream()`` by default).  The names match the C entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+
+from ._lib import (FMT_FP16, FMT_INT4, MAX_DIN, MAX_MATS, MODE_THRESHOLD, MODE_TOPK,  # noqa: F401
+                   MODE_TOPK_GUIDED, TIER_APPROX, TIER_FULL, TIER_SKIP, Layout, Phase,
+                   SpaxError, Step, TierParams, check, lib, LIB_PATH)
+
+__all__ = [
+    "spax_layout_init", "spax_pack_columns", "spax_build_tiers", "spax_gemv_workspace_bytes",
+    "spax_tiered_gemv", "spax_step_workspace_bytes", "spax_decode_step_projections",
+    "spax_key_threshold", "spax_counts_from_fractions", "spax_guided_bounds", "spax_version",
+    "topk_params", "threshold_params", "guided_params", "make_phase", "Layout", "TierParams",
+    "Phase", "Step", "SpaxError", "LIB_PATH",
+]
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------ layout / pack
+
+def spax_layout_init(d_in: int, d_out, base_fmt: int = FMT_FP16, base_group: int = 128,
+                     approx_group: int = 128) -> Layout:
+    d_out = [int(v) for v in d_out]
+    L = Layout()
+    L.n_mats = len(d_out)
+    L.d_in = int(d_in)
+    for m, v in enumerate(d_out[:MAX_MATS]):
+        L.d_out[m] = v
+    L.base_fmt = int(base_fmt)
+    L.base_group = int(base_group)
+    L.approx_group = int(approx_group)
+    if len(d_out) > MAX_MATS:
+        L.n_mats = len(d_out)   # rejected by the library
+    check(lib.spax_layout_init(C.byref(L)), "spax_layout_init")
+    return L
+
+
+def spax_pack_columns(layout: Layout, Ws, packed, stream=None) -> None:
+    arr = (C.c_void_p * max(1, len(Ws)))(*[_ptr(w) for w in Ws])
+    check(lib.spax_pack_columns(C.byref(layout), arr, _ptr(packed), _stream(stream)),
+          "spax_pack_columns")
+
+
+# ------------------------------------------------------------------ tier masks
+
+def topk_params(n_full: int, n_approx: int) -> TierParams:
+    p = TierParams()
+    p.mode, p.n_full, p.n_approx = MODE_TOPK, int(n_full), int(n_approx)
+    p.approx_den = 1
+    return p
+
+
+def threshold_params(tau_skip: float, tau_full: float) -> TierParams:
+    p = TierParams()
+    p.mode, p.tau_skip, p.tau_full = MODE_THRESHOLD, float(tau_skip), float(tau_full)
+    p.approx_den = 1
+    return p
+
+
+def guided_params(tau: float, n_skip_lo: int, n_skip_hi: int, approx_num: int,
+                  approx_den: int) -> TierParams:
+    p = TierParams()
+    p.mode, p.tau = MODE_TOPK_GUIDED, float(tau)
+    p.n_skip_lo, p.n_skip_hi = int(n_skip_lo), int(n_skip_hi)
+    p.approx_num, p.approx_den = int(approx_num), int(approx_den)
+    return p
+
+
+def spax_build_tiers(x, d_in: int, params: TierParams, tier, full_idx, approx_idx, counts,
+                     stream=None) -> None:
+    check(lib.spax_build_tiers(_ptr(x), int(d_in), C.byref(params), _ptr(tier), _ptr(full_idx),
+                               _ptr(approx_idx), _ptr(counts), _stream(stream)),
+          "spax_build_tiers")
+
+
+# ------------------------------------------------------------------ GEMV
+
+def spax_gemv_workspace_bytes(layout: Layout) -> int:
+    return int(lib.spax_gemv_workspace_bytes(C.byref(layout)))
+
+
+def spax_tiered_gemv(layout: Layout, packed, x, full_idx, approx_idx, counts, y, ws,
+                     ws_bytes: int | None = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    check(lib.spax_tiered_gemv(C.byref(layout), _ptr(packed), _ptr(x), _ptr(full_idx),
+                               _ptr(approx_idx), _ptr(counts), _ptr(y), _ptr(ws), int(ws_bytes),
+                               _stream(stream)),
+          "spax_tiered_gemv")
+
+
+# ------------------------------------------------------------------ decode step
+
+def make_phase(layout: Layout, packed, x, params: TierParams, tier, full_idx, approx_idx,
+               counts, y) -> Phase:
+    ph = Phase()
+    ph.layout = C.pointer(layout)
+    ph.packed, ph.x = _ptr(packed), _ptr(x)
+    ph.params = params
+    ph.tier, ph.full_idx, ph.approx_idx = _ptr(tier), _ptr(full_idx), _ptr(approx_idx)
+    ph.counts, ph.y = _ptr(counts), _ptr(y)
+    ph._keep = (layout,)  # keep the layout alive as long as the phase
+    return ph
+
+
+def phase_array(phases):
+    arr = (Phase * len(phases))(*phases)
+    return arr
+
+
+def spax_step_workspace_bytes(phases) -> int:
+    arr = phases if isinstance(phases, C.Array) else phase_array(phases)
+    return int(lib.spax_step_workspace_bytes(arr, len(arr)))
+
+
+def spax_decode_step_projections(phases, ws, ws_bytes: int | None = None, flags: int = 0,
+                                 stream=None) -> None:
+    arr = phases if isinstance(phases, C.Array) else phase_array(phases)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    st = Step()
+    st.n_phases = len(arr)
+    st.flags = int(flags)
+    st.phases = C.cast(arr, C.POINTER(Phase))
+    st.ws = _ptr(ws)
+    st.ws_bytes = int(ws_bytes)
+    check(lib.spax_decode_step_projections(C.byref(st), _stream(stream)),
+          "spax_decode_step_projections")
+
+
+# ------------------------------------------------------------------ host helpers
+
+def spax_key_threshold(tau: float) -> int:
+    return int(lib.spax_key_threshold(float(tau)))
+
+
+def spax_counts_from_fractions(d: int, p_full: float, p_approx: float):
+    a, b = C.c_int32(), C.c_int32()
+    check(lib.spax_counts_from_fractions(int(d), float(p_full), float(p_approx), C.byref(a),
+                                         C.byref(b)), "spax_counts_from_fractions")
+    return int(a.value), int(b.value)
+
+
+def spax_guided_bounds(d: int, s: float, delta: float):
+    a, b = C.c_int32(), C.c_int32()
+    check(lib.spax_guided_bounds(int(d), float(s), float(delta), C.byref(a), C.byref(b)),
+          "spax_guided_bounds")
+    return int(a.value), int(b.value)
+
+
+def spax_version() -> str:
+    return lib.spax_version().decode()

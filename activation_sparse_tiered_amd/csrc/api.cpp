@@ -1,0 +1,141 @@
+// Entry points of libspax: argument validation, then kernel launches.
+// Every check runs before anything is enqueued; on error no output is touched.
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+using namespace spax;
+
+namespace {
+
+// Prefix the current thread-local message with the phase number.
+int phase_fail(int st, int i) {
+  char msg[400];
+  snprintf(msg, sizeof(msg), "%s", spax_last_error());
+  return fail(st, "phase %d: %s", i, msg);
+}
+
+int check_tier_outputs(const uint16_t* x, int32_t d_in, const int32_t* full_idx,
+                       const int32_t* approx_idx, const int32_t* counts) {
+  if (!x || !full_idx || !approx_idx || !counts)
+    return fail(SPAX_ERR_NULL, "x, full_idx, approx_idx and counts are required");
+  if (d_in < 1 || d_in > SPAX_MAX_DIN)
+    return fail(SPAX_ERR_SHAPE, "d_in %d outside 1..%d", d_in, SPAX_MAX_DIN);
+  if (!aligned(x, 4) || !aligned(full_idx, 4) || !aligned(approx_idx, 4) || !aligned(counts, 4))
+    return fail(SPAX_ERR_ALIGN, "x, lists and counts must be 4-byte aligned");
+  return SPAX_OK;
+}
+
+int check_gemv_args(const spax_layout* L, const void* packed, const uint16_t* x,
+                    const int32_t* full_idx, const int32_t* approx_idx, const int32_t* counts,
+                    const float* y, const void* ws, size_t ws_bytes, GemvPlan* plan) {
+  if (!L) return fail(SPAX_ERR_NULL, "layout is NULL");
+  if (!layout_ok(L)) return fail(SPAX_ERR_SHAPE, "layout not initialised by spax_layout_init");
+  if (!packed || !x || !full_idx || !approx_idx || !counts || !y)
+    return fail(SPAX_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(packed, 256) || !aligned(ws, 256))
+    return fail(SPAX_ERR_ALIGN, "packed and ws must be 256-byte aligned");
+  if (!aligned(x, 4) || !aligned(full_idx, 4) || !aligned(approx_idx, 4) || !aligned(counts, 4) ||
+      !aligned(y, 16))
+    return fail(SPAX_ERR_ALIGN, "x/lists/counts must be 4-byte aligned and y 16-byte aligned");
+  *plan = gemv_plan(L);
+  if (plan->ws_bytes > 0 && !ws) return fail(SPAX_ERR_NULL, "workspace is NULL");
+  if (ws_bytes < plan->ws_bytes)
+    return fail(SPAX_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, plan->ws_bytes);
+  return SPAX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spax_pack_columns(const spax_layout* L, const uint16_t* const* W, void* packed,
+                      hipStream_t stream) {
+  clear_error();
+  if (!L || !W || !packed) return fail(SPAX_ERR_NULL, "layout, W and packed are required");
+  if (!layout_ok(L)) return fail(SPAX_ERR_SHAPE, "layout not initialised by spax_layout_init");
+  if (!aligned(packed, 256)) return fail(SPAX_ERR_ALIGN, "packed must be 256-byte aligned");
+  for (int m = 0; m < L->n_mats; ++m) {
+    if (!W[m]) return fail(SPAX_ERR_NULL, "W[%d] is NULL", m);
+    if (!aligned(W[m], 16)) return fail(SPAX_ERR_ALIGN, "W[%d] must be 16-byte aligned", m);
+  }
+  return launch_pack(L, W, packed, stream);
+}
+
+int spax_build_tiers(const uint16_t* x, int32_t d_in, const spax_tier_params* p, uint8_t* tier,
+                     int32_t* full_idx, int32_t* approx_idx, int32_t* counts, hipStream_t stream) {
+  clear_error();
+  int st = check_tier_outputs(x, d_in, full_idx, approx_idx, counts);
+  if (st) return st;
+  TierArgs a;
+  st = tier_args_from_params(p, d_in, &a);
+  if (st) return st;
+  return launch_build_tiers(a, x, tier, full_idx, approx_idx, counts, nullptr, 0, stream);
+}
+
+size_t spax_gemv_workspace_bytes(const spax_layout* L) {
+  if (!layout_ok(L)) return 0;
+  return gemv_plan(L).ws_bytes;
+}
+
+int spax_tiered_gemv(const spax_layout* L, const void* packed, const uint16_t* x,
+                     const int32_t* full_idx, const int32_t* approx_idx, const int32_t* counts,
+                     float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  GemvPlan plan;
+  int st = check_gemv_args(L, packed, x, full_idx, approx_idx, counts, y, ws, ws_bytes, &plan);
+  if (st) return st;
+  return launch_tiered_gemv(L, plan, packed, x, full_idx, approx_idx, counts, y, false, stream);
+}
+
+size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases) {
+  if (!phases || n_phases < 1) return 0;
+  size_t mx = 0;
+  for (int i = 0; i < n_phases; ++i) {
+    if (!layout_ok(phases[i].layout)) return 0;
+    const size_t b = gemv_plan(phases[i].layout).ws_bytes;
+    if (b > mx) mx = b;
+  }
+  return mx;
+}
+
+int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
+  clear_error();
+  if (!step || !step->phases) return fail(SPAX_ERR_NULL, "step and step->phases are required");
+  if (step->n_phases < 1) return fail(SPAX_ERR_SHAPE, "n_phases %d < 1", step->n_phases);
+  if (step->flags != SPAX_STEP_DEFAULT) return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags");
+  // Validate every phase before enqueueing anything.
+  for (int i = 0; i < step->n_phases; ++i) {
+    const spax_phase& ph = step->phases[i];
+    if (!ph.layout) return fail(SPAX_ERR_NULL, "phase %d: layout is NULL", i);
+    int st = check_tier_outputs(ph.x, ph.layout->d_in, ph.full_idx, ph.approx_idx, ph.counts);
+    if (st) return phase_fail(st, i);
+    TierArgs a;
+    st = tier_args_from_params(&ph.params, ph.layout->d_in, &a);
+    if (st) return phase_fail(st, i);
+    GemvPlan plan;
+    st = check_gemv_args(ph.layout, ph.packed, ph.x, ph.full_idx, ph.approx_idx, ph.counts, ph.y,
+                         step->ws, step->ws_bytes, &plan);
+    if (st) return phase_fail(st, i);
+  }
+  for (int i = 0; i < step->n_phases; ++i) {
+    const spax_phase& ph = step->phases[i];
+    TierArgs a;
+    tier_args_from_params(&ph.params, ph.layout->d_in, &a);
+    const GemvPlan plan = gemv_plan(ph.layout);
+    // The mask kernel also clears y when the GEMV accumulates it with atomics (small y only:
+    // one workgroup does the clearing).
+    const bool clear_in_mask = plan.n_chunks > 1 && ph.layout->d_out_total <= kMaskClearMax;
+    int st = launch_build_tiers(a, ph.x, ph.tier, ph.full_idx, ph.approx_idx, ph.counts,
+                                clear_in_mask ? ph.y : nullptr,
+                                clear_in_mask ? ph.layout->d_out_total : 0, stream);
+    if (st) return st;
+    st = launch_tiered_gemv(ph.layout, plan, ph.packed, ph.x, ph.full_idx, ph.approx_idx,
+                            ph.counts, ph.y, clear_in_mask, stream);
+    if (st) return st;
+  }
+  return SPAX_OK;
+}
+
+}  // extern "C"

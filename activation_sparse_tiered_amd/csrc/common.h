@@ -1,0 +1,76 @@
+// Internal declarations shared by the libspax translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "spax.h"
+
+namespace spax {
+
+// ------------------------------------------------------------------ errors
+// Record a thread-local message and return the status.
+int fail(int status, const char* fmt, ...);
+void clear_error();
+int hip_fail(hipError_t e, const char* what);
+
+#define SPAX_HIP_CHECK(expr)                                   \
+  do {                                                         \
+    hipError_t e_ = (expr);                                    \
+    if (e_ != hipSuccess) return ::spax::hip_fail(e_, #expr);  \
+  } while (0)
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ------------------------------------------------------------------ layout
+// True if *L has been through spax_layout_init (derived fields consistent).
+bool layout_ok(const spax_layout* L);
+
+// ------------------------------------------------------------------ tier mask
+// Tier parameters after host-side conversion: everything is integer on the device.
+struct TierArgs {
+  int32_t mode;
+  int32_t d;
+  int32_t n_full, n_approx;   // TOPK
+  int32_t k_skip, k_full;     // THRESHOLD key thresholds
+  int32_t k_tau;              // TOPK_GUIDED key threshold
+  int32_t n_lo, n_hi, num, den;
+};
+
+// Validate *p against d and convert float thresholds to keys.
+int tier_args_from_params(const spax_tier_params* p, int32_t d, TierArgs* out);
+
+// y_zero/n_zero: an fp32 buffer the mask kernel also clears (NULL/0: none).
+int launch_build_tiers(const TierArgs& a, const uint16_t* x, uint8_t* tier, int32_t* full_idx,
+                       int32_t* approx_idx, int32_t* counts, float* y_zero, int64_t n_zero,
+                       hipStream_t s);
+
+// ------------------------------------------------------------------ pack
+int launch_pack(const spax_layout* L, const uint16_t* const* W, void* packed, hipStream_t s);
+
+// ------------------------------------------------------------------ gemv
+constexpr int kTileRows = 512;       // rows per workgroup tile (64 lanes x 8 rows)
+constexpr int kGemvThreads = 512;    // 8 waves share one tile, split the columns
+constexpr int64_t kMaxRowsTotal = (int64_t)1 << 24;  // largest d_out_total of a layout
+
+struct GemvPlan {
+  int32_t n_tiles;   // ceil(d_out_total / kTileRows)
+  int32_t n_chunks;  // split-K factor over the selected column lists
+  size_t ws_bytes;   // workspace the launch needs (currently none)
+};
+GemvPlan gemv_plan(const spax_layout* L);
+
+int launch_zero_f32(float* y, int64_t n, hipStream_t s);
+
+// Largest y the single-workgroup mask kernel clears on the side.
+constexpr int64_t kMaskClearMax = 65536;
+
+// y_zeroed: y already holds zeros (stream-ordered); otherwise a zero fill is enqueued first
+// whenever the plan splits K.
+int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* packed,
+                       const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
+                       const int32_t* counts, float* y, bool y_zeroed, hipStream_t s);
+
+}  // namespace spax

@@ -1,0 +1,272 @@
+"""Benchmark: one batch-one decode step over all projections of a 32-layer 7B-shaped decoder.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sparsity 0.5] [--no-cpu-baseline]
+
+A step is one token: for each of 32 layers and each projection group (q|k|v, o, gate|up,
+down) one TopK-Guided tier mask (s +- 0.01, approximate tier = 3/10 of the kept channels,
+two-bit groups of 128 rows) and one tiered GEMV over the fused fp16 matrices, in order.
+Weights are synthetic (fp16 N(0, 0.02), drawn on the device from a seed) and packed by
+spax_pack_columns before timing; activations are seeded Laplace(0, 1) vectors, one per
+(token, layer, group), resident in HBM before the timed region.
+
+Prints one JSON line.  ``value`` is microseconds per token (lower is better).  The
+``roofline`` object is for the tiered GEMV kernel (the dominant kernel): algorithmic bytes
+= selected column records + activations + index lists + y, per launch, over the kernel's
+average duration measured with HIP events on the launch stream.  ``cpu_baseline`` times the
+oracle (float64 NumPy) on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "tiered sparse GEMV µs/token (7B projections); achieved GB/s vs HBM peak"
+HBM_PEAK_GBS = 8000.0
+SEED = 20261003
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--sparsity", type=float, default=0.5)
+    ap.add_argument("--delta", type=float, default=0.01)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--tokens", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=6,
+                    help="layers of one token the oracle runs for the CPU baseline")
+    return ap.parse_args()
+
+
+class Stack:
+    """Packed weights, per-token activations and per-phase output buffers on the device."""
+
+    def __init__(self, spax, torch, dev, layers, tokens, s, delta):
+        self.spax, self.torch, self.dev = spax, torch, dev
+        self.shapes = synth.decoder_phases_7b()
+        self.layers, self.tokens = layers, tokens
+        self.layouts, self.packed, self.params, self.bufs = [], [], [], []
+        t0 = time.time()
+        for l in range(layers):
+            for k, (name, d_in, d_out) in enumerate(self.shapes):
+                L = spax.spax_layout_init(d_in, d_out, spax.FMT_FP16, 128, 128)
+                packed = torch.empty(int(L.total_bytes), dtype=torch.uint8, device=dev)
+                Ws = [synth.weights_device(SEED, d_in, r, dev, l, k, m) for m, r in enumerate(d_out)]
+                spax.spax_pack_columns(L, Ws, packed)
+                del Ws
+                lo, hi = spax.spax_guided_bounds(d_in, s, delta)
+                p = spax.guided_params(-math.log(1.0 - s), lo, hi, 3, 10)
+                T = int(L.d_out_total)
+                self.layouts.append(L)
+                self.packed.append(packed)
+                self.params.append(p)
+                self.bufs.append(dict(
+                    tier=torch.empty(d_in, dtype=torch.uint8, device=dev),
+                    f=torch.empty(d_in, dtype=torch.int32, device=dev),
+                    a=torch.empty(d_in, dtype=torch.int32, device=dev),
+                    c=torch.zeros(3, dtype=torch.int32, device=dev),
+                    y=torch.empty(T, dtype=torch.float32, device=dev)))
+        torch.cuda.synchronize()
+        log(f"[bench] packed {layers} layers in {time.time() - t0:.1f} s, "
+            f"{sum(int(L.total_bytes) for L in self.layouts) / 1e9:.2f} GB")
+        # activations: one fp16 vector per (token, layer, group)
+        self.x = []
+        for t in range(tokens):
+            row = []
+            for l in range(layers):
+                for k, (name, d_in, d_out) in enumerate(self.shapes):
+                    row.append(torch.from_numpy(synth.activations(SEED, d_in, t, l, k)).to(dev))
+            self.x.append(row)
+        self.phase_arrays = []
+        for t in range(tokens):
+            ph = [spax.make_phase(L, pk, x, p, b["tier"], b["f"], b["a"], b["c"], b["y"])
+                  for L, pk, x, p, b in zip(self.layouts, self.packed, self.x[t], self.params, self.bufs)]
+            self.phase_arrays.append(spax.phase_array(ph))
+        self.ws = torch.zeros(spax.spax_step_workspace_bytes(self.phase_arrays[0]),
+                              dtype=torch.uint8, device=dev)
+
+    def step(self, t):
+        self.spax.spax_decode_step_projections(self.phase_arrays[t % self.tokens], self.ws)
+
+    def algorithmic_bytes(self, i, counts):
+        """Bytes the GEMV of phase i must read/write for a mask with these counts."""
+        L = self.layouts[i]
+        nF, nA = int(counts[0]), int(counts[1])
+        return (nF * int(L.rec_F) + nA * int(L.rec_A) + 2 * int(L.d_in) + 4 * (nF + nA)
+                + 4 * int(L.d_out_total))
+
+    def timed_kernels(self, t):
+        """The same step as separate mask / GEMV launches with events around each GEMV."""
+        torch, spax = self.torch, self.spax
+        evs = []
+        for i, (L, pk, p, b) in enumerate(zip(self.layouts, self.packed, self.params, self.bufs)):
+            x = self.x[t % self.tokens][i]
+            spax.spax_build_tiers(x, int(L.d_in), p, b["tier"], b["f"], b["a"], b["c"])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            spax.spax_tiered_gemv(L, pk, x, b["f"], b["a"], b["c"], b["y"], self.ws)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        counts = [b["c"].cpu().numpy() for b in self.bufs]
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        return ms, counts
+
+
+def cpu_baseline(stack, layers, s, delta):
+    """The oracle on `layers` layers of token 0, timed on the host, scaled to one token."""
+    from oracle import gemv as ogemv
+    from oracle import pack as opack
+    from oracle import tiers as otiers
+    torch = stack.torch
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover
+        limiter = None
+    phases = []
+    for l in range(layers):
+        for k, (name, d_in, d_out) in enumerate(stack.shapes):
+            Ws = [synth.weights_device(SEED, d_in, r, stack.dev, l, k, m).cpu().numpy()
+                  for m, r in enumerate(d_out)]
+            phases.append((opack.Layout(d_in, d_out, 0, 128, 128), Ws,
+                           synth.activations(SEED, d_in, 0, l, k)))
+    n_lo_hi = {}
+    t0 = time.perf_counter()
+    for O, Ws, x in phases:
+        d = O.d_in
+        if d not in n_lo_hi:
+            n_lo_hi[d] = otiers.guided_bounds(d, s, delta)
+        lo, hi = n_lo_hi[d]
+        _, f, a, _ = otiers.build_tiers(x, otiers.MODE_TOPK_GUIDED, tau=-math.log(1 - s),
+                                        n_lo=lo, n_hi=hi, num=3, den=10)
+        ogemv.tiered_gemv(O, Ws, x, f, a)
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    per_token_us = dt / layers * stack.layers * 1e6
+    return {"value": round(per_token_us, 1), "unit": "us/token", "cores": cores, "kind": "oracle",
+            "sample": f"{layers} of {stack.layers} layers (4 projection groups each) of one token: "
+                      f"float64 NumPy tier mask + tiered GEMV, scaled x{stack.layers / layers:g}; "
+                      f"{dt:.1f} s measured; BLAS threads = cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the path shards by "
+                                   "output rows across GPUs but no multi-GPU run is built",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import activation_sparse_tiered_amd as spax
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s, delta = args.sparsity, args.delta
+    stack = Stack(spax, torch, dev, args.layers, args.tokens, s, delta)
+
+    # ---- warmup, then exactly `steps` timed decode steps
+    for t in range(args.warmup):
+        stack.step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for t in range(args.steps):
+        stack.step(args.warmup + t)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    step_ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] decode step: {step_ms * 1e3:.1f} us/token (event), wall {wall_ms / args.steps:.3f} ms/step")
+
+    # ---- per-kernel timing of the tiered GEMV over the same steps
+    tot_bytes, tot_ms, n_launch, sel_bytes_tok = 0, 0.0, 0, []
+    per_phase = {}
+    for t in range(args.steps):
+        ms, counts = stack.timed_kernels(args.warmup + t)
+        tok_bytes = 0
+        for i, (m, c) in enumerate(zip(ms, counts)):
+            b = stack.algorithmic_bytes(i, c)
+            tot_bytes += b
+            tot_ms += m
+            n_launch += 1
+            tok_bytes += b
+            name = stack.shapes[i % 4][0]
+            pb = per_phase.setdefault(name, [0, 0.0, 0])
+            pb[0] += b
+            pb[1] += m
+            pb[2] += 1
+        sel_bytes_tok.append(tok_bytes)
+    avg_ms = tot_ms / n_launch
+    avg_bytes = tot_bytes / n_launch
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+    for name, (b, m, n) in per_phase.items():
+        log(f"[bench]   gemv {name:7s}: {m / n * 1e3:7.2f} us avg, {b / n / 1e6:7.2f} MB, "
+            f"{b / (m * 1e-3) / 1e9:7.1f} GB/s")
+    log(f"[bench] gemv avg {avg_ms * 1e3:.2f} us/launch, {avg_bytes / 1e6:.2f} MB/launch, "
+        f"{achieved:.1f} GB/s; sum of gemv time per token {tot_ms / args.steps * 1e3:.1f} us; "
+        f"selected bytes/token {np.mean(sel_bytes_tok) / 1e9:.3f} GB")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(stack, min(args.cpu_layers, args.layers), s, delta)
+        log(f"[bench] cpu baseline {cpu}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_ms * 1e3, 2),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode7b: {args.layers} layers x (q|k|v 4096->3x4096, o 4096->4096, "
+                        f"gate|up 4096->2x11008, down 11008->4096), fp16 weights, "
+                        f"TopK-Guided mask s={s}+-{delta}, approx tier 3/10 of kept, 2-bit G=128, "
+                        f"batch 1, layer-serial",
+            "sparsity": s, "layers": args.layers, "tokens": args.tokens,
+            "selected_GB_per_token": round(float(np.mean(sel_bytes_tok)) / 1e9, 4),
+            "effective_GBps_per_token": round(float(np.mean(sel_bytes_tok)) / (step_ms * 1e-3) / 1e9, 1),
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "tiered_gemv_kernel<fp16>",
+                     "avg_launch_us": round(avg_ms * 1e3, 3),
+                     "avg_algorithmic_MB": round(avg_bytes / 1e6, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+/*
+ * spax.h -- C ABI of libspax: three-tier activation-sparse decoding GEMV on gfx950.
+ *
+ * What the library computes (batch-one decoding, one activation vector per call):
+ *
+ *   SpAx, "Activation Sparsity with Weight Approximation for Faster LLM Decoding on
+ *   Offloaded Weights" (arXiv:2610.02598), Abstract: each weight is read in its original
+ *   form, read from a compressed approximation, or not read; activations closest to zero
+ *   skip their weights, smaller-magnitude ones read the approximation, the largest read
+ *   the original.  The eigenradar commentary on SpAx ("The route outside GPU memory",
+ *   first and third paragraphs) makes the unit one weight column per input channel, the
+ *   approximation two-bit, and stores jointly accessed columns together.
+ *
+ *   TopK-Guided (arXiv:2610.01763), section 2.1 "TopK-Guided Masking": the tier mask may
+ *   be a TopK, a threshold, or a threshold estimate clipped to +-delta around the target
+ *   followed by TopK.
+ *
+ *   y[r] = sum_{j in FULL} x[j] * W[r][j]  +  sum_{j in APPROX} x[j] * What[r][j]
+ *
+ * Conventions shared by every entry point:
+ *   - Return SPAX_OK (0) or a negative spax_status.  All argument validation happens on
+ *     the host before anything is enqueued; on error nothing runs and no output buffer
+ *     is touched.  spax_last_error() then holds a thread-local message.
+ *   - "device pointer" means memory the GPU can address (hipMalloc).  The caller owns
+ *     every buffer; the library never allocates device memory in these calls.
+ *   - Work is enqueued on the given HIP stream and is asynchronous unless stated.
+ *   - fp16 values are passed as uint16_t bit patterns; y is fp32.
+ *   - No exceptions cross this boundary.
+ */
+#ifndef SPAX_H
+#define SPAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+typedef enum spax_status {
+  SPAX_OK = 0,
+  SPAX_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  SPAX_ERR_SHAPE = -2,       /* layout sizes not supported (see spax_layout_init)    */
+  SPAX_ERR_PARAM = -3,       /* tier parameters out of range                         */
+  SPAX_ERR_ALIGN = -4,       /* a pointer is not aligned as required                 */
+  SPAX_ERR_WORKSPACE = -5,   /* workspace too small                                  */
+  SPAX_ERR_HIP = -6,         /* a HIP runtime call failed (message has the details)  */
+  SPAX_ERR_UNSUPPORTED = -7  /* valid request this build does not implement          */
+} spax_status;
+
+/* ---------------------------------------------------------------- packed layout */
+enum { SPAX_FMT_FP16 = 0, SPAX_FMT_INT4 = 1 };
+
+#define SPAX_MAX_MATS 4
+#define SPAX_MAX_DIN 32768     /* largest input vector one tier-mask workgroup holds */
+#define SPAX_RECORD_ALIGN 128  /* column records are padded to one 128-byte line     */
+
+/*
+ * spax_layout: shape and byte layout of one packed weight blob.
+ *
+ * Pages: eigenradar commentary on SpAx, "The route outside GPU memory", third
+ * paragraph (jointly accessed columns are placed together).  Matrices that multiply the
+ * same activation vector (q|k|v, gate|up) are fused: the record of input channel j holds
+ * column j of every matrix, concatenated along rows (matrix 0 rows first).
+ *
+ * Blob = region F (original tier) then region A (two-bit approximation); both are
+ * column-major with one record per input channel, in channel order, each record
+ * zero-padded to a multiple of 128 bytes:
+ *   region F, record j at  j * stride_F:
+ *     FP16: d_out_total fp16 values (little endian);
+ *     INT4: d_out_total/2 bytes of codes (row 2k in bits [3:0], row 2k+1 in [7:4]) then
+ *           d_out_total/base_group u32 words, fp16 scale in bits [15:0], fp16 zero in
+ *           bits [31:16];
+ *   region A, record j at  off_A + j * stride_A:
+ *     d_out_total/4 bytes of two-bit codes (row 4k+i in bits [2i+1:2i]) then
+ *     d_out_total/approx_group (scale, zero) u32 words as above.
+ * A group of G rows reconstructs as w_hat = s*q + z (z = group minimum, s = (max-min)/L,
+ * q = round-half-even((w - z)/s) clamped to [0, L], L = 3 for two-bit, 15 for int4;
+ * every step in fp32 with round-to-nearest-even, s and z rounded to fp16).
+ *
+ * The caller fills the input fields; spax_layout_init fills the derived ones.
+ */
+typedef struct spax_layout {
+  /* inputs */
+  int32_t n_mats;                /* 1..SPAX_MAX_MATS matrices sharing one input       */
+  int32_t d_in;                  /* input channels = columns, 1..SPAX_MAX_DIN          */
+  int32_t d_out[SPAX_MAX_MATS];  /* rows of each matrix; each a multiple of every group */
+  int32_t base_fmt;              /* SPAX_FMT_FP16 or SPAX_FMT_INT4                     */
+  int32_t base_group;            /* INT4 group rows: 128                               */
+  int32_t approx_group;          /* two-bit group rows: 64 or 128                      */
+  int32_t reserved0;
+  /* derived by spax_layout_init */
+  int64_t d_out_total;           /* sum of d_out                                       */
+  int64_t rec_F, rec_A;          /* unpadded record bytes                              */
+  int64_t stride_F, stride_A;    /* padded record bytes (multiples of 128)             */
+  int64_t off_A;                 /* byte offset of region A = d_in * stride_F          */
+  int64_t total_bytes;           /* blob size                                          */
+} spax_layout;
+
+/* Validate the inputs of *L and fill its derived fields.  Host only; enqueues nothing.
+ * Errors: SPAX_ERR_NULL; SPAX_ERR_SHAPE if n_mats, d_in, a group size or the format is
+ * out of range, or any d_out[m] is not a positive multiple of approx_group (and of
+ * base_group for INT4). */
+int spax_layout_init(spax_layout* L);
+
+/*
+ * Pack fp16 weights into the blob (offline, once per weight set).
+ *   W[m]   : host array of n_mats device pointers; W[m] is matrix m stored column-major
+ *            as d_in records of d_out[m] fp16 values (the record of channel j is column j).
+ *   packed : device pointer, total_bytes, 256-byte aligned; fully overwritten, padding
+ *            included, so the result is a deterministic function of the weights.
+ * Weights must be finite (non-finite input gives unspecified codes).
+ * Errors: SPAX_ERR_NULL, SPAX_ERR_SHAPE (layout not initialised), SPAX_ERR_ALIGN
+ * (packed not 256-byte aligned or a W[m] not 16-byte aligned), SPAX_ERR_HIP.
+ */
+int spax_pack_columns(const spax_layout* L, const uint16_t* const* W, void* packed,
+                      hipStream_t stream);
+
+/* ---------------------------------------------------------------- tier masks */
+enum { SPAX_TIER_SKIP = 0, SPAX_TIER_APPROX = 1, SPAX_TIER_FULL = 2 };
+enum { SPAX_MODE_TOPK = 0, SPAX_MODE_THRESHOLD = 1, SPAX_MODE_TOPK_GUIDED = 2 };
+
+/*
+ * Tier-mask parameters.  Ranking: channel j outranks k iff key_j > key_k, or equal keys
+ * and j < k, with key = (fp16 bits of x) & 0x7FFF (so NaN ranks above +Inf).
+ *   TOPK         : ranks [0, n_full) FULL, the next n_approx APPROX, the rest SKIP.
+ *   THRESHOLD    : FULL if |x| >= tau_full, else APPROX if |x| >= tau_skip, else SKIP.
+ *   TOPK_GUIDED  : natural skip count c = #{|x| < tau}; n_skip = min(max(c, n_skip_lo),
+ *                  n_skip_hi); kept = d - n_skip; n_approx = floor((approx_num*kept +
+ *                  floor(approx_den/2)) / approx_den); then TOPK(kept - n_approx, n_approx).
+ *                  (TopK-Guided section 2.1; spax_guided_bounds gives the +-delta band.)
+ * Float thresholds are compared as fp16 keys: |x| >= tau  <=>  key >= K(tau), with K(tau)
+ * from spax_key_threshold.
+ */
+typedef struct spax_tier_params {
+  int32_t mode;
+  int32_t n_full, n_approx;        /* TOPK                                   */
+  int32_t n_skip_lo, n_skip_hi;    /* TOPK_GUIDED clip band on the skip count */
+  int32_t approx_num, approx_den;  /* TOPK_GUIDED FULL/APPROX split of kept   */
+  int32_t reserved0;
+  double tau_skip, tau_full;       /* THRESHOLD                               */
+  double tau;                      /* TOPK_GUIDED calibrated threshold        */
+} spax_tier_params;
+
+/*
+ * Build one tier mask (one workgroup per vector).
+ *   x          : device, d_in fp16 activations.
+ *   tier       : device, d_in bytes of SPAX_TIER_* (may be NULL: not written).
+ *   full_idx   : device, capacity d_in int32; ascending channel indices of the FULL tier.
+ *   approx_idx : device, capacity d_in int32; ascending indices of the APPROX tier.
+ *   counts     : device, 3 int32 = {n_full, n_approx, n_skip}.  Stays on the device.
+ * List entries past their count are unspecified.  x, lists and counts 4-byte aligned.
+ * Errors: SPAX_ERR_NULL, SPAX_ERR_SHAPE (d_in outside 1..SPAX_MAX_DIN), SPAX_ERR_PARAM
+ * (unknown mode, counts out of range, n_skip_lo > n_skip_hi, approx_den <= 0,
+ * approx_num outside [0, approx_den], tau_skip > tau_full, NaN thresholds),
+ * SPAX_ERR_ALIGN, SPAX_ERR_HIP.
+ */
+int spax_build_tiers(const uint16_t* x, int32_t d_in, const spax_tier_params* p,
+                     uint8_t* tier, int32_t* full_idx, int32_t* approx_idx, int32_t* counts,
+                     hipStream_t stream);
+
+/* ---------------------------------------------------------------- tiered GEMV */
+
+/* Workspace bytes spax_tiered_gemv needs for layout *L.  The current kernels need none and
+ * return 0 (then ws may be NULL); callers should still size ws with this function.
+ * Returns 0 also if *L is not initialised. */
+size_t spax_gemv_workspace_bytes(const spax_layout* L);
+
+/*
+ * y = tiered product of one packed blob with one activation vector.
+ *   packed      : device blob laid out by *L (spax_pack_columns), 256-byte aligned.
+ *   x           : device, d_in fp16 activations (the same vector the mask was built from),
+ *                 4-byte aligned; for odd d_in the kernels may read the two bytes that pad
+ *                 x to a whole dword (never past that dword).
+ *   full_idx, approx_idx, counts : device, as written by spax_build_tiers (or any
+ *                 caller lists of distinct channels with counts[0], counts[1]).  Counts are
+ *                 clamped to [0, d_in] and indices to [0, d_in) on the device, so malformed
+ *                 lists give an unspecified y but never an out-of-bounds access.
+ *   y           : device, d_out_total fp32, 16-byte aligned; fully overwritten (all zeros
+ *                 if both lists are empty).  Rows follow the fused order of *L.
+ *   ws, ws_bytes: device workspace of at least spax_gemv_workspace_bytes(L) bytes,
+ *                 256-byte aligned (may be NULL when that size is 0).
+ * Accumulation is fp32.  Column chunks handled by different workgroups meet in y through
+ * fp32 atomic adds, so y can differ in the last bits between runs; the tier masks and
+ * lists are bit-exact.  Enqueues a zero fill of y before the product when the launch
+ * splits the column lists.
+ * Errors: SPAX_ERR_NULL, SPAX_ERR_SHAPE, SPAX_ERR_ALIGN, SPAX_ERR_WORKSPACE, SPAX_ERR_HIP.
+ */
+int spax_tiered_gemv(const spax_layout* L, const void* packed, const uint16_t* x,
+                     const int32_t* full_idx, const int32_t* approx_idx,
+                     const int32_t* counts, float* y, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ---------------------------------------------------------------- decode step */
+
+/*
+ * One group of projections that share an activation vector (q|k|v, o, gate|up, down).
+ * All pointers are device pointers as in spax_build_tiers / spax_tiered_gemv.
+ */
+typedef struct spax_phase {
+  const spax_layout* layout;   /* host pointer to an initialised layout */
+  const void* packed;
+  const uint16_t* x;
+  spax_tier_params params;
+  uint8_t* tier;               /* may be NULL */
+  int32_t* full_idx;
+  int32_t* approx_idx;
+  int32_t* counts;
+  float* y;
+} spax_phase;
+
+/* spax_step.flags */
+enum { SPAX_STEP_DEFAULT = 0 };
+
+typedef struct spax_step {
+  int32_t n_phases;            /* e.g. 32 layers x 4 groups = 128               */
+  int32_t flags;
+  const spax_phase* phases;    /* host array of n_phases                        */
+  void* ws;                    /* device workspace, see spax_step_workspace_bytes */
+  size_t ws_bytes;
+} spax_step;
+
+/* Workspace bytes for spax_decode_step_projections over these phases (the maximum of
+ * the per-phase GEMV workspaces; currently 0). */
+size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases);
+
+/*
+ * One batch-one decode step over all projection groups, in order: for each phase, the
+ * tier mask of its activation vector, then the tiered GEMV of its fused matrices.
+ * Phase p+1 is enqueued after phase p (stream order), as in a decoder where each
+ * group's input depends on the previous group's output.  Two launches per phase: the mask
+ * kernel (which also clears y) and the GEMV.
+ * (eigenradar commentary on SpAx, second and last paragraphs: selection applies per
+ * generated token during batch-one decoding.)
+ * Errors: the union of spax_build_tiers and spax_tiered_gemv errors, reported before
+ * anything is enqueued.
+ */
+int spax_decode_step_projections(const spax_step* step, hipStream_t stream);
+
+/* ---------------------------------------------------------------- host helpers */
+
+/* K(tau): smallest fp16 magnitude key k in [0, 0x7C00] with half(k) >= tau (compared in
+ * double), else 0x7C01.  Returns -1 for NaN. */
+int32_t spax_key_threshold(double tau);
+
+/* Fixed keep fractions -> counts by cumulative round-half-up:
+ * n_full = floor(p_full*d + 0.5), n_keep = floor((p_full + p_approx)*d + 0.5). */
+int spax_counts_from_fractions(int32_t d, double p_full, double p_approx,
+                               int32_t* n_full, int32_t* n_approx);
+
+/* TopK-Guided +-delta band on the skip count (section 2.1): n_lo = max(0,
+ * ceil(d*(s - delta) - 1e-9)), n_hi = min(d, floor(d*(s + delta) + 1e-9)). */
+int spax_guided_bounds(int32_t d, double s, double delta, int32_t* n_lo, int32_t* n_hi);
+
+const char* spax_status_string(int status);
+const char* spax_last_error(void);   /* thread-local; "" if none */
+const char* spax_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPAX_H */
