@@ -10,6 +10,8 @@ from __future__ import annotations
 
 import ctypes as C
 
+STEP_DEFAULT, STEP_FUSED_MASK = 0, 1
+
 from ._lib import (FMT_FP16, FMT_INT4, MAX_DIN, MAX_MATS, MODE_THRESHOLD, MODE_TOPK,  # noqa: F401
                    MODE_TOPK_GUIDED, TIER_APPROX, TIER_FULL, TIER_SKIP, Layout, Phase,
                    SpaxError, Step, TierParams, check, lib, LIB_PATH)
@@ -138,16 +140,23 @@ def spax_step_workspace_bytes(phases) -> int:
 
 
 def spax_decode_step_projections(phases, ws, ws_bytes: int | None = None, flags: int = 0,
-                                 stream=None) -> None:
+                                 stream=None, events=None) -> None:
+    """``events``: optional list of 2 * n_phases torch.cuda.Event(enable_timing=True);
+    events[2i] -> events[2i+1] then brackets phase i's GEMV launch on the stream."""
     arr = phases if isinstance(phases, C.Array) else phase_array(phases)
     if ws_bytes is None:
-        ws_bytes = ws.numel() * ws.element_size()
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = Step()
     st.n_phases = len(arr)
     st.flags = int(flags)
     st.phases = C.cast(arr, C.POINTER(Phase))
     st.ws = _ptr(ws)
     st.ws_bytes = int(ws_bytes)
+    if events is not None:
+        if len(events) != 2 * len(arr):
+            raise ValueError("need 2 * n_phases events")
+        ev = (C.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+        st.events = C.cast(ev, C.POINTER(C.c_void_p))
     check(lib.spax_decode_step_projections(C.byref(st), _stream(stream)),
           "spax_decode_step_projections")
 

@@ -54,7 +54,7 @@ class Phase(C.Structure):
 
 class Step(C.Structure):
     _fields_ = [("n_phases", C.c_int32), ("flags", C.c_int32), ("phases", C.POINTER(Phase)),
-                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("events", C.POINTER(C.c_void_p))]
 
 
 def _hip_runtimes():

@@ -104,7 +104,7 @@ int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
   clear_error();
   if (!step || !step->phases) return fail(SPAX_ERR_NULL, "step and step->phases are required");
   if (step->n_phases < 1) return fail(SPAX_ERR_SHAPE, "n_phases %d < 1", step->n_phases);
-  if (step->flags != SPAX_STEP_DEFAULT) return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags");
+  if (step->flags & ~SPAX_STEP_FUSED_MASK) return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags");
   // Validate every phase before enqueueing anything.
   for (int i = 0; i < step->n_phases; ++i) {
     const spax_phase& ph = step->phases[i];
@@ -119,23 +119,7 @@ int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
                          step->ws, step->ws_bytes, &plan);
     if (st) return phase_fail(st, i);
   }
-  for (int i = 0; i < step->n_phases; ++i) {
-    const spax_phase& ph = step->phases[i];
-    TierArgs a;
-    tier_args_from_params(&ph.params, ph.layout->d_in, &a);
-    const GemvPlan plan = gemv_plan(ph.layout);
-    // The mask kernel also clears y when the GEMV accumulates it with atomics (small y only:
-    // one workgroup does the clearing).
-    const bool clear_in_mask = plan.n_chunks > 1 && ph.layout->d_out_total <= kMaskClearMax;
-    int st = launch_build_tiers(a, ph.x, ph.tier, ph.full_idx, ph.approx_idx, ph.counts,
-                                clear_in_mask ? ph.y : nullptr,
-                                clear_in_mask ? ph.layout->d_out_total : 0, stream);
-    if (st) return st;
-    st = launch_tiered_gemv(ph.layout, plan, ph.packed, ph.x, ph.full_idx, ph.approx_idx,
-                            ph.counts, ph.y, clear_in_mask, stream);
-    if (st) return st;
-  }
-  return SPAX_OK;
+  return launch_decode_step(step, stream);
 }
 
 }  // extern "C"

@@ -67,6 +67,14 @@ int launch_zero_f32(float* y, int64_t n, hipStream_t s);
 // Largest y the single-workgroup mask kernel clears on the side.
 constexpr int64_t kMaskClearMax = 65536;
 
+// ------------------------------------------------------------------ decode step
+// The fused mask+GEMV kernel keeps the activations and its list slices in LDS.
+constexpr int32_t kFusedMaxDin = 16384;
+constexpr size_t kFusedMaxDynLds = 48 * 1024;
+bool fused_phase_ok(const spax_layout* L);
+// Enqueue a validated step.
+int launch_decode_step(const spax_step* st, hipStream_t s);
+
 // y_zeroed: y already holds zeros (stream-ordered); otherwise a zero fill is enqueued first
 // whenever the plan splits K.
 int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* packed,

@@ -1,0 +1,232 @@
+// Decode step over a stack of projection groups.
+//
+// Pages: eigenradar commentary on SpAx, second and last paragraphs (selection per generated
+// token during batch-one decoding); TopK-Guided (arXiv:2610.01763) section 2.1 (per-token
+// mask, O(d)); ByteCross abstract (fixed kernel costs add to the byte account).
+//
+// Default: per group, the stand-alone mask kernel (tiers.hip, which also clears y) and then
+// the stand-alone GEMV (gemv.hip).  With SPAX_STEP_FUSED_MASK, a group's mask and its GEMV
+// run in one kernel: every workgroup loads the activation vector
+// into LDS, finds the two tier boundaries and ranks the channels (mask_core.h), keeps only
+// the slice of the FULL / APPROX lists its column chunk needs (channel | fp16 x_j << 16 per
+// LDS entry), then streams those columns for its 512-row tile (gemv_core.h).  Workgroup 0 also
+// writes the tier bytes, the ascending lists and the counts, so the outputs equal those of
+// spax_build_tiers.  The redundant O(d) mask work per workgroup replaces a separate mask
+// launch and the counts -> indices -> activations chain of dependent global loads; it is
+// measured slower on gfx950 because the mask is issue-bound inside one CU and the fused form
+// repeats it in every workgroup.
+//
+// y of a group is accumulated with fp32 atomics and must start at zero: the mask kernel (or,
+// fused, the previous launch, spread over its workgroups) clears it; otherwise a small
+// kernel does.
+#include "gemv_core.h"
+#include "mask_core.h"
+
+namespace spax {
+namespace {
+
+constexpr int kFusedThreads = kGemvThreads;  // 512
+
+struct FusedArgs {
+  TierArgs ta;
+  gemv::Shape sh;
+  const uint8_t* packed;
+  const uint16_t* x;
+  uint8_t* tier;
+  int32_t* full_idx;
+  int32_t* approx_idx;
+  int32_t* counts;
+  float* y;
+  float4* y_next;    // cleared as a side job (NULL: none)
+  int64_t n_next4;
+  int32_t cap;       // LDS list entries per tier
+  int32_t xs_bytes;  // LDS bytes of the activations (lists follow)
+};
+
+template <int FMT, int MAXD>
+__global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  // The mask's scratch and the GEMV's cross-wave reduction are never live together.
+  __shared__ union {
+    mask::Shared<kFusedThreads> msh;
+    float red[gemv::kWaves][kTileRows];
+  } u;
+  mask::Shared<kFusedThreads>& msh = u.msh;
+  uint32_t* xs32 = reinterpret_cast<uint32_t*>(dyn);
+  uint32_t* lF = reinterpret_cast<uint32_t*>(dyn + a.xs_bytes);
+  uint32_t* lA = lF + a.cap;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const gemv::Shape& sh = a.sh;
+  const int tile = blockIdx.x % sh.n_tiles;
+  const int chunk = blockIdx.x / sh.n_tiles;
+  const int d = a.ta.d;
+
+  // Side job: clear this workgroup's slice of the next group's output.
+  if (a.y_next) {
+    const int64_t per = (a.n_next4 + gridDim.x - 1) / gridDim.x;
+    const int64_t b = (int64_t)blockIdx.x * per;
+    const int64_t e = min(b + per, a.n_next4);
+    for (int64_t i = b + tid; i < e; i += kFusedThreads) a.y_next[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  // ---- mask (every workgroup; workgroup 0 also writes the outputs of the mask)
+  mask::Keys k;
+  const mask::Plan p = mask::build_plan<kFusedThreads, MAXD>(msh, k, xs32, a.x, a.ta);
+  const int nF = p.n_full, nA = p.n_kept - p.n_full;
+  const int fb = (int)((int64_t)nF * chunk / sh.n_chunks);
+  const int fe = (int)((int64_t)nF * (chunk + 1) / sh.n_chunks);
+  const int ab = (int)((int64_t)nA * chunk / sh.n_chunks);
+  const int ae = (int)((int64_t)nA * (chunk + 1) / sh.n_chunks);
+  const bool writer = blockIdx.x == 0;
+  mask::emit<kFusedThreads>(
+      msh, k, p,
+      [&](int t, int rank, int j, uint32_t raw) {
+        const uint32_t e = (uint32_t)j | (raw << 16);
+        if (t == SPAX_TIER_FULL) {
+          if (rank >= fb && rank < fe) lF[rank - fb] = e;
+          if (writer) a.full_idx[rank] = j;
+        } else {
+          if (rank >= ab && rank < ae) lA[rank - ab] = e;
+          if (writer) a.approx_idx[rank] = j;
+        }
+      },
+      [&](int j, int t) {
+        if (writer && a.tier) a.tier[j] = (uint8_t)t;
+      });
+  if (writer && tid == 0) {
+    a.counts[0] = nF;
+    a.counts[1] = nA;
+    a.counts[2] = d - p.n_kept;
+  }
+  __syncthreads();  // list slices complete; the mask scratch is dead from here on
+
+  // ---- GEMV over this workgroup's slice
+  const int T = sh.T;
+  const int row0 = tile * kTileRows;
+  const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
+  int wfb, wfe, wab, wae;
+  gemv::wave_range(fb, fe, wave, wfb, wfe);
+  gemv::wave_range(ab, ae, wave, wab, wae);
+  float acc[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
+  float zsum = 0.0f;
+  const uint32_t jmax = (uint32_t)d - 1u;
+  gemv::stream_full<FMT>(sh, a.packed, row, wfb, wfe, gemv::LdsList{lF, fb, jmax}, acc, zsum);
+  gemv::stream_approx(sh, a.packed, row, wab, wae, gemv::LdsList{lA, ab, jmax}, acc, zsum);
+  gemv::finish_tile(u.red, acc, zsum, wave, lane, row0, T, sh.n_chunks, a.y);
+}
+
+struct FusedLds {
+  int32_t cap, xs_bytes;
+  size_t bytes;
+};
+
+// Dynamic LDS: the activations (d_in halves rounded up to whole dwords, in bytes, rounded
+// to 16), then the workgroup's two list slices.
+FusedLds fused_lds(const spax_layout* L, const GemvPlan& plan) {
+  FusedLds f;
+  f.cap = (L->d_in + plan.n_chunks - 1) / plan.n_chunks;
+  f.xs_bytes = (4 * ((L->d_in + 1) / 2) + 15) / 16 * 16;
+  f.bytes = (size_t)f.xs_bytes + 8 * (size_t)f.cap;
+  return f;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+bool fused_phase_ok(const spax_layout* L) {
+  if (L->d_in > kFusedMaxDin) return false;
+  return fused_lds(L, gemv_plan(L)).bytes <= kFusedMaxDynLds;
+}
+
+int launch_decode_step(const spax_step* st, hipStream_t s) {
+  const int n = st->n_phases;
+  const bool separate = (st->flags & SPAX_STEP_FUSED_MASK) == 0;
+  auto fused_phase_ok = [&](const spax_layout* L) { return !separate && spax::fused_phase_ok(L); };
+  for (int i = 0; i < n; ++i) {
+    const spax_phase& ph = st->phases[i];
+    const spax_layout* L = ph.layout;
+    TierArgs ta;
+    tier_args_from_params(&ph.params, L->d_in, &ta);
+    const GemvPlan plan = gemv_plan(L);
+    const size_t ybytes = (size_t)L->d_out_total * 4;
+    // Was this group's y cleared by the previous launch?
+    bool cleared = false;
+    if (i > 0) {
+      const spax_phase& pp = st->phases[i - 1];
+      cleared = fused_phase_ok(pp.layout) && plan.n_chunks > 1 &&
+                !overlaps(pp.y, (size_t)pp.layout->d_out_total * 4, ph.y, ybytes);
+    }
+    if (!fused_phase_ok(L)) {
+      // Large input vectors: stand-alone mask kernel (which clears y) + GEMV.
+      const bool clear_in_mask = plan.n_chunks > 1 && L->d_out_total <= kMaskClearMax && !cleared;
+      if (plan.n_chunks > 1 && !cleared && !clear_in_mask) {
+        int rc = launch_zero_f32(ph.y, L->d_out_total, s);
+        if (rc) return rc;
+        cleared = true;
+      }
+      int rc = launch_build_tiers(ta, ph.x, ph.tier, ph.full_idx, ph.approx_idx, ph.counts,
+                                  clear_in_mask ? ph.y : nullptr,
+                                  clear_in_mask ? L->d_out_total : 0, s);
+      if (rc) return rc;
+      if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[2 * i], s));
+      rc = launch_tiered_gemv(L, plan, ph.packed, ph.x, ph.full_idx, ph.approx_idx, ph.counts,
+                              ph.y, cleared || clear_in_mask, s);
+      if (rc) return rc;
+      if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[2 * i + 1], s));
+      continue;
+    }
+    if (plan.n_chunks > 1 && !cleared) {
+      int rc = launch_zero_f32(ph.y, L->d_out_total, s);
+      if (rc) return rc;
+    }
+    if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[2 * i], s));
+    FusedArgs a{};
+    a.ta = ta;
+    a.sh = gemv_shape(L, plan);
+    a.packed = static_cast<const uint8_t*>(ph.packed);
+    a.x = ph.x;
+    a.tier = ph.tier;
+    a.full_idx = ph.full_idx;
+    a.approx_idx = ph.approx_idx;
+    a.counts = ph.counts;
+    a.y = ph.y;
+    a.y_next = nullptr;
+    a.n_next4 = 0;
+    if (i + 1 < n) {
+      const spax_phase& nx = st->phases[i + 1];
+      const GemvPlan np = gemv_plan(nx.layout);
+      if (np.n_chunks > 1 && !overlaps(ph.y, ybytes, nx.y, (size_t)nx.layout->d_out_total * 4)) {
+        a.y_next = reinterpret_cast<float4*>(nx.y);
+        a.n_next4 = (nx.layout->d_out_total + 3) / 4;
+      }
+    }
+    const FusedLds f = fused_lds(L, plan);
+    a.cap = f.cap;
+    a.xs_bytes = f.xs_bytes;
+    const dim3 grid((unsigned)(plan.n_tiles * plan.n_chunks));
+    // Two register budgets for the activations: d_in <= 4096 (8 per lane) and the rest.
+    const bool small = L->d_in <= 4096;
+    const dim3 blk(kFusedThreads);
+    if (L->base_fmt == SPAX_FMT_FP16) {
+      if (small) hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_FP16, 4096>), grid, blk, f.bytes, s, a);
+      else hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_FP16, kFusedMaxDin>), grid, blk, f.bytes, s, a);
+    } else {
+      if (small) hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_INT4, 4096>), grid, blk, f.bytes, s, a);
+      else hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_INT4, kFusedMaxDin>), grid, blk, f.bytes, s, a);
+    }
+    SPAX_HIP_CHECK(hipGetLastError());
+    if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[2 * i + 1], s));
+  }
+  return SPAX_OK;
+}
+
+}  // namespace spax

@@ -76,7 +76,8 @@ int tier_args_from_params(const spax_tier_params* p, int32_t d, TierArgs* out) {
       if (p->n_skip_lo < 0 || p->n_skip_lo > p->n_skip_hi || p->n_skip_hi > d)
         return fail(SPAX_ERR_PARAM, "skip band [%d, %d] invalid for d=%d", p->n_skip_lo,
                     p->n_skip_hi, d);
-      if (p->approx_den <= 0 || p->approx_num < 0 || p->approx_num > p->approx_den)
+      if (p->approx_den <= 0 || p->approx_den > 65535 || p->approx_num < 0 ||
+          p->approx_num > p->approx_den)
         return fail(SPAX_ERR_PARAM, "approx split %d/%d invalid", p->approx_num, p->approx_den);
       a.k_tau = spax_key_threshold(p->tau);
       a.n_lo = p->n_skip_lo;

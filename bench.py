@@ -104,8 +104,11 @@ class Stack:
         self.ws = torch.zeros(spax.spax_step_workspace_bytes(self.phase_arrays[0]),
                               dtype=torch.uint8, device=dev)
 
+    flags = 0
+
     def step(self, t):
-        self.spax.spax_decode_step_projections(self.phase_arrays[t % self.tokens], self.ws)
+        self.spax.spax_decode_step_projections(self.phase_arrays[t % self.tokens], self.ws,
+                                               flags=self.flags)
 
     def algorithmic_bytes(self, i, counts):
         """Bytes the GEMV of phase i must read/write for a mask with these counts."""
@@ -115,20 +118,20 @@ class Stack:
                 + 4 * int(L.d_out_total))
 
     def timed_kernels(self, t):
-        """The same step as separate mask / GEMV launches with events around each GEMV."""
-        torch, spax = self.torch, self.spax
-        evs = []
-        for i, (L, pk, p, b) in enumerate(zip(self.layouts, self.packed, self.params, self.bufs)):
-            x = self.x[t % self.tokens][i]
-            spax.spax_build_tiers(x, int(L.d_in), p, b["tier"], b["f"], b["a"], b["c"])
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            spax.spax_tiered_gemv(L, pk, x, b["f"], b["a"], b["c"], b["y"], self.ws)
-            e1.record()
-            evs.append((e0, e1))
+        """The same decode step with events recorded by the library right before and after
+        each phase's GEMV launch on the launch stream."""
+        torch = self.torch
+        n = len(self.layouts)
+        if not hasattr(self, "events"):
+            self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+            for e in self.events:   # creates the underlying HIP events
+                e.record()
+            torch.cuda.synchronize()
+        self.spax.spax_decode_step_projections(self.phase_arrays[t % self.tokens], self.ws,
+                                               events=self.events, flags=self.flags)
         torch.cuda.synchronize()
         counts = [b["c"].cpu().numpy() for b in self.bufs]
-        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        ms = [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(n)]
         return ms, counts
 
 
@@ -203,7 +206,7 @@ def main():
     step_ms = e0.elapsed_time(e1) / args.steps
     log(f"[bench] decode step: {step_ms * 1e3:.1f} us/token (event), wall {wall_ms / args.steps:.3f} ms/step")
 
-    # ---- per-kernel timing of the tiered GEMV over the same steps
+    # ---- per-kernel timing of the tiered GEMV kernel over the same steps
     tot_bytes, tot_ms, n_launch, sel_bytes_tok = 0, 0.0, 0, []
     per_phase = {}
     for t in range(args.steps):

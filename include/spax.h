@@ -153,8 +153,8 @@ typedef struct spax_tier_params {
  *   counts     : device, 3 int32 = {n_full, n_approx, n_skip}.  Stays on the device.
  * List entries past their count are unspecified.  x, lists and counts 4-byte aligned.
  * Errors: SPAX_ERR_NULL, SPAX_ERR_SHAPE (d_in outside 1..SPAX_MAX_DIN), SPAX_ERR_PARAM
- * (unknown mode, counts out of range, n_skip_lo > n_skip_hi, approx_den <= 0,
- * approx_num outside [0, approx_den], tau_skip > tau_full, NaN thresholds),
+ * (unknown mode, counts out of range, n_skip_lo > n_skip_hi, approx_den outside
+ * 1..65535, approx_num outside [0, approx_den], tau_skip > tau_full, NaN thresholds),
  * SPAX_ERR_ALIGN, SPAX_ERR_HIP.
  */
 int spax_build_tiers(const uint16_t* x, int32_t d_in, const spax_tier_params* p,
@@ -212,7 +212,13 @@ typedef struct spax_phase {
 } spax_phase;
 
 /* spax_step.flags */
-enum { SPAX_STEP_DEFAULT = 0 };
+enum {
+  /* one mask launch + one GEMV launch per phase */
+  SPAX_STEP_DEFAULT = 0,
+  /* one fused launch per phase in which every workgroup rebuilds the mask from x
+   * (same outputs; pays the mask once per workgroup instead of once per phase) */
+  SPAX_STEP_FUSED_MASK = 1
+};
 
 typedef struct spax_step {
   int32_t n_phases;            /* e.g. 32 layers x 4 groups = 128               */
@@ -220,6 +226,11 @@ typedef struct spax_step {
   const spax_phase* phases;    /* host array of n_phases                        */
   void* ws;                    /* device workspace, see spax_step_workspace_bytes */
   size_t ws_bytes;
+  /* Optional timing hook (NULL: none): 2 * n_phases caller-created events.  events[2i] and
+   * events[2i+1] are recorded on the stream right before and right after phase i's GEMV
+   * launch (its fused mask+GEMV launch with SPAX_STEP_FUSED_MASK), so they bracket exactly
+   * that kernel. */
+  hipEvent_t* events;
 } spax_step;
 
 /* Workspace bytes for spax_decode_step_projections over these phases (the maximum of
@@ -230,8 +241,8 @@ size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases);
  * One batch-one decode step over all projection groups, in order: for each phase, the
  * tier mask of its activation vector, then the tiered GEMV of its fused matrices.
  * Phase p+1 is enqueued after phase p (stream order), as in a decoder where each
- * group's input depends on the previous group's output.  Two launches per phase: the mask
- * kernel (which also clears y) and the GEMV.
+ * group's input depends on the previous group's output.  Default: two launches per phase,
+ * the mask kernel (which also clears y) and the GEMV; see SPAX_STEP_FUSED_MASK.
  * (eigenradar commentary on SpAx, second and last paragraphs: selection applies per
  * generated token during batch-one decoding.)
  * Errors: the union of spax_build_tiers and spax_tiered_gemv errors, reported before

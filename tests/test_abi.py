@@ -41,7 +41,7 @@ def test_struct_sizes_match_c():
     assert C.sizeof(_lib.Layout) == 96
     assert C.sizeof(_lib.TierParams) == 56
     assert C.sizeof(_lib.Phase) == 120
-    assert C.sizeof(_lib.Step) == 32
+    assert C.sizeof(_lib.Step) == 40
 
 
 def test_key_threshold_golden_and_oracle():
@@ -126,7 +126,8 @@ def test_build_tiers_validation():
     for p in [spax.topk_params(5, 4), spax.topk_params(-1, 0), spax.threshold_params(2.0, 1.0),
               spax.threshold_params(float("nan"), 1.0), spax.guided_params(1.0, 5, 4, 1, 2),
               spax.guided_params(1.0, 0, 9, 1, 2), spax.guided_params(1.0, 0, 4, 1, 0),
-              spax.guided_params(1.0, 0, 4, 3, 2), spax.guided_params(float("nan"), 0, 4, 1, 2)]:
+              spax.guided_params(1.0, 0, 4, 3, 2), spax.guided_params(float("nan"), 0, 4, 1, 2),
+              spax.guided_params(1.0, 0, 4, 1, 65536)]:
         assert lib.spax_build_tiers(FAKE, 8, C.byref(p), 0, FAKE, FAKE, FAKE, 0) == _lib.SPAX_ERR_PARAM
     bad_mode = spax.topk_params(1, 1)
     bad_mode.mode = 7
@@ -184,6 +185,6 @@ def test_decode_step_validates_all_phases_first():
         spax.spax_decode_step_projections(arr, FAKE, ws_bytes=ws, stream=0)
     assert e.value.status == _lib.SPAX_ERR_PARAM and "phase 2" in str(e.value)
     with pytest.raises(spax.SpaxError) as e:
-        spax.spax_decode_step_projections(spax.phase_array([good]), FAKE, ws_bytes=ws, flags=99,
+        spax.spax_decode_step_projections(spax.phase_array([good]), FAKE, ws_bytes=ws, flags=6,
                                           stream=0)
     assert e.value.status == _lib.SPAX_ERR_UNSUPPORTED

@@ -1,0 +1,182 @@
+"""GPU parity of spax_decode_step_projections: every path the step can take.
+
+* fused mask+GEMV launches (d_in <= 16384), fp16 and int4 base formats;
+* the two-kernel fallback (d_in > 16384) mixed into the same step;
+* a single column chunk (tiny d_in: plain stores instead of atomics);
+* consecutive phases writing the same y buffer (the early clearing must not fire);
+* TOPK, THRESHOLD and TOPK_GUIDED masks in one step.
+Masks, lists and counts bit-exact against the oracle; y within relative L2 1e-3.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import gemv as ogemv
+from oracle import pack as opack
+from oracle import tiers as otiers
+
+pytestmark = pytest.mark.gpu
+REL_L2 = 1e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import activation_sparse_tiered_amd as spax
+    return torch, spax, torch.device("cuda:0")
+
+
+def rel_l2(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(np.asarray(got, dtype=np.float64) - ref)
+    return num / den if den > 0 else num
+
+
+def _oracle_args(mode_spec, d):
+    kind = mode_spec[0]
+    if kind == "topk":
+        nf, na = otiers.counts_from_fractions(d, mode_spec[1], mode_spec[2])
+        return dict(mode=otiers.MODE_TOPK, n_full=nf, n_approx=na)
+    if kind == "threshold":
+        return dict(mode=otiers.MODE_THRESHOLD, tau_skip=mode_spec[1], tau_full=mode_spec[2])
+    s, delta = mode_spec[1], mode_spec[2]
+    lo, hi = otiers.guided_bounds(d, s, delta)
+    return dict(mode=otiers.MODE_TOPK_GUIDED, tau=-math.log(1 - s), n_lo=lo, n_hi=hi, num=3, den=10)
+
+
+def _params(spax, oa):
+    if oa["mode"] == otiers.MODE_TOPK:
+        return spax.topk_params(oa["n_full"], oa["n_approx"])
+    if oa["mode"] == otiers.MODE_THRESHOLD:
+        return spax.threshold_params(oa["tau_skip"], oa["tau_full"])
+    return spax.guided_params(oa["tau"], oa["n_lo"], oa["n_hi"], oa["num"], oa["den"])
+
+
+def run_step(env, specs, seed, share_y=None, flags=0):
+    """specs: list of (d_in, d_out list, base_fmt, G, mode_spec).  share_y: set of phase
+    indices whose y buffer is the same tensor as the previous phase's (same size)."""
+    torch, spax, dev = env
+    phases, keep = [], []
+    share_y = share_y or set()
+    prev_y = None
+    for i, (d_in, d_out, fmt, G, mspec) in enumerate(specs):
+        L = spax.spax_layout_init(d_in, d_out, fmt, 128, G)
+        O = opack.Layout(d_in, d_out, fmt, 128, G)
+        Ws = [synth.weights(seed + i, d_in, r, m) for m, r in enumerate(d_out)]
+        packed = torch.empty(int(L.total_bytes), dtype=torch.uint8, device=dev)
+        spax.spax_pack_columns(L, [torch.from_numpy(w).to(dev) for w in Ws], packed)
+        x16 = synth.activations(seed, d_in, i, token_scale=synth.token_scale(seed, i))
+        oa = _oracle_args(mspec, d_in)
+        if i in share_y:
+            y = prev_y
+        else:
+            y = torch.full((int(L.d_out_total),), float("nan"), dtype=torch.float32, device=dev)
+        b = dict(x=torch.from_numpy(x16).to(dev),
+                 tier=torch.full((d_in,), 0xAB, dtype=torch.uint8, device=dev),
+                 f=torch.full((d_in,), -7, dtype=torch.int32, device=dev),
+                 a=torch.full((d_in,), -7, dtype=torch.int32, device=dev),
+                 c=torch.full((3,), -7, dtype=torch.int32, device=dev), y=y)
+        phases.append(spax.make_phase(L, packed, b["x"], _params(spax, oa), b["tier"], b["f"],
+                                      b["a"], b["c"], b["y"]))
+        keep.append((L, O, Ws, x16, oa, packed, b))
+        prev_y = y
+    arr = spax.phase_array(phases)
+    ws = torch.zeros(max(1, spax.spax_step_workspace_bytes(arr)), dtype=torch.uint8, device=dev)
+    spax.spax_decode_step_projections(arr, ws, flags=flags)
+    torch.cuda.synchronize()
+    return keep
+
+
+def check(keep, skip_y=()):
+    for i, (L, O, Ws, x16, oa, packed, b) in enumerate(keep):
+        args = dict(oa)
+        mode = args.pop("mode")
+        wt, wf, wa, wc = otiers.build_tiers(x16, mode, **args)
+        c = b["c"].cpu().numpy()
+        assert list(c) == list(wc), (i, c, wc)
+        assert np.array_equal(b["tier"].cpu().numpy(), wt), i
+        assert np.array_equal(b["f"].cpu().numpy()[:c[0]], wf), i
+        assert np.array_equal(b["a"].cpu().numpy()[:c[1]], wa), i
+        if i in skip_y:
+            continue
+        ref = ogemv.tiered_gemv(O, Ws, x16, wf, wa)
+        err = rel_l2(b["y"].cpu().numpy(), ref)
+        assert err <= REL_L2, (i, err)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_fp16_and_int4(env, flags):
+    specs = [(1024, [1024, 512, 512], 0, 128, ("guided", 0.5, 0.01)),
+             (1024, [1024], 0, 128, ("guided", 0.3, 0.01)),
+             (1024, [2816, 2816], 1, 128, ("topk", 0.25, 0.35)),
+             (2816, [1024], 1, 64, ("threshold", 0.5, 1.5)),
+             (768, [640], 0, 64, ("topk", 0.2, 0.3))]
+    check(run_step(env, specs, 101, flags=flags))
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_both_paths_same_outputs(env, flags):
+    """The separate mask + GEMV launches and the fused launch give the same masks."""
+    specs = [(4096, [1024, 512, 512], 0, 128, ("guided", 0.5, 0.01)),
+             (2048, [2048], 1, 128, ("topk", 0.25, 0.35)),
+             (3000, [1024], 0, 64, ("threshold", 0.6, 1.4))]
+    check(run_step(env, specs, 707, flags=flags))
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_wide_input(env, flags):
+    """Fused phases whose activation vector needs more LDS than the reduction buffer
+    (d_in > 8192): the activations, list slices and reduction area must not overlap."""
+    specs = [(11008, [512], 0, 128, ("guided", 0.5, 0.01)),
+             (16384, [256], 0, 128, ("topk", 0.3, 0.3)),
+             (9000, [1024], 1, 128, ("guided", 0.7, 0.01)),
+             (8194, [256], 0, 64, ("threshold", 0.5, 1.5))]
+    check(run_step(env, specs, 606, flags=flags))
+
+
+def test_step_fallback_large_din(env):
+    specs = [(512, [512], 0, 64, ("guided", 0.5, 0.05)),
+             (20000, [256], 0, 128, ("guided", 0.7, 0.01)),     # > 16384: two-kernel path
+             (256, [1024, 1024], 0, 128, ("topk", 0.3, 0.3)),
+             (17000, [384], 1, 128, ("topk", 0.25, 0.35))]
+    check(run_step(env, specs, 202))
+
+
+def test_step_single_chunk_phases(env):
+    specs = [(8, [4096], 0, 128, ("topk", 0.5, 0.25)),   # d_in < 32: one chunk, plain stores
+             (20, [64], 0, 64, ("topk", 1.0, 0.0)),
+             (3000, [512], 0, 64, ("guided", 0.5, 0.01))]
+    check(run_step(env, specs, 303))
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_shared_y_buffers(env, flags):
+    """Phases 1 and 2 write the same y: only the last writer's result must remain."""
+    specs = [(512, [1024], 0, 128, ("guided", 0.5, 0.05)),
+             (640, [1024], 0, 128, ("topk", 0.3, 0.3)),
+             (768, [1024], 0, 128, ("topk", 0.2, 0.3)),
+             (512, [512], 0, 64, ("threshold", 0.4, 1.2))]
+    keep = run_step(env, specs, 404, share_y={2}, flags=flags)
+    check(keep, skip_y={1})
+
+
+def test_step_repeated_calls_stable(env):
+    torch, spax, dev = env
+    specs = [(2048, [1536, 512], 0, 128, ("guided", 0.5, 0.01)), (1536, [2048], 0, 128, ("topk", 0.3, 0.3))]
+    keep = run_step(env, specs, 505)
+    first = [b["y"].cpu().numpy().copy() for *_, b in keep]
+    # run the same phases again through a fresh step call on the same buffers
+    phases = [spax.make_phase(L, packed, b["x"], _params(spax, oa), b["tier"], b["f"], b["a"],
+                              b["c"], b["y"]) for (L, O, Ws, x16, oa, packed, b) in keep]
+    for _ in range(5):
+        spax.spax_decode_step_projections(spax.phase_array(phases), None, ws_bytes=0)
+    torch.cuda.synchronize()
+    for f0, (*_, b) in zip(first, keep):
+        assert rel_l2(b["y"].cpu().numpy(), f0) <= 1e-6
+    check(keep)
