@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   const int ab = (int)((int64_t)nA * chunk / sh.n_chunks);
   const int ae = (int)((int64_t)nA * (chunk + 1) / sh.n_chunks);
   const bool writer = blockIdx.x == 0;
+  const bool tier_even = ((uintptr_t)a.tier & 1) == 0;  // channel pairs start at even j
   mask::emit<kFusedThreads>(
       msh, k, p,
       [&](int t, int rank, int j, uint32_t raw) {
@@ -93,8 +94,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
           if (writer) a.approx_idx[rank] = j;
         }
       },
-      [&](int j, int t) {
-        if (writer && a.tier) a.tier[j] = (uint8_t)t;
+      [&](int j, uint32_t t0, uint32_t t1, int n) {
+        if (!writer || !a.tier) return;
+        if (n == 2 && tier_even) *reinterpret_cast<uint16_t*>(a.tier + j) = (uint16_t)(t0 | t1 << 8);
+        else {
+          a.tier[j] = (uint8_t)t0;
+          if (n == 2) a.tier[j + 1] = (uint8_t)t1;
+        }
       });
   if (writer && tid == 0) {
     a.counts[0] = nF;

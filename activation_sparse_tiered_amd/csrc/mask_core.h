@@ -11,12 +11,16 @@
 // channels (by index) whose key is kb.  Threshold masks use (K(tau), all).
 //
 // x is copied to LDS once; wave w owns the contiguous channels [w*C, (w+1)*C), C a multiple
-// of 128.  Three passes over the wave's channels:
-//   1. 256-bin histogram of the high key bits (LDS atomics), natural count;
+// of 128.  Passes over the wave's channels:
+//   1. 256-bin histogram of the high key bits (LDS atomics into lane-group copies) and
+//      per-lane counters, summed once per wave;
 //   2. (TopK boundaries) per-wave 128-bin histograms of the low bits inside the boundary
-//      bucket, from which each wave gets its own "greater" / "equal" counts;
-//   3. emit: ranks from ballots plus per-wave bases derived from those counts.
-// One emit pass and no block-wide scan.
+//      buckets, from which each wave gets its own "greater" / "equal" counts;
+//   3. emit: ranks from ballots plus per-wave bases that wave 0 derives with one scan.
+// The kernels are issue-bound inside one CU (every wave instruction competes with those of
+// the other waves), so fixed per-wave work is kept small and is not repeated by each wave:
+// two 16-bit counts share one 32-bit lane sum (a wave holds at most 32768 channels), and a
+// step without boundary keys skips the tie ranking.
 #pragma once
 
 #include "common.h"
@@ -32,26 +36,31 @@ struct Select {
 template <int NT>
 struct Shared {
   static constexpr int W = NT / 64;
-  // Level-1 histogram in 16 copies (one per lane & 15, odd stride so the copies of a bin
-  // sit in different banks): lanes whose keys share a bin mostly hit different addresses.
-  static constexpr int kCopies = 16, kStride = 257;
-  int hist_rep[kCopies * kStride];
+  // Level-1 histogram in 8 copies (one per lane & 7, odd stride so the copies of a bin sit
+  // in different banks): lanes whose keys share a bin mostly hit different addresses.
+  static constexpr int kCopies = 8, kStride = 257;
+  static constexpr int kRep = (kCopies * kStride + 3) / 4 * 4;
+  alignas(16) int hist_rep[kRep];
+  alignas(16) int wave_hist[2][W][128];
   int hist_hi[256];
-  int wave_hist[2][W][128];
-  int wave_cnt[W][6];  // natural, gt0, eq0, gt1, eq1, spare
+  int wave_cnt[W][2];   // (gt | eq << 16) against the FULL and the kept boundary
+  int wave_nat[W];      // natural count (keys below K(tau))
+  int wave_base[W][4];  // FULL rank base, APPROX rank base, ties before (FULL, kept)
+  int totals[2];        // n_full, n_kept
+  int R[2];
   int sel_b[2], sel_above[2];
   Select sel[2];
 };
 
-// Channel layout: wave w owns channels [j0, j0 + n), j0 = w*C (C a multiple of 128); at step
-// s, lane l handles the two adjacent channels j0 + 128 s + 2 l + {0, 1}, stored as one dword
-// of raw fp16 bits (low half: even channel) in LDS, so every step is one conflict-free,
-// coalesced 256-byte LDS read per wave.  The passes are rolled loops: the kernels run once per
-// token, so their code is fetched cold and must stay small.
+// Channel layout: wave w owns channels [j0, j0 + n), j0 = w*C; at step s, lane l handles
+// the two adjacent channels j0 + 128 s + 2 l + {0, 1}, stored as one dword of raw fp16 bits
+// (low half: even channel) in LDS, so every step is one conflict-free 256-byte LDS read per
+// wave.  Passes are rolled loops: the kernels run once per token, so their code is fetched
+// cold and must stay small.
 struct Keys {
   const uint32_t* xs32;  // LDS, d halves rounded up to dwords
   int C;                 // channels per wave (multiple of 128)
-  int j0;                // first channel of this wave
+  int j0;                // first channel of this wave (even)
   int n;                 // channels of this wave
   int steps;             // steps of this wave
   __device__ __forceinline__ int off(int s, int lane, int e) const { return 128 * s + 2 * lane + e; }
@@ -115,13 +124,14 @@ struct Plan {
   int n_full, n_kept;
 };
 
-// Load x into LDS (xs32: roundup(d, 2) halves), then passes 1 and 2 plus the selects.
-// Leaves each wave's (gt, eq) counts against both boundaries in sh.wave_cnt.  Contains the
-// barriers it needs and ends with one.  d <= MAXD.
+// Load x into LDS (xs32: roundup(d, 2) halves), find both boundaries and every wave's rank
+// bases (sh.wave_base).  Contains the barriers it needs and ends with one.  d <= MAXD.
 template <int NT, int MAXD>
 __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs32,
                                            const uint16_t* __restrict__ x, const TierArgs& a) {
   constexpr int W = NT / 64;
+  using S = Shared<NT>;
+  static_assert(MAXD <= 32768 && NT >= 256, "per-wave counts are packed in 16 bits");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int d = a.d;
@@ -132,86 +142,98 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
   k.steps = (k.n + 127) / 128;
   const bool thresholds = a.mode == SPAX_MODE_THRESHOLD;
 
-  // ---- x into LDS: every load of a thread in flight at once.  For odd d the last dword
-  // also holds the two bytes past x (same dword, never used as a channel).
+  // ---- x into LDS, four loads in flight per thread and iteration.  For odd d the last
+  // dword also holds the two bytes past x (same dword, never used as a channel).
   {
     const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
     const int ndw = (d + 1) >> 1;
-    constexpr int PER = (MAXD / 2 + NT - 1) / NT;
-    uint32_t v[PER];
+    for (int i = tid; i < ndw; i += 4 * NT) {
+      uint32_t v[4];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int i = tid + q * NT;
-      v[q] = i < ndw ? x32[i] : 0u;
-    }
+      for (int q = 0; q < 4; ++q) v[q] = i + q * NT < ndw ? x32[i + q * NT] : 0u;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int i = tid + q * NT;
-      if (i < ndw) xs32[i] = v[q];
+      for (int q = 0; q < 4; ++q)
+        if (i + q * NT < ndw) xs32[i + q * NT] = v[q];
     }
   }
   if (!thresholds) {
-    for (int i = tid; i < Shared<NT>::kCopies * Shared<NT>::kStride; i += NT) sh.hist_rep[i] = 0;
-    for (int i = tid; i < 2 * W * 128; i += NT) (&sh.wave_hist[0][0][0])[i] = 0;
+    const int4 z = make_int4(0, 0, 0, 0);
+    int4* hr = reinterpret_cast<int4*>(sh.hist_rep);
+    for (int i = tid; i < S::kRep / 4; i += NT) hr[i] = z;
+    int4* wh = reinterpret_cast<int4*>(&sh.wave_hist[0][0][0]);
+    for (int i = tid; i < 2 * W * 128 / 4; i += NT) wh[i] = z;
   }
   __syncthreads();
 
-  // ---- pass 1: high-bit histogram, natural count, threshold counts
-  int nat = 0, gt0 = 0, eq0 = 0, gt1 = 0, eq1 = 0;
-  for (int s = 0; s < k.steps; ++s) {
-    const uint32_t wd = k.word(s, lane);
+  // ---- pass 1: high-bit histogram and natural count, or the threshold counts
+  if (thresholds) {
+    int c0 = 0, c1 = 0;  // gt | eq << 16
+    for (int s = 0; s < k.steps; ++s) {
+      const uint32_t wd = k.word(s, lane);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const bool valid = k.valid(s, lane, e);
-      const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
-      if (valid && !thresholds)
-        atomicAdd(&sh.hist_rep[(lane & 15) * Shared<NT>::kStride + (key >> 7)], 1);
-      nat += popc(__ballot(valid && key < a.k_tau));
-      if (thresholds) {
-        gt0 += popc(__ballot(valid && key > a.k_full));
-        eq0 += popc(__ballot(valid && key == a.k_full));
-        gt1 += popc(__ballot(valid && key > a.k_skip));
-        eq1 += popc(__ballot(valid && key == a.k_skip));
+      for (int e = 0; e < 2; ++e) {
+        const int key = k.valid(s, lane, e) ? (int)((e ? wd >> 16 : wd) & 0x7FFFu) : -1;
+        c0 += key > a.k_full ? 1 : key == a.k_full ? 0x10000 : 0;
+        c1 += key > a.k_skip ? 1 : key == a.k_skip ? 0x10000 : 0;
       }
     }
-  }
-  if (lane == 0) {
-    sh.wave_cnt[wave][0] = nat;
-    sh.wave_cnt[wave][1] = gt0;
-    sh.wave_cnt[wave][2] = eq0;
-    sh.wave_cnt[wave][3] = gt1;
-    sh.wave_cnt[wave][4] = eq1;
+    c0 = wave_sum(c0);
+    c1 = wave_sum(c1);
+    if (lane == 0) {
+      sh.wave_cnt[wave][0] = c0;
+      sh.wave_cnt[wave][1] = c1;
+    }
+    if (tid == 0) {
+      sh.sel[0] = Select{a.k_full, d};
+      sh.sel[1] = Select{a.k_skip, d};
+    }
+  } else {
+    int nat = 0;
+    for (int s = 0; s < k.steps; ++s) {
+      const uint32_t wd = k.word(s, lane);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bool valid = k.valid(s, lane, e);
+        const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
+        if (valid) atomicAdd(&sh.hist_rep[(lane & (S::kCopies - 1)) * S::kStride + (key >> 7)], 1);
+        nat += valid && key < a.k_tau;
+      }
+    }
+    nat = wave_sum(nat);
+    if (lane == 0) sh.wave_nat[wave] = nat;
   }
   __syncthreads();
 
-  Plan p;
-  if (thresholds) {
-    p.s0 = Select{a.k_full, d};
-    p.s1 = Select{a.k_skip, d};
-  } else {
-    int natural = 0;
-    for (int w = 0; w < W; ++w) natural += sh.wave_cnt[w][0];
-    int R[2];
-    if (a.mode == SPAX_MODE_TOPK) {
-      R[0] = a.n_full;
-      R[1] = a.n_full + a.n_approx;
-    } else {
-      const int n_skip = min(max(natural, a.n_lo), a.n_hi);
-      const int kept = d - n_skip;
-      // num <= den <= 65535 and kept <= 32768: fits 32 bits
-      const int n_approx = (int)(((uint32_t)a.num * (uint32_t)kept + (uint32_t)(a.den / 2)) /
-                                 (uint32_t)a.den);
-      R[0] = kept - n_approx;
-      R[1] = kept;
+  if (!thresholds) {
+    // ---- rank targets (wave 0) and the folded level-1 histogram (threads < 256)
+    if (wave == 0) {
+      int R0, R1;
+      if (a.mode == SPAX_MODE_TOPK) {
+        R0 = a.n_full;
+        R1 = a.n_full + a.n_approx;
+      } else {
+        const int natural = wave_sum(lane < W ? sh.wave_nat[lane] : 0);
+        const int n_skip = min(max(natural, a.n_lo), a.n_hi);
+        const int kept = d - n_skip;
+        // num <= den <= 65535 and kept <= 32768: fits 32 bits
+        const int n_approx = (int)(((uint32_t)a.num * (uint32_t)kept + (uint32_t)(a.den / 2)) /
+                                   (uint32_t)a.den);
+        R0 = kept - n_approx;
+        R1 = kept;
+      }
+      if (lane == 0) {
+        sh.R[0] = R0;
+        sh.R[1] = R1;
+      }
     }
-    // ---- fold the histogram copies
     for (int b = tid; b < 256; b += NT) {
       int t = 0;
 #pragma unroll
-      for (int c = 0; c < Shared<NT>::kCopies; ++c) t += sh.hist_rep[c * Shared<NT>::kStride + b];
+      for (int c = 0; c < S::kCopies; ++c) t += sh.hist_rep[c * S::kStride + b];
       sh.hist_hi[b] = t;
     }
     __syncthreads();
+    const int R[2] = {sh.R[0], sh.R[1]};
     // ---- level 1: bucket of each boundary (waves 0 and 1)
     if (wave < 2) {
       int local[4];
@@ -227,7 +249,8 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
     __syncthreads();
     const int b0 = sh.sel_b[0], b1 = sh.sel_b[1];
     // ---- pass 2: per-wave low-bit histograms inside the buckets; keys above the buckets
-    int above0 = 0, above1 = 0;
+    // (above0 | above1 << 16)
+    int above = 0;
     for (int s = 0; s < k.steps; ++s) {
       const uint32_t wd = k.word(s, lane);
 #pragma unroll
@@ -237,17 +260,18 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
         const int hi = valid ? key >> 7 : -2;
         if (hi == b0) atomicAdd(&sh.wave_hist[0][wave][key & 127], 1);
         if (hi == b1) atomicAdd(&sh.wave_hist[1][wave][key & 127], 1);
-        above0 += popc(__ballot(b0 >= 0 && hi > b0));
-        above1 += popc(__ballot(b1 >= 0 && hi > b1));
+        above += (b0 >= 0 && hi > b0 ? 1 : 0) + (b1 >= 0 && hi > b1 ? 0x10000 : 0);
       }
     }
+    above = wave_sum(above);
     __syncthreads();
     // ---- level 2: exact boundary keys (waves 0 and 1 sum the per-wave histograms)
     if (wave < 2) {
       int local[2] = {0, 0};
       for (int w = 0; w < W; ++w) {
-        local[0] += sh.wave_hist[wave][w][lane * 2];
-        local[1] += sh.wave_hist[wave][w][lane * 2 + 1];
+        const int2 h = *reinterpret_cast<const int2*>(&sh.wave_hist[wave][w][lane * 2]);
+        local[0] += h.x;
+        local[1] += h.y;
       }
       int v = -1, ab = 0;
       if (R[wave] > 0) suffix_find<2>(local, R[wave], sh.sel_above[wave], lane, &v, &ab);
@@ -256,99 +280,105 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
             R[wave] > 0 ? Select{(sh.sel_b[wave] << 7) | v, R[wave] - ab} : Select{0x8000, 0};
     }
     __syncthreads();
-    p.s0 = sh.sel[0];
-    p.s1 = sh.sel[1];
-    // ---- this wave's counts against the boundaries, from its own histograms
-    const int low0 = p.s0.kb & 127, low1 = p.s1.kb & 127;
-    const int c0a = sh.wave_hist[0][wave][lane * 2], c0b = sh.wave_hist[0][wave][lane * 2 + 1];
-    const int c1a = sh.wave_hist[1][wave][lane * 2], c1b = sh.wave_hist[1][wave][lane * 2 + 1];
-    const int G0 = wave_sum((lane * 2 > low0 ? c0a : 0) + (lane * 2 + 1 > low0 ? c0b : 0));
-    const int E0 = wave_sum((lane * 2 == low0 ? c0a : 0) + (lane * 2 + 1 == low0 ? c0b : 0));
-    const int G1 = wave_sum((lane * 2 > low1 ? c1a : 0) + (lane * 2 + 1 > low1 ? c1b : 0));
-    const int E1 = wave_sum((lane * 2 == low1 ? c1a : 0) + (lane * 2 + 1 == low1 ? c1b : 0));
+    // ---- this wave's (gt | eq << 16) against the boundaries, from its own histograms
+    const int low0 = sh.sel[0].kb & 127, low1 = sh.sel[1].kb & 127;
+    const int2 h0 = *reinterpret_cast<const int2*>(&sh.wave_hist[0][wave][lane * 2]);
+    const int2 h1 = *reinterpret_cast<const int2*>(&sh.wave_hist[1][wave][lane * 2]);
+    auto ge = [&](int bin, int c, int low) { return bin > low ? c : bin == low ? c << 16 : 0; };
+    const int c0 = wave_sum(ge(lane * 2, h0.x, low0) + ge(lane * 2 + 1, h0.y, low0));
+    const int c1 = wave_sum(ge(lane * 2, h1.x, low1) + ge(lane * 2 + 1, h1.y, low1));
     if (lane == 0) {
       // R == 0: boundary above every key, nothing greater or equal
-      sh.wave_cnt[wave][1] = R[0] > 0 ? above0 + G0 : 0;
-      sh.wave_cnt[wave][2] = R[0] > 0 ? E0 : 0;
-      sh.wave_cnt[wave][3] = R[1] > 0 ? above1 + G1 : 0;
-      sh.wave_cnt[wave][4] = R[1] > 0 ? E1 : 0;
+      sh.wave_cnt[wave][0] = R[0] > 0 ? c0 + (above & 0xFFFF) : 0;
+      sh.wave_cnt[wave][1] = R[1] > 0 ? c1 + (above >> 16) : 0;
     }
     __syncthreads();
   }
-  // totals: a wave's selected ties are clamp(m - ties before it, 0, its ties)
-  int eqb0 = 0, eqb1 = 0;
-  p.n_full = 0;
-  p.n_kept = 0;
-  for (int w = 0; w < W; ++w) {
-    const int g0 = sh.wave_cnt[w][1], e0 = sh.wave_cnt[w][2];
-    const int g1 = sh.wave_cnt[w][3], e1 = sh.wave_cnt[w][4];
-    p.n_full += g0 + min(max(p.s0.m - eqb0, 0), e0);
-    p.n_kept += g1 + min(max(p.s1.m - eqb1, 0), e1);
-    eqb0 += e0;
-    eqb1 += e1;
+
+  // ---- rank bases of every wave (wave 0, lane w <-> wave w).  Ties are taken in index
+  // order, so a wave's selected ties are clamp(m - ties before it, 0, its ties).
+  Plan p;
+  p.s0 = sh.sel[0];
+  p.s1 = sh.sel[1];
+  if (wave == 0) {
+    const bool on = lane < W;
+    const int w0 = on ? sh.wave_cnt[lane][0] : 0, w1 = on ? sh.wave_cnt[lane][1] : 0;
+    const int g0 = w0 & 0xFFFF, e0 = w0 >> 16, g1 = w1 & 0xFFFF, e1 = w1 >> 16;
+    const int eb0 = wave_scan(e0) - e0, eb1 = wave_scan(e1) - e1;  // up to 32768 each
+    const int f = g0 + min(max(p.s0.m - eb0, 0), e0);
+    const int kk = g1 + min(max(p.s1.m - eb1, 0), e1);
+    const int fs = wave_scan(f), ks = wave_scan(kk);
+    if (on) {
+      sh.wave_base[lane][0] = fs - f;
+      sh.wave_base[lane][1] = (ks - kk) - (fs - f);  // FULL is a subset of kept
+      sh.wave_base[lane][2] = eb0;
+      sh.wave_base[lane][3] = eb1;
+    }
+    if (lane == 0) {
+      sh.totals[0] = __builtin_amdgcn_readlane(fs, 63);
+      sh.totals[1] = __builtin_amdgcn_readlane(ks, 63);
+    }
   }
+  __syncthreads();
+  p.n_full = sh.totals[0];
+  p.n_kept = sh.totals[1];
   return p;
 }
 
-// Pass 3: every FULL / APPROX channel goes to emit_list(tier, rank, j, raw) with its rank
-// in the ascending list; emit_tier(j, tier) sees every channel.  Uses the per-wave counts
-// build_plan left in sh.wave_cnt; no barrier.
+// Pass 3: every FULL / APPROX channel goes to emit_list(tier, rank, j, raw) with its rank in
+// the ascending list; emit_tier(j, t_even, t_odd, n) sees each lane's pair of channels
+// (j even, n = 2, or 1 when j + 1 is past the wave's range).  Uses build_plan's bases; no
+// barrier.
 template <int NT, class EmitList, class EmitTier>
 __device__ __forceinline__ void emit(const Shared<NT>& sh, const Keys& k, const Plan& p,
                                      EmitList emit_list, EmitTier emit_tier) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int eqb0 = 0, eqb1 = 0, fbase = 0, kbase = 0;
-  for (int w = 0; w < wave; ++w) {
-    const int g0 = sh.wave_cnt[w][1], e0 = sh.wave_cnt[w][2];
-    const int g1 = sh.wave_cnt[w][3], e1 = sh.wave_cnt[w][4];
-    fbase += g0 + min(max(p.s0.m - eqb0, 0), e0);
-    kbase += g1 + min(max(p.s1.m - eqb1, 0), e1);
-    eqb0 += e0;
-    eqb1 += e1;
-  }
-  // FULL is a subset of kept, so APPROX before this wave = kept before - FULL before.
-  // Within a step the order is lane-major: channel 2l, 2l+1, 2l+2, ...  so the channels
-  // before (l, e) are both channels of lanes < l, plus the even channel of lane l if e = 1.
-  int fpos = fbase, apos = kbase - fbase;
-  const uint64_t lt = (1ull << lane) - 1ull;
+  int fpos = sh.wave_base[wave][0], apos = sh.wave_base[wave][1];
+  int eqb0 = sh.wave_base[wave][2], eqb1 = sh.wave_base[wave][3];
+  const Select s0 = p.s0, s1 = p.s1;
+  // Within a step the order is lane-major: channel 2l, 2l+1, 2l+2, ...  so the channels before
+  // (l, e) are both channels of lanes < l, plus the even channel of lane l if e = 1.
   for (int s = 0; s < k.steps; ++s) {
     const uint32_t wd = k.word(s, lane);
-    const uint32_t raw[2] = {wd & 0xFFFFu, wd >> 16};
-    int key[2];
-    bool val[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      val[e] = k.valid(s, lane, e);
-      key[e] = val[e] ? (int)(raw[e] & 0x7FFFu) : -1;
+    const uint32_t raw0 = wd & 0xFFFFu, raw1 = wd >> 16;
+    const bool v0 = k.valid(s, lane, 0), v1 = k.valid(s, lane, 1);
+    const int key0 = v0 ? (int)(raw0 & 0x7FFFu) : -1;
+    const int key1 = v1 ? (int)(raw1 & 0x7FFFu) : -1;
+    bool f0, f1, a0, a1;
+    const bool tie = key0 == s0.kb || key1 == s0.kb || key0 == s1.kb || key1 == s1.kb;
+    if (__ballot(tie) == 0) {  // no boundary key in this step: plain comparisons
+      f0 = key0 > s0.kb;
+      f1 = key1 > s0.kb;
+      a0 = !f0 && key0 > s1.kb;
+      a1 = !f1 && key1 > s1.kb;
+    } else {
+      const uint64_t q0e = __ballot(key0 == s0.kb), q0o = __ballot(key1 == s0.kb);
+      const uint64_t q1e = __ballot(key0 == s1.kb), q1o = __ballot(key1 == s1.kb);
+      const int r0 = eqb0 + (int)lanes_below(q0e) + (int)lanes_below(q0o);  // ties before even
+      const int r1 = eqb1 + (int)lanes_below(q1e) + (int)lanes_below(q1o);
+      f0 = key0 > s0.kb || (key0 == s0.kb && r0 < s0.m);
+      f1 = key1 > s0.kb || (key1 == s0.kb && r0 + (key0 == s0.kb) < s0.m);
+      const bool k0 = key0 > s1.kb || (key0 == s1.kb && r1 < s1.m);
+      const bool k1 = key1 > s1.kb || (key1 == s1.kb && r1 + (key0 == s1.kb) < s1.m);
+      a0 = k0 && !f0;
+      a1 = k1 && !f1;
+      eqb0 += popc(q0e) + popc(q0o);
+      eqb1 += popc(q1e) + popc(q1o);
     }
-    const uint64_t q0e = __ballot(key[0] == p.s0.kb), q0o = __ballot(key[1] == p.s0.kb);
-    const uint64_t q1e = __ballot(key[0] == p.s1.kb), q1o = __ballot(key[1] == p.s1.kb);
-    const int r0 = eqb0 + popc(q0e & lt) + popc(q0o & lt);  // ties before the even channel
-    const int r1 = eqb1 + popc(q1e & lt) + popc(q1o & lt);
-    bool isF[2], isA[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int t0 = r0 + (e ? (key[0] == p.s0.kb) : 0);
-      const int t1 = r1 + (e ? (key[0] == p.s1.kb) : 0);
-      isF[e] = key[e] > p.s0.kb || (key[e] == p.s0.kb && t0 < p.s0.m);
-      const bool kept = key[e] > p.s1.kb || (key[e] == p.s1.kb && t1 < p.s1.m);
-      isA[e] = kept && !isF[e];
-    }
-    eqb0 += popc(q0e) + popc(q0o);
-    eqb1 += popc(q1e) + popc(q1o);
-    const uint64_t bfe = __ballot(isF[0]), bfo = __ballot(isF[1]);
-    const uint64_t bae = __ballot(isA[0]), bao = __ballot(isA[1]);
-    const int fr = fpos + popc(bfe & lt) + popc(bfo & lt);
-    const int ar = apos + popc(bae & lt) + popc(bao & lt);
+    const uint64_t bfe = __ballot(f0), bfo = __ballot(f1);
+    const uint64_t bae = __ballot(a0), bao = __ballot(a1);
+    const int fr = fpos + (int)lanes_below(bfe) + (int)lanes_below(bfo);
+    const int ar = apos + (int)lanes_below(bae) + (int)lanes_below(bao);
     const int jb = k.j0 + k.off(s, lane, 0);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int fe = fr + (e ? (int)isF[0] : 0);
-      const int ae = ar + (e ? (int)isA[0] : 0);
-      if (isF[e]) emit_list(SPAX_TIER_FULL, fe, jb + e, raw[e]);
-      if (isA[e]) emit_list(SPAX_TIER_APPROX, ae, jb + e, raw[e]);
-      if (val[e]) emit_tier(jb + e, isF[e] ? SPAX_TIER_FULL : isA[e] ? SPAX_TIER_APPROX : SPAX_TIER_SKIP);
+    if (f0) emit_list(SPAX_TIER_FULL, fr, jb, raw0);
+    if (a0) emit_list(SPAX_TIER_APPROX, ar, jb, raw0);
+    if (f1) emit_list(SPAX_TIER_FULL, fr + (int)f0, jb + 1, raw1);
+    if (a1) emit_list(SPAX_TIER_APPROX, ar + (int)a0, jb + 1, raw1);
+    if (v0) {
+      const uint32_t t0 = f0 ? SPAX_TIER_FULL : a0 ? SPAX_TIER_APPROX : SPAX_TIER_SKIP;
+      const uint32_t t1 = f1 ? SPAX_TIER_FULL : a1 ? SPAX_TIER_APPROX : SPAX_TIER_SKIP;
+      emit_tier(jb, t0, t1, v1 ? 2 : 1);
     }
     fpos += popc(bfe) + popc(bfo);
     apos += popc(bae) + popc(bao);

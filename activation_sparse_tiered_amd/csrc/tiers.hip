@@ -4,34 +4,43 @@
 // section 2.1 -- clipped natural sparsity then TopK, O(d) per token.  The selection logic
 // lives in mask_core.h; this kernel writes the tier bytes, both ascending index lists and
 // the counts to global memory.
+#include <cstdlib>
+
 #include "mask_core.h"
 
 namespace spax {
 namespace {
 
-constexpr int kTierThreads = 1024;
+constexpr int kTierThreadsDefault = 1024;
 
-__global__ __launch_bounds__(kTierThreads) void build_tiers_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void build_tiers_kernel(
     TierArgs a, const uint16_t* __restrict__ x, uint8_t* __restrict__ tier,
     int32_t* __restrict__ full_idx, int32_t* __restrict__ approx_idx,
     int32_t* __restrict__ counts, float4* __restrict__ y_zero, int32_t n_zero4) {
-  __shared__ mask::Shared<kTierThreads> sh;
+  __shared__ mask::Shared<NT> sh;
   __shared__ uint32_t xs32[SPAX_MAX_DIN / 2];
   const int tid = threadIdx.x;
 
   // Side job: clear the fp32 output the following GEMV accumulates into.
-  for (int i = tid; i < n_zero4; i += kTierThreads) y_zero[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = tid; i < n_zero4; i += NT) y_zero[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 
   mask::Keys k;
-  const mask::Plan p = mask::build_plan<kTierThreads, SPAX_MAX_DIN>(sh, k, xs32, x, a);
-  mask::emit<kTierThreads>(
+  const mask::Plan p = mask::build_plan<NT, SPAX_MAX_DIN>(sh, k, xs32, x, a);
+  const bool tier_even = ((uintptr_t)tier & 1) == 0;  // channel pairs start at even j
+  mask::emit<NT>(
       sh, k, p,
       [&](int t, int rank, int j, uint32_t) {
         if (t == SPAX_TIER_FULL) full_idx[rank] = j;
         else approx_idx[rank] = j;
       },
-      [&](int j, int t) {
-        if (tier) tier[j] = (uint8_t)t;
+      [&](int j, uint32_t t0, uint32_t t1, int n) {
+        if (!tier) return;
+        if (n == 2 && tier_even) *reinterpret_cast<uint16_t*>(tier + j) = (uint16_t)(t0 | t1 << 8);
+        else {
+          tier[j] = (uint8_t)t0;
+          if (n == 2) tier[j + 1] = (uint8_t)t1;
+        }
       });
   if (tid == 0) {
     counts[0] = p.n_full;
@@ -46,8 +55,22 @@ int launch_build_tiers(const TierArgs& a, const uint16_t* x, uint8_t* tier, int3
                        int32_t* approx_idx, int32_t* counts, float* y_zero, int64_t n_zero,
                        hipStream_t s) {
   const int32_t n4 = y_zero ? (int32_t)((n_zero + 3) / 4) : 0;
-  hipLaunchKernelGGL(build_tiers_kernel, dim3(1), dim3(kTierThreads), 0, s, a, x, tier, full_idx,
-                     approx_idx, counts, reinterpret_cast<float4*>(y_zero), n4);
+  float4* yz = reinterpret_cast<float4*>(y_zero);
+  // Workgroup size: the kernel is issue- and latency-bound inside one CU.
+  static const int nt = [] {
+    const char* v = getenv("SPAX_TIER_THREADS");
+    const int t = v ? atoi(v) : 0;
+    return (t == 256 || t == 512 || t == 1024) ? t : kTierThreadsDefault;
+  }();
+  if (nt == 256)
+    hipLaunchKernelGGL(build_tiers_kernel<256>, dim3(1), dim3(256), 0, s, a, x, tier, full_idx,
+                       approx_idx, counts, yz, n4);
+  else if (nt == 512)
+    hipLaunchKernelGGL(build_tiers_kernel<512>, dim3(1), dim3(512), 0, s, a, x, tier, full_idx,
+                       approx_idx, counts, yz, n4);
+  else
+    hipLaunchKernelGGL(build_tiers_kernel<1024>, dim3(1), dim3(1024), 0, s, a, x, tier, full_idx,
+                       approx_idx, counts, yz, n4);
   SPAX_HIP_CHECK(hipGetLastError());
   return SPAX_OK;
 }
