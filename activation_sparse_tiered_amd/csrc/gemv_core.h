@@ -111,116 +111,94 @@ struct LdsList {
   }
 };
 
-// FULL columns [b, e) of `src` into acc / zsum.  `row` is the lane's first row (or 0 for
-// lanes past the last row, which read valid memory and are never stored).
-template <int FMT, class Src>
-__device__ __forceinline__ void stream_full(const Shape& sh, const uint8_t* __restrict__ packed,
-                                            int row, int b, int e, const Src& src,
-                                            float (&acc)[8], float& zsum) {
-  if (FMT == SPAX_FMT_FP16) {
-    const uint32_t loff = (uint32_t)row * 2u;
-    int i = b;
-    for (; i + kUnroll <= e; i += kUnroll) {
-      int j[kUnroll];
-      float xv[kUnroll];
-      uint4 v[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) src.get(i + u, j[u], xv[u]);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        v[u] = *reinterpret_cast<const uint4*>(packed + (int64_t)j[u] * sh.stride_F + loff);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) fma_fp16x8(acc, xv[u], v[u]);
-    }
-    for (; i < e; ++i) {
-      int j;
-      float xv;
-      src.get(i, j, xv);
-      const uint4 v = *reinterpret_cast<const uint4*>(packed + (int64_t)j * sh.stride_F + loff);
-      fma_fp16x8(acc, xv, v);
-    }
-  } else {
-    const uint32_t loff = (uint32_t)row / 2u;
-    const uint32_t szoff = (uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u;
-    int i = b;
-    for (; i + kUnroll <= e; i += kUnroll) {
-      int j[kUnroll];
-      float xv[kUnroll];
-      uint32_t c[kUnroll], sz[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) src.get(i + u, j[u], xv[u]);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint8_t* col = packed + (int64_t)j[u] * sh.stride_F;
-        c[u] = *reinterpret_cast<const uint32_t*>(col + loff);
-        sz[u] = *reinterpret_cast<const uint32_t*>(col + szoff);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        fma_int4x8(acc, xv[u] * half_lo(sz[u]), c[u]);
-        zsum = fmaf(xv[u], half_hi(sz[u]), zsum);
-      }
-    }
-    for (; i < e; ++i) {
-      int j;
-      float xv;
-      src.get(i, j, xv);
-      const uint8_t* col = packed + (int64_t)j * sh.stride_F;
-      const uint32_t c = *reinterpret_cast<const uint32_t*>(col + loff);
-      const uint32_t sz = *reinterpret_cast<const uint32_t*>(col + szoff);
-      fma_int4x8(acc, xv * half_lo(sz), c);
-      zsum = fmaf(xv, half_hi(sz), zsum);
-    }
-  }
-}
-
-// APPROX (two-bit) columns [b, e) of `src`.
-template <class Src>
-__device__ __forceinline__ void stream_approx(const Shape& sh, const uint8_t* __restrict__ packed,
-                                              int row, int b, int e, const Src& src,
-                                              float (&acc)[8], float& zsum) {
+// FULL columns [fb, fe) of `srcF` and APPROX (two-bit) columns [ab, ae) of `srcA` into
+// acc / zsum.  Each round issues the loads of up to kUnroll FULL and kUnroll APPROX columns
+// back to back (the counts are wave-uniform, so the guards are scalar branches) and only then
+// waits and multiplies: a wave's few columns cost one or two memory round trips, not one per
+// column.  `row` is the lane's first row (or 0 for lanes past the last row, which read valid
+// memory and are never stored).
+template <int FMT, class SrcF, class SrcA>
+__device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* __restrict__ packed,
+                                               int row, int fb, int fe, const SrcF& srcF, int ab,
+                                               int ae, const SrcA& srcA, float (&acc)[8],
+                                               float& zsum) {
   const uint8_t* regionA = packed + sh.off_A;
-  const uint32_t loff = (uint32_t)row / 4u;
-  const uint32_t szoff = (uint32_t)(sh.T / 4) + (uint32_t)(row / sh.approx_group) * 4u;
-  int i = b;
-  for (; i + kUnroll <= e; i += kUnroll) {
-    int j[kUnroll];
-    float xv[kUnroll];
-    uint32_t c[kUnroll], sz[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) src.get(i + u, j[u], xv[u]);
+  const uint32_t loffA = (uint32_t)row / 4u;
+  const uint32_t szoffA = (uint32_t)(sh.T / 4) + (uint32_t)(row / sh.approx_group) * 4u;
+  const uint32_t loffF = FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u;
+  const uint32_t szoffF = (uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u;
+  int fi = fb, ai = ab;
+  while (fi < fe || ai < ae) {
+    const int nf = min(fe - fi, kUnroll), na = min(ae - ai, kUnroll);  // may be <= 0
+    int jf[kUnroll], ja[kUnroll];
+    float xf[kUnroll], xa[kUnroll];
+    uint4 vf[kUnroll];
+    uint32_t cf[kUnroll], sf[kUnroll], ca[kUnroll], sa[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint8_t* col = regionA + (int64_t)j[u] * sh.stride_A;
-      c[u] = (uint32_t)*reinterpret_cast<const uint16_t*>(col + loff);
-      sz[u] = *reinterpret_cast<const uint32_t*>(col + szoff);
+      if (u < nf) srcF.get(fi + u, jf[u], xf[u]);
+      if (u < na) srcA.get(ai + u, ja[u], xa[u]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      fma_int2x8(acc, xv[u] * half_lo(sz[u]), c[u]);
-      zsum = fmaf(xv[u], half_hi(sz[u]), zsum);
+      if (u < nf) {
+        const uint8_t* col = packed + (int64_t)jf[u] * sh.stride_F;
+        if (FMT == SPAX_FMT_FP16) {
+          vf[u] = *reinterpret_cast<const uint4*>(col + loffF);
+        } else {
+          cf[u] = *reinterpret_cast<const uint32_t*>(col + loffF);
+          sf[u] = *reinterpret_cast<const uint32_t*>(col + szoffF);
+        }
+      }
     }
-  }
-  for (; i < e; ++i) {
-    int j;
-    float xv;
-    src.get(i, j, xv);
-    const uint8_t* col = regionA + (int64_t)j * sh.stride_A;
-    const uint32_t c = (uint32_t)*reinterpret_cast<const uint16_t*>(col + loff);
-    const uint32_t sz = *reinterpret_cast<const uint32_t*>(col + szoff);
-    fma_int2x8(acc, xv * half_lo(sz), c);
-    zsum = fmaf(xv, half_hi(sz), zsum);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u < na) {
+        const uint8_t* col = regionA + (int64_t)ja[u] * sh.stride_A;
+        ca[u] = (uint32_t)*reinterpret_cast<const uint16_t*>(col + loffA);
+        sa[u] = *reinterpret_cast<const uint32_t*>(col + szoffA);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u < nf) {
+        if (FMT == SPAX_FMT_FP16) {
+          fma_fp16x8(acc, xf[u], vf[u]);
+        } else {
+          fma_int4x8(acc, xf[u] * half_lo(sf[u]), cf[u]);
+          zsum = fmaf(xf[u], half_hi(sf[u]), zsum);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u < na) {
+        fma_int2x8(acc, xa[u] * half_lo(sa[u]), ca[u]);
+        zsum = fmaf(xa[u], half_hi(sa[u]), zsum);
+      }
+    }
+    fi += max(nf, 0);
+    ai += max(na, 0);
   }
 }
 
-// Split [b, e) evenly over the workgroup's waves.
+// First item of part c when n items are split into `parts` contiguous parts.  n <= 32768
+// and parts <= 2048, so 32-bit unsigned arithmetic suffices (a 64-bit division costs a
+// wavefront ~130 scalar instructions, and every wave of the CU shares one scalar unit).
+__device__ __forceinline__ int split_at(int n, int c, int parts) {
+  return (int)((uint32_t)n * (uint32_t)c / (uint32_t)parts);
+}
+
+// Split [b, e) evenly over the workgroup's NW waves.
+template <int NW>
 __device__ __forceinline__ void wave_range(int b, int e, int wave, int& wb, int& we) {
-  wb = b + (e - b) * wave / kWaves;
-  we = b + (e - b) * (wave + 1) / kWaves;
+  wb = b + (e - b) * wave / NW;
+  we = b + (e - b) * (wave + 1) / NW;
 }
 
-// Reduce the waves' partial rows through LDS, then write (one chunk) or atomically add
+// Reduce the NW waves' partial rows through LDS, then write (one chunk) or atomically add
 // (several chunks, y zeroed beforehand in stream order) the tile into y.
+template <int NW>
 __device__ __forceinline__ void finish_tile(float (*red)[kTileRows], const float (&acc)[8],
                                             float zsum, int wave, int lane, int row0, int T,
                                             int n_chunks, float* __restrict__ y) {
@@ -229,15 +207,16 @@ __device__ __forceinline__ void finish_tile(float (*red)[kTileRows], const float
   dst[0] = make_float4(acc[0] + zsum, acc[1] + zsum, acc[2] + zsum, acc[3] + zsum);
   dst[1] = make_float4(acc[4] + zsum, acc[5] + zsum, acc[6] + zsum, acc[7] + zsum);
   __syncthreads();
-  float sum = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) sum += red[w][tid];
   const int grow = row0 + tid;
-  if (grow >= T) return;
-  // Several chunks meet through hardware fp32 atomics at device scope; y is read only after
-  // the kernel ends, so no device-scope fence is needed.
-  if (n_chunks == 1) y[grow] = sum;
-  else unsafeAtomicAdd(&y[grow], sum);
+  if (tid < kTileRows && grow < T) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += red[w][tid];
+    // Several chunks meet through hardware fp32 atomics at device scope; y is read only after
+    // the kernel ends, so no device-scope fence is needed.
+    if (n_chunks == 1) y[grow] = sum;
+    else unsafeAtomicAdd(&y[grow], sum);
+  }
 }
 
 }  // namespace gemv

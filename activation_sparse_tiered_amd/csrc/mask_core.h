@@ -23,6 +23,8 @@
 // step without boundary keys skips the tie ranking.
 #pragma once
 
+#include <climits>
+
 #include "common.h"
 
 namespace spax {
@@ -45,7 +47,8 @@ struct Shared {
   int hist_hi[256];
   int wave_cnt[W][2];   // (gt | eq << 16) against the FULL and the kept boundary
   int wave_nat[W];      // natural count (keys below K(tau))
-  int wave_base[W][4];  // FULL rank base, APPROX rank base, ties before (FULL, kept)
+  int wave_base[W + 1][4];  // FULL rank base, APPROX rank base, ties before (FULL, kept);
+                            // row W holds the totals
   int totals[2];        // n_full, n_kept
   int R[2];
   int sel_b[2], sel_above[2];
@@ -302,13 +305,13 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
   p.s1 = sh.sel[1];
   if (wave == 0) {
     const bool on = lane < W;
-    const int w0 = on ? sh.wave_cnt[lane][0] : 0, w1 = on ? sh.wave_cnt[lane][1] : 0;
+    const int w0 = on ? sh.wave_cnt[lane][0] : 0, w1 = on ? sh.wave_cnt[lane][1] : 0;  // lane W: 0
     const int g0 = w0 & 0xFFFF, e0 = w0 >> 16, g1 = w1 & 0xFFFF, e1 = w1 >> 16;
     const int eb0 = wave_scan(e0) - e0, eb1 = wave_scan(e1) - e1;  // up to 32768 each
     const int f = g0 + min(max(p.s0.m - eb0, 0), e0);
     const int kk = g1 + min(max(p.s1.m - eb1, 0), e1);
     const int fs = wave_scan(f), ks = wave_scan(kk);
-    if (on) {
+    if (lane <= W) {
       sh.wave_base[lane][0] = fs - f;
       sh.wave_base[lane][1] = (ks - kk) - (fs - f);  // FULL is a subset of kept
       sh.wave_base[lane][2] = eb0;
@@ -325,21 +328,30 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
   return p;
 }
 
-// Pass 3: every FULL / APPROX channel goes to emit_list(tier, rank, j, raw) with its rank in
-// the ascending list; emit_tier(j, t_even, t_odd, n) sees each lane's pair of channels
-// (j even, n = 2, or 1 when j + 1 is past the wave's range).  Uses build_plan's bases; no
+// Pass 3: FULL / APPROX channels go to emit_list(tier, rank, j, raw) with their rank in the
+// ascending list; emit_tier(j, t_even, t_odd, n) sees each lane's pair of channels (j even,
+// n = 2, or 1 when j + 1 is past the wave's range).  Only ranks in [f_lo, f_hi) (FULL) and
+// [a_lo, a_hi) (APPROX) are wanted.  Unless every channel must reach emit_tier
+// (all_channels), a wave whose rank ranges miss both windows does nothing, and a wave stops
+// once it is past both (ranks grow with the channel index).  Uses build_plan's bases; no
 // barrier.
 template <int NT, class EmitList, class EmitTier>
 __device__ __forceinline__ void emit(const Shared<NT>& sh, const Keys& k, const Plan& p,
+                                     bool all_channels, int f_lo, int f_hi, int a_lo, int a_hi,
                                      EmitList emit_list, EmitTier emit_tier) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int fpos = sh.wave_base[wave][0], apos = sh.wave_base[wave][1];
   int eqb0 = sh.wave_base[wave][2], eqb1 = sh.wave_base[wave][3];
+  const int f_end = sh.wave_base[wave + 1][0], a_end = sh.wave_base[wave + 1][1];
+  const bool wantF = fpos < f_hi && f_end > f_lo && f_lo < f_hi;
+  const bool wantA = apos < a_hi && a_end > a_lo && a_lo < a_hi;
+  if (!all_channels && !wantF && !wantA) return;
+  if (all_channels) f_hi = a_hi = INT_MAX;
   const Select s0 = p.s0, s1 = p.s1;
   // Within a step the order is lane-major: channel 2l, 2l+1, 2l+2, ...  so the channels before
   // (l, e) are both channels of lanes < l, plus the even channel of lane l if e = 1.
-  for (int s = 0; s < k.steps; ++s) {
+  for (int s = 0; s < k.steps && (fpos < f_hi || apos < a_hi); ++s) {
     const uint32_t wd = k.word(s, lane);
     const uint32_t raw0 = wd & 0xFFFFu, raw1 = wd >> 16;
     const bool v0 = k.valid(s, lane, 0), v1 = k.valid(s, lane, 1);

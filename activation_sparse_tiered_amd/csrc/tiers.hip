@@ -4,6 +4,7 @@
 // section 2.1 -- clipped natural sparsity then TopK, O(d) per token.  The selection logic
 // lives in mask_core.h; this kernel writes the tier bytes, both ascending index lists and
 // the counts to global memory.
+#include <climits>
 #include <cstdlib>
 
 #include "mask_core.h"
@@ -22,14 +23,11 @@ __global__ __launch_bounds__(NT) void build_tiers_kernel(
   __shared__ uint32_t xs32[SPAX_MAX_DIN / 2];
   const int tid = threadIdx.x;
 
-  // Side job: clear the fp32 output the following GEMV accumulates into.
-  for (int i = tid; i < n_zero4; i += NT) y_zero[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-
   mask::Keys k;
   const mask::Plan p = mask::build_plan<NT, SPAX_MAX_DIN>(sh, k, xs32, x, a);
   const bool tier_even = ((uintptr_t)tier & 1) == 0;  // channel pairs start at even j
   mask::emit<NT>(
-      sh, k, p,
+      sh, k, p, true, 0, INT_MAX, 0, INT_MAX,
       [&](int t, int rank, int j, uint32_t) {
         if (t == SPAX_TIER_FULL) full_idx[rank] = j;
         else approx_idx[rank] = j;
@@ -47,6 +45,9 @@ __global__ __launch_bounds__(NT) void build_tiers_kernel(
     counts[1] = p.n_kept - p.n_full;
     counts[2] = a.d - p.n_kept;
   }
+  // Side job: clear the fp32 output the following GEMV accumulates into.  Issued last, so
+  // that waiting for the activation loads never includes these stores.
+  for (int i = tid; i < n_zero4; i += NT) y_zero[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 }  // namespace
