@@ -68,7 +68,8 @@ __device__ __forceinline__ void fma_int4x8(float (&acc)[8], float a, uint32_t c)
   acc[7] = fmaf(a, (float)(hi >> 24), acc[7]);
 }
 
-// 8 two-bit codes (row 4k+i in bits [2i+1:2i] of byte k) scaled by a.
+// 8 two-bit codes (row 4k+i in bits [2i+1:2i] of byte k; only bits 0..15 of c are read)
+// scaled by a.
 __device__ __forceinline__ void fma_int2x8(float (&acc)[8], float a, uint32_t c) {
   const uint32_t t0 = c & 0x0303u;          // rows 0 (byte 0) and 4 (byte 1)
   const uint32_t t1 = (c >> 2) & 0x0303u;   // rows 1, 5
@@ -115,34 +116,43 @@ struct LdsList {
 // acc / zsum.  Each round issues the loads of up to kUnroll FULL and kUnroll APPROX columns
 // back to back (the counts are wave-uniform, so the guards are scalar branches) and only then
 // waits and multiplies: a wave's few columns cost one or two memory round trips, not one per
-// column.  `row` is the lane's first row (or 0 for lanes past the last row, which read valid
-// memory and are never stored).
+// column.  Slots past the end keep zero data and a zero activation and are multiplied
+// anyway: with conditional multiplies the compiler's wait tracking cannot tell which loads of
+// the previous round are still in flight and makes every load wait for all earlier ones.
+// `row` is the lane's first row (or 0 for lanes past the last row, which read valid memory
+// and are never stored).
 template <int FMT, class SrcF, class SrcA>
 __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* __restrict__ packed,
                                                int row, int fb, int fe, const SrcF& srcF, int ab,
                                                int ae, const SrcA& srcA, float (&acc)[8],
                                                float& zsum) {
   const uint8_t* regionA = packed + sh.off_A;
-  const uint32_t loffA = (uint32_t)row / 4u;
+  // A lane's 2 bytes of two-bit codes are read as the aligned dword that holds them (a
+  // 16-bit load would be widened right after it is issued, which makes it wait).
+  const uint32_t loffA4 = ((uint32_t)row / 4u) & ~3u;
+  const uint32_t shA = (((uint32_t)row / 4u) & 2u) * 8u;
   const uint32_t szoffA = (uint32_t)(sh.T / 4) + (uint32_t)(row / sh.approx_group) * 4u;
   const uint32_t loffF = FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u;
   const uint32_t szoffF = (uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u;
   int fi = fb, ai = ab;
   while (fi < fe || ai < ae) {
     const int nf = min(fe - fi, kUnroll), na = min(ae - ai, kUnroll);  // may be <= 0
-    int jf[kUnroll], ja[kUnroll];
     float xf[kUnroll], xa[kUnroll];
     uint4 vf[kUnroll];
     uint32_t cf[kUnroll], sf[kUnroll], ca[kUnroll], sa[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (u < nf) srcF.get(fi + u, jf[u], xf[u]);
-      if (u < na) srcA.get(ai + u, ja[u], xa[u]);
+      xf[u] = 0.0f;
+      xa[u] = 0.0f;
+      vf[u] = make_uint4(0u, 0u, 0u, 0u);
+      cf[u] = sf[u] = ca[u] = sa[u] = 0u;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (u < nf) {
-        const uint8_t* col = packed + (int64_t)jf[u] * sh.stride_F;
+        int j;
+        srcF.get(fi + u, j, xf[u]);
+        const uint8_t* col = packed + (int64_t)j * sh.stride_F;
         if (FMT == SPAX_FMT_FP16) {
           vf[u] = *reinterpret_cast<const uint4*>(col + loffF);
         } else {
@@ -154,28 +164,26 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (u < na) {
-        const uint8_t* col = regionA + (int64_t)ja[u] * sh.stride_A;
-        ca[u] = (uint32_t)*reinterpret_cast<const uint16_t*>(col + loffA);
+        int j;
+        srcA.get(ai + u, j, xa[u]);
+        const uint8_t* col = regionA + (int64_t)j * sh.stride_A;
+        ca[u] = *reinterpret_cast<const uint32_t*>(col + loffA4);
         sa[u] = *reinterpret_cast<const uint32_t*>(col + szoffA);
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (u < nf) {
-        if (FMT == SPAX_FMT_FP16) {
-          fma_fp16x8(acc, xf[u], vf[u]);
-        } else {
-          fma_int4x8(acc, xf[u] * half_lo(sf[u]), cf[u]);
-          zsum = fmaf(xf[u], half_hi(sf[u]), zsum);
-        }
+      if (FMT == SPAX_FMT_FP16) {
+        fma_fp16x8(acc, xf[u], vf[u]);
+      } else {
+        fma_int4x8(acc, xf[u] * half_lo(sf[u]), cf[u]);
+        zsum = fmaf(xf[u], half_hi(sf[u]), zsum);
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (u < na) {
-        fma_int2x8(acc, xa[u] * half_lo(sa[u]), ca[u]);
-        zsum = fmaf(xa[u], half_hi(sa[u]), zsum);
-      }
+      fma_int2x8(acc, xa[u] * half_lo(sa[u]), ca[u] >> shA);
+      zsum = fmaf(xa[u], half_hi(sa[u]), zsum);
     }
     fi += max(nf, 0);
     ai += max(na, 0);

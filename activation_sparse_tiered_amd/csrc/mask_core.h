@@ -127,11 +127,12 @@ struct Plan {
   int n_full, n_kept;
 };
 
-// Load x into LDS (xs32: roundup(d, 2) halves), find both boundaries and every wave's rank
-// bases (sh.wave_base).  Contains the barriers it needs and ends with one.  d <= MAXD.
+// Stage 1: load x into LDS (xs32: roundup(d, 2) halves), pass 1 and level 1.  Afterwards
+// sh.sel holds the exact boundaries for THRESHOLD; otherwise sh.R holds the rank targets and
+// sh.sel_b / sh.sel_above the level-1 buckets (-1: R == 0).  Ends with a barrier.  d <= MAXD.
 template <int NT, int MAXD>
-__device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs32,
-                                           const uint16_t* __restrict__ x, const TierArgs& a) {
+__device__ __forceinline__ void plan_stage1(Shared<NT>& sh, Keys& k, uint32_t* xs32,
+                                            const uint16_t* __restrict__ x, const TierArgs& a) {
   constexpr int W = NT / 64;
   using S = Shared<NT>;
   static_assert(MAXD <= 32768 && NT >= 256, "per-wave counts are packed in 16 bits");
@@ -158,6 +159,9 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
       for (int q = 0; q < 4; ++q)
         if (i + q * NT < ndw) xs32[i + q * NT] = v[q];
     }
+    // Every load has landed: say so to the compiler's wait tracking, so that loads issued
+    // after the mask passes are not made to wait for these conditional ones.
+    __builtin_amdgcn_s_waitcnt(0);
   }
   if (!thresholds) {
     const int4 z = make_int4(0, 0, 0, 0);
@@ -250,6 +254,18 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
       }
     }
     __syncthreads();
+  }
+}
+
+// Stage 2: pass 2 and level 2 (TopK boundaries), then every wave's rank bases
+// (sh.wave_base).  Returns the plan on every thread; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ Plan plan_stage2(Shared<NT>& sh, const Keys& k, const TierArgs& a) {
+  constexpr int W = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (a.mode != SPAX_MODE_THRESHOLD) {
+    const int R[2] = {sh.R[0], sh.R[1]};
     const int b0 = sh.sel_b[0], b1 = sh.sel_b[1];
     // ---- pass 2: per-wave low-bit histograms inside the buckets; keys above the buckets
     // (above0 | above1 << 16)
@@ -326,6 +342,30 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
   p.n_full = sh.totals[0];
   p.n_kept = sh.totals[1];
   return p;
+}
+
+// Both stages: boundaries, totals and rank bases.
+template <int NT, int MAXD>
+__device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs32,
+                                           const uint16_t* __restrict__ x, const TierArgs& a) {
+  plan_stage1<NT, MAXD>(sh, k, xs32, x, a);
+  return plan_stage2<NT>(sh, k, a);
+}
+
+// Key intervals known after stage 1, per boundary b (0: FULL, 1: kept): keys > U_b are
+// certainly selected, keys < L_b certainly not, keys in [L_b, U_b] wait for stage 2.  The
+// exact boundary key lies in [L_b, U_b] (TopK: the level-1 bucket); THRESHOLD decides every
+// key at once (U_b = K - 1, L_b = K); a boundary holding no channel has L_b = 0x8000.
+struct Interval {
+  int L0, U0, L1, U1;
+};
+
+template <int NT>
+__device__ __forceinline__ Interval intervals(const Shared<NT>& sh, const TierArgs& a) {
+  if (a.mode == SPAX_MODE_THRESHOLD) return Interval{a.k_full, a.k_full - 1, a.k_skip, a.k_skip - 1};
+  const int b0 = sh.sel_b[0], b1 = sh.sel_b[1];
+  return Interval{b0 >= 0 ? b0 << 7 : 0x8000, b0 >= 0 ? (b0 << 7) + 127 : 0x7FFF,
+                  b1 >= 0 ? b1 << 7 : 0x8000, b1 >= 0 ? (b1 << 7) + 127 : 0x7FFF};
 }
 
 // Pass 3: FULL / APPROX channels go to emit_list(tier, rank, j, raw) with their rank in the

@@ -58,9 +58,10 @@ def _params(spax, oa):
     return spax.guided_params(oa["tau"], oa["n_lo"], oa["n_hi"], oa["num"], oa["den"])
 
 
-def run_step(env, specs, seed, share_y=None, flags=0):
+def run_step(env, specs, seed, share_y=None, flags=0, xs=None):
     """specs: list of (d_in, d_out list, base_fmt, G, mode_spec).  share_y: set of phase
-    indices whose y buffer is the same tensor as the previous phase's (same size)."""
+    indices whose y buffer is the same tensor as the previous phase's (same size).  xs: optional
+    {phase: fp16 activations} replacing the synthetic ones."""
     torch, spax, dev = env
     phases, keep = [], []
     share_y = share_y or set()
@@ -72,6 +73,9 @@ def run_step(env, specs, seed, share_y=None, flags=0):
         packed = torch.empty(int(L.total_bytes), dtype=torch.uint8, device=dev)
         spax.spax_pack_columns(L, [torch.from_numpy(w).to(dev) for w in Ws], packed)
         x16 = synth.activations(seed, d_in, i, token_scale=synth.token_scale(seed, i))
+        if xs and i in xs:
+            x16 = np.ascontiguousarray(xs[i], dtype=np.float16)
+            assert x16.shape == (d_in,)
         oa = _oracle_args(mspec, d_in)
         if i in share_y:
             y = prev_y
@@ -140,19 +144,21 @@ def test_step_wide_input(env, flags):
     check(run_step(env, specs, 606, flags=flags))
 
 
-def test_step_fallback_large_din(env):
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_fallback_large_din(env, flags):
     specs = [(512, [512], 0, 64, ("guided", 0.5, 0.05)),
              (20000, [256], 0, 128, ("guided", 0.7, 0.01)),     # > 16384: two-kernel path
              (256, [1024, 1024], 0, 128, ("topk", 0.3, 0.3)),
              (17000, [384], 1, 128, ("topk", 0.25, 0.35))]
-    check(run_step(env, specs, 202))
+    check(run_step(env, specs, 202, flags=flags))
 
 
-def test_step_single_chunk_phases(env):
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_single_chunk_phases(env, flags):
     specs = [(8, [4096], 0, 128, ("topk", 0.5, 0.25)),   # d_in < 32: one chunk, plain stores
              (20, [64], 0, 64, ("topk", 1.0, 0.0)),
              (3000, [512], 0, 64, ("guided", 0.5, 0.01))]
-    check(run_step(env, specs, 303))
+    check(run_step(env, specs, 303, flags=flags))
 
 
 @pytest.mark.parametrize("flags", [0, 1])
@@ -166,17 +172,66 @@ def test_step_shared_y_buffers(env, flags):
     check(keep, skip_y={1})
 
 
-def test_step_repeated_calls_stable(env):
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_repeated_calls_stable(env, flags):
     torch, spax, dev = env
     specs = [(2048, [1536, 512], 0, 128, ("guided", 0.5, 0.01)), (1536, [2048], 0, 128, ("topk", 0.3, 0.3))]
-    keep = run_step(env, specs, 505)
+    keep = run_step(env, specs, 505, flags=flags)
     first = [b["y"].cpu().numpy().copy() for *_, b in keep]
     # run the same phases again through a fresh step call on the same buffers
     phases = [spax.make_phase(L, packed, b["x"], _params(spax, oa), b["tier"], b["f"], b["a"],
                               b["c"], b["y"]) for (L, O, Ws, x16, oa, packed, b) in keep]
     for _ in range(5):
-        spax.spax_decode_step_projections(spax.phase_array(phases), None, ws_bytes=0)
+        spax.spax_decode_step_projections(spax.phase_array(phases), None, ws_bytes=0, flags=flags)
     torch.cuda.synchronize()
     for f0, (*_, b) in zip(first, keep):
         assert rel_l2(b["y"].cpu().numpy(), f0) <= 1e-6
     check(keep)
+
+
+def _tie_inputs(seed):
+    """Activations whose tier boundaries fall inside runs of equal magnitudes."""
+    r = np.random.default_rng(seed)
+    x0 = r.laplace(0, 1, 4096).astype(np.float16)
+    x0[r.random(4096) < 0.6] = 0                     # zeros: the kept boundary splits them
+    x1 = r.choice(np.array([-2, -1, -0.5, -0.25, 0.25, 0.5, 1, 2], np.float16), 4096)
+    x2 = r.laplace(0, 1, 3000).astype(np.float16)
+    x2[r.random(3000) < 0.3] = 0.5                   # exactly at the thresholds
+    x2[r.random(3000) < 0.2] = -1.0
+    x3 = np.full(2048, 0.75, np.float16)             # one key for every channel
+    x3[::7] = -0.75
+    x4 = r.laplace(0, 1, 11008).astype(np.float16)
+    x4[r.random(11008) < 0.7] = 0
+    x4[r.random(11008) < 0.1] = 1.5
+    return {0: x0, 1: x1, 2: x2, 3: x3, 4: x4}
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_ties(env, flags):
+    """Boundaries that keep some but not all channels of one magnitude: ties go by channel
+    order in both launch forms."""
+    specs = [(4096, [1024], 0, 128, ("guided", 0.5, 0.01)),
+             (4096, [2048], 1, 128, ("topk", 0.3, 0.3)),
+             (3000, [512], 0, 64, ("threshold", 0.5, 1.0)),
+             (2048, [512], 0, 128, ("topk", 0.2, 0.3)),
+             (11008, [768], 0, 128, ("guided", 0.5, 0.01))]
+    check(run_step(env, specs, 808, flags=flags, xs=_tie_inputs(808)))
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_step_special_values(env, flags):
+    """-0, subnormals, infinities and NaN order by their key; masks and lists stay exact
+    (y is not compared where x holds infinities or NaN)."""
+    r = np.random.default_rng(909)
+    x0 = r.laplace(0, 1, 4096).astype(np.float16)
+    x0[r.integers(0, 4096, 300)] = np.float16(-0.0)
+    x0[r.integers(0, 4096, 300)] = np.float16(6e-8)          # subnormal
+    x1 = x0.copy()
+    x1[r.integers(0, 4096, 20)] = np.inf
+    x1[r.integers(0, 4096, 20)] = -np.inf
+    x1[r.integers(0, 4096, 20)] = np.nan
+    specs = [(4096, [1024], 0, 128, ("guided", 0.5, 0.01)),
+             (4096, [1024], 0, 128, ("topk", 0.25, 0.35)),
+             (4096, [512], 1, 128, ("threshold", 0.5, 1.5))]
+    keep = run_step(env, specs, 909, flags=flags, xs={0: x0, 1: x1, 2: x1})
+    check(keep, skip_y={1, 2})
