@@ -104,7 +104,7 @@ int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
   clear_error();
   if (!step || !step->phases) return fail(SPAX_ERR_NULL, "step and step->phases are required");
   if (step->n_phases < 1) return fail(SPAX_ERR_SHAPE, "n_phases %d < 1", step->n_phases);
-  if (step->flags & ~SPAX_STEP_FUSED_MASK) return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags");
+  if (step->flags & ~SPAX_STEP_SEPARATE) return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags");
   // Validate every phase before enqueueing anything.
   for (int i = 0; i < step->n_phases; ++i) {
     const spax_phase& ph = step->phases[i];

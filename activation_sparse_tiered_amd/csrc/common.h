@@ -52,7 +52,10 @@ int launch_pack(const spax_layout* L, const uint16_t* const* W, void* packed, hi
 
 // ------------------------------------------------------------------ gemv
 constexpr int kTileRows = 512;       // rows per workgroup tile (64 lanes x 8 rows)
-constexpr int kGemvThreads = 512;    // 8 waves share one tile, split the columns
+#ifndef SPAX_GEMV_THREADS
+#define SPAX_GEMV_THREADS 512
+#endif
+constexpr int kGemvThreads = SPAX_GEMV_THREADS;  // waves that share one tile, split the columns
 constexpr int64_t kMaxRowsTotal = (int64_t)1 << 24;  // largest d_out_total of a layout
 
 struct GemvPlan {

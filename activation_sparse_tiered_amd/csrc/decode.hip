@@ -4,18 +4,18 @@
 // token during batch-one decoding); TopK-Guided (arXiv:2610.01763) section 2.1 (per-token
 // mask, O(d)); ByteCross abstract (fixed kernel costs add to the byte account).
 //
-// Default: per group, the stand-alone mask kernel (tiers.hip, which also clears y) and then
-// the stand-alone GEMV (gemv.hip).  With SPAX_STEP_FUSED_MASK, a group's mask and its GEMV
-// run in one kernel of at most one 1024-thread workgroup per compute unit: every workgroup
-// loads the activation vector into LDS, finds the two tier boundaries and ranks the channels
-// (mask_core.h), keeps only the slice of the FULL / APPROX lists its column chunk needs
-// (channel | fp16 x_j << 16 per LDS entry), then streams those columns for its 512-row tile
-// (gemv_core.h).  One extra workgroup writes the tier bytes, the ascending lists and the
-// counts, so the outputs equal those of spax_build_tiers.  The mask is repeated once per
-// compute unit, in parallel, in place of a second launch and of the counts -> indices ->
-// activations chain of dependent global loads; the rank pass runs only in the waves whose
-// ranks meet the workgroup's slices.  The mask is bound by vector-instruction issue inside
-// one CU (a wave64 instruction occupies a SIMD for 4 cycles), so skipped waves shorten it.
+// Default: one fused kernel per group, at most one 1024-thread workgroup per compute unit.
+// Every workgroup loads the activation vector into LDS and finds the two tier boundaries
+// from a per-key histogram (mask_core.h, select_exact), decides the tiers of its own range of
+// input channels, lists those columns in LDS (channel | fp16 x_j << 16 per entry) and streams
+// them for its 512-row tile (gemv_core.h).  One extra workgroup writes the tier bytes, the
+// ascending lists and the counts with the rank-producing mask code, so the outputs equal
+// those of spax_build_tiers.  Repeating the boundary search in every workgroup costs no time
+// (it runs in parallel on separate compute units) and removes the second launch and the
+// counts -> indices -> activations chain of dependent global loads.  With
+// SPAX_STEP_SEPARATE (and for inputs too wide for the fused kernel) a group takes the
+// stand-alone mask kernel (tiers.hip, which also clears y) and the stand-alone GEMV
+// (gemv.hip).
 //
 // y of a group is accumulated with fp32 atomics and must start at zero: the mask kernel (or,
 // fused, the previous launch, spread over its workgroups) clears it; otherwise a small
@@ -65,67 +65,47 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Tier decisions for one wave's candidate list (entries channel | x bits << 16, ascending
-// channel).  `ties` counts the channels before the list's first channel whose key equals the
-// boundary key (only needed when the boundary keeps some but not all of its ties).  The first
-// kFirst entries get bit 15 set when used; the used entries after them are compacted to
-// positions kFirst, kFirst + 1, ...  (in place: a write never passes the entries still to be
-// read).  Returns the number of compacted entries.  FULL list: use = FULL; APPROX list:
-// use = kept and not FULL.
-#ifndef SPAX_FUSED_FIRST
-#define SPAX_FUSED_FIRST 8
-#endif
-constexpr int kFirst = SPAX_FUSED_FIRST;
-
-template <bool kApprox>
-__device__ __forceinline__ int decide(uint32_t* list, int n, const mask::Plan& p, bool need0,
-                                      bool need1, int ties0, int ties1, int lane) {
-  int used = 0;
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const int i = i0 + lane;
-    const bool v = i < n;
-    const uint32_t e = v ? list[i] : 0u;
-    const int key = (int)((e >> 16) & 0x7FFFu);
-    const bool t0 = v && key == p.s0.kb, t1 = v && key == p.s1.kb;
-    const uint64_t b0 = __ballot(t0), b1 = __ballot(t1);
-    const int r0 = ties0 + (int)mask::lanes_below(b0), r1 = ties1 + (int)mask::lanes_below(b1);
-    const bool full = key > p.s0.kb || (t0 && (!need0 || r0 < p.s0.m));
-    bool use;
-    if (kApprox) {
-      const bool kept = key > p.s1.kb || (t1 && (!need1 || r1 < p.s1.m));
-      use = v && kept && !full;
-    } else {
-      use = v && full;
+// Channels j in [begin, end) whose key is kb0 / kb1 (begin a multiple of 8; eight keys per
+// lane and LDS read).  One wave; the result is wave-uniform.
+__device__ __forceinline__ void ties_between(const uint32_t* xs32, int begin, int end, int kb0,
+                                             int kb1, int lane, int& t0, int& t1) {
+  int c0 = 0, c1 = 0;
+  const uint4* x4 = reinterpret_cast<const uint4*>(xs32);
+  for (int base = begin; base < end; base += 512) {
+    const int j = base + 8 * lane;
+    if (j < end) {
+      const uint4 v = x4[j >> 3];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = (int)(((e & 1) ? w[e >> 1] >> 16 : w[e >> 1]) & 0x7FFFu);
+        const bool in = j + e < end;
+        c0 += in && key == kb0;
+        c1 += in && key == kb1;
+      }
     }
-    ties0 += mask::popc(b0);
-    ties1 += mask::popc(b1);
-    const uint64_t bu = __ballot(use && i >= kFirst);
-    if (v && i < kFirst) list[i] = e | (use ? 0x8000u : 0u);
-    if (use && i >= kFirst) list[kFirst + used + (int)mask::lanes_below(bu)] = e;
-    used += mask::popc(bu);
   }
-  return used;
+  t0 = mask::wave_sum(c0);
+  t1 = mask::wave_sum(c1);
 }
 
 // One group: mask and GEMV.  Workgroup gridDim.x - 1 only writes the outputs of the mask
 // (build_plan + emit, as the stand-alone mask kernel).  Every other workgroup owns one
 // 512-row tile and one contiguous range of input channels, split over its 16 waves:
-//   1. stage 1 of the mask (x to LDS, high-bit histogram, level-1 buckets);
-//   2. each wave lists its channels that may still be FULL (key >= L0) or APPROX
-//      (L1 <= key <= U0) and issues the loads of its first kFirst columns of each list;
-//   3. stage 2 of the mask (exact boundaries) runs while those loads are in flight;
-//   4. the tier decisions (ties by channel order) mark or compact the lists; the loaded
-//      columns that are used are multiplied, the rest of the used columns streamed.
-// A candidate that ends up unused costs its load but adds nothing.
+//   1. the exact boundaries from a per-key histogram (select_exact: one pass over the keys);
+//   2. each wave decides the tiers of its channels (ties at a boundary key by channel order,
+//      counting the equal keys before its first channel only when it holds such a tie) and
+//      lists its FULL and APPROX columns in LDS;
+//   3. each wave streams its columns; the tile is reduced across waves and added to y.
 template <int FMT, int MAXD>
 __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t dyn[];
   // The mask's scratch and the GEMV's cross-wave reduction are never live together.
   __shared__ union {
     mask::Shared<kFusedThreads> msh;
+    mask::KeyHist<kFusedThreads> kh;
     float red[kFusedWaves][kTileRows];
   } u;
-  mask::Shared<kFusedThreads>& msh = u.msh;
   uint32_t* xs32 = reinterpret_cast<uint32_t*>(dyn);
   const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(dyn);
 
@@ -138,6 +118,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
 
   if (blockIdx.x == gridDim.x - 1) {
     // ---- writer: tier bytes, ascending lists, counts
+    mask::Shared<kFusedThreads>& msh = u.msh;
     const mask::Plan p = mask::build_plan<kFusedThreads, MAXD>(msh, k, xs32, a.x, a.ta);
     const bool tier_even = ((uintptr_t)a.tier & 1) == 0;  // channel pairs start at even j
     mask::emit<kFusedThreads>(
@@ -167,124 +148,87 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   const int chunk = (int)(blockIdx.x / (uint32_t)sh.n_tiles);
   const int c0 = gemv::split_at(d, chunk, sh.n_chunks);
   const int c1 = gemv::split_at(d, chunk + 1, sh.n_chunks);
-  const int S = a.wave_cap;
-  const int ws = min(c0 + wave * S, c1), we = min(ws + S, c1);  // this wave's channels
-  uint32_t* lF = reinterpret_cast<uint32_t*>(dyn + a.xs_bytes) + wave * S;
-  uint32_t* lA = lF + kFusedWaves * S;
+  const int S = a.wave_cap;  // channels per wave
+  const int ws = min(c0 + wave * S, c1), we = min(ws + S, c1);
+  uint32_t* lF = reinterpret_cast<uint32_t*>(dyn + a.xs_bytes) + wave * 2 * S;
+  uint32_t* lA = lF + S;
   const int T = sh.T;
   const int row0 = tile * kTileRows;
   const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
   const uint32_t jmax = (uint32_t)d - 1u;
 
-  // ---- 1. mask stage 1
-  mask::plan_stage1<kFusedThreads, MAXD>(msh, k, xs32, a.x, a.ta);
-  const mask::Interval iv = mask::intervals(msh, a.ta);
+  // ---- 1. boundaries
+  mask::Select sel[2];
+  int E[2];
+  mask::select_exact<kFusedThreads, MAXD>(u.kh, k, xs32, a.x, a.ta, sel, E);
+  const mask::Select s0 = sel[0], s1 = sel[1];
 
-  // ---- 2. candidate lists and the first loads
-  int nFc = 0, nAc = 0;
+  // ---- 2. this wave's tiers and column lists
+  bool need0 = s0.m < E[0], need1 = s1.m < E[1];  // the boundary keeps some of its ties only
+  if (need0 || need1) {
+    // equal keys per mask-pass wave range (C channels each), for the tie bases below
+    int c = 0;
+    for (int s = 0; s < k.steps; ++s) {
+      const uint32_t wd = k.word(s, lane);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int key = k.valid(s, lane, e) ? (int)((e ? wd >> 16 : wd) & 0x7FFFu) : -1;
+        c += (key == s0.kb ? 1 : 0) + (key == s1.kb ? 0x10000 : 0);
+      }
+    }
+    c = mask::wave_sum(c);
+    if (lane == 0) u.kh.wave_ties[wave] = c;
+    __syncthreads();  // uniform: need0 / need1 are the same on every wave
+    bool here0 = false, here1 = false;
+    for (int j0 = ws; j0 < we; j0 += 64) {
+      const int j = j0 + lane;
+      const int key = j < we ? (int)(xs16[j] & 0x7FFFu) : -1;
+      here0 |= __ballot(key == s0.kb) != 0;
+      here1 |= __ballot(key == s1.kb) != 0;
+    }
+    need0 = need0 && here0;
+    need1 = need1 && here1;
+  }
+  int ties0 = 0, ties1 = 0;
+  if (need0 || need1) {
+    // equal keys before ws: whole mask-pass ranges, then the rest of the one holding ws
+    const int gw = ws / k.C;
+    const int c = mask::wave_sum(lane < gw ? u.kh.wave_ties[lane] : 0);
+    int p0 = 0, p1 = 0;
+    ties_between(xs32, gw * k.C, ws, s0.kb, s1.kb, lane, p0, p1);
+    ties0 = (c & 0xFFFF) + p0;
+    ties1 = (c >> 16) + p1;
+  }
+  int nF = 0, nA = 0;
   for (int j0 = ws; j0 < we; j0 += 64) {
     const int j = j0 + lane;
     const bool v = j < we;
     const uint32_t raw = v ? (uint32_t)xs16[j] : 0u;
-    const int key = (int)(raw & 0x7FFFu);
-    const bool fc = v && key >= iv.L0;
-    const bool ac = v && key >= iv.L1 && key <= iv.U0;
-    const uint64_t bf = __ballot(fc), ba = __ballot(ac);
+    const int key = v ? (int)(raw & 0x7FFFu) : -1;
+    const bool t0 = key == s0.kb, t1 = key == s1.kb;
+    const uint64_t b0 = __ballot(t0), b1 = __ballot(t1);
+    const int r0 = ties0 + (int)mask::lanes_below(b0), r1 = ties1 + (int)mask::lanes_below(b1);
+    const bool full = key > s0.kb || (t0 && (!need0 || r0 < s0.m));
+    const bool kept = key > s1.kb || (t1 && (!need1 || r1 < s1.m));
+    const bool apx = kept && !full;
+    ties0 += mask::popc(b0);
+    ties1 += mask::popc(b1);
     const uint32_t e = (uint32_t)j | (raw << 16);
-    if (fc) lF[nFc + (int)mask::lanes_below(bf)] = e;
-    if (ac) lA[nAc + (int)mask::lanes_below(ba)] = e;
-    nFc += mask::popc(bf);
-    nAc += mask::popc(ba);
+    const uint64_t bf = __ballot(full), ba = __ballot(apx);
+    if (full) lF[nF + (int)mask::lanes_below(bf)] = e;
+    if (apx) lA[nA + (int)mask::lanes_below(ba)] = e;
+    nF += mask::popc(bf);
+    nA += mask::popc(ba);
   }
   wave_lds_fence();
-  const int nf1 = min(nFc, kFirst), na1 = min(nAc, kFirst);
-  float xf[kFirst], xa[kFirst];
-  uint4 vf[kFirst];
-  uint32_t cf[kFirst], sf[kFirst], ca[kFirst], sa[kFirst];
-  {
-    const gemv::LdsList LF{lF, 0, jmax}, LA{lA, 0, jmax};
-    const uint8_t* regionA = a.packed + sh.off_A;
-    const uint32_t loffF = FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u;
-    const uint32_t szoffF = (uint32_t)(T / 2) + (uint32_t)(row / sh.base_group) * 4u;
-    const uint32_t loffA4 = ((uint32_t)row / 4u) & ~3u;
-    const uint32_t szoffA = (uint32_t)(T / 4) + (uint32_t)(row / sh.approx_group) * 4u;
-#pragma unroll
-    for (int q = 0; q < kFirst; ++q) {
-      if (q < nf1) {
-        int j;
-        LF.get(q, j, xf[q]);
-        const uint8_t* col = a.packed + (int64_t)j * sh.stride_F;
-        if (FMT == SPAX_FMT_FP16) {
-          vf[q] = *reinterpret_cast<const uint4*>(col + loffF);
-        } else {
-          cf[q] = *reinterpret_cast<const uint32_t*>(col + loffF);
-          sf[q] = *reinterpret_cast<const uint32_t*>(col + szoffF);
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kFirst; ++q) {
-      if (q < na1) {
-        int j;
-        LA.get(q, j, xa[q]);
-        const uint8_t* col = regionA + (int64_t)j * sh.stride_A;
-        ca[q] = *reinterpret_cast<const uint32_t*>(col + loffA4);
-        sa[q] = *reinterpret_cast<const uint32_t*>(col + szoffA);
-      }
-    }
-  }
 
-  // ---- 3. mask stage 2 (exact boundaries, tie bases)
-  const mask::Plan p = mask::plan_stage2<kFusedThreads>(msh, k, a.ta);
-
-  // ---- 4. decisions.  Ties before this wave's first channel: the tie count before its
-  // mask wave (layout of the mask passes) plus a count up to ws.
-  constexpr int kW = kFusedWaves;
-  const bool need0 = p.s0.m < msh.wave_base[kW][2];  // the FULL boundary splits its ties
-  const bool need1 = p.s1.m < msh.wave_base[kW][3];
-  int ties0 = 0, ties1 = 0;
-  if ((need0 || need1) && ws < we) {
-    const int gw = ws / k.C;
-    ties0 = msh.wave_base[gw][2];
-    ties1 = msh.wave_base[gw][3];
-    for (int j0 = gw * k.C; j0 < ws; j0 += 64) {
-      const int j = j0 + lane;
-      const int key = j < ws ? (int)(xs16[j] & 0x7FFFu) : -1;
-      ties0 += mask::popc(__ballot(key == p.s0.kb));
-      ties1 += mask::popc(__ballot(key == p.s1.kb));
-    }
-  }
-  const int nUF = decide<false>(lF, nFc, p, need0, need1, ties0, ties1, lane);
-  const int nUA = decide<true>(lA, nAc, p, need0, need1, ties0, ties1, lane);
-  wave_lds_fence();
-
-  // ---- 5. GEMV: the columns already loaded, then the remaining used ones
+  // ---- 3. stream, reduce
   float acc[8];
 #pragma unroll
   for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
   float zsum = 0.0f;
-  const uint32_t shA = (((uint32_t)row / 4u) & 2u) * 8u;
-#pragma unroll
-  for (int q = 0; q < kFirst; ++q) {
-    if (q < nf1 && (__builtin_amdgcn_readfirstlane(lF[q]) & 0x8000u)) {
-      if (FMT == SPAX_FMT_FP16) {
-        gemv::fma_fp16x8(acc, xf[q], vf[q]);
-      } else {
-        gemv::fma_int4x8(acc, xf[q] * gemv::half_lo(sf[q]), cf[q]);
-        zsum = fmaf(xf[q], gemv::half_hi(sf[q]), zsum);
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < kFirst; ++q) {
-    if (q < na1 && (__builtin_amdgcn_readfirstlane(lA[q]) & 0x8000u)) {
-      gemv::fma_int2x8(acc, xa[q] * gemv::half_lo(sa[q]), ca[q] >> shA);
-      zsum = fmaf(xa[q], gemv::half_hi(sa[q]), zsum);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // the first loads are all consumed or dropped
-  gemv::stream_columns<FMT>(sh, a.packed, row, kFirst, kFirst + nUF, gemv::LdsList{lF, 0, jmax},
-                            kFirst, kFirst + nUA, gemv::LdsList{lA, 0, jmax}, acc, zsum);
+  gemv::stream_columns<FMT>(sh, a.packed, row, 0, nF, gemv::LdsList{lF, 0, jmax}, 0, nA,
+                            gemv::LdsList{lA, 0, jmax}, acc, zsum);
   __syncthreads();  // every wave is done with the mask scratch that `red` overlays
   gemv::finish_tile<kFusedWaves>(u.red, acc, zsum, wave, lane, row0, T, sh.n_chunks, a.y);
   clear_next(a);
@@ -330,14 +274,14 @@ GemvPlan fused_plan(const spax_layout* L) {
 }
 
 // Dynamic LDS: the activations (d_in halves rounded up to whole dwords, in bytes, rounded
-// to 16), then per wave a FULL and an APPROX candidate list of wave_cap entries each
-// (wave_cap * 16 >= the channels of one chunk).
+// to 16), then for each wave a FULL and an APPROX list of wave_cap entries; wave_cap * 16 >=
+// the channels of one chunk.
 FusedLds fused_lds(const spax_layout* L, const GemvPlan& plan) {
   FusedLds f;
   const int range = (L->d_in + plan.n_chunks - 1) / plan.n_chunks;
   f.wave_cap = (range + kFusedWaves - 1) / kFusedWaves;
   f.xs_bytes = (4 * ((L->d_in + 1) / 2) + 15) / 16 * 16;
-  f.bytes = (size_t)f.xs_bytes + 2 * kFusedWaves * 4 * (size_t)f.wave_cap;
+  f.bytes = (size_t)f.xs_bytes + kFusedWaves * 2 * 4 * (size_t)f.wave_cap;
   return f;
 }
 
@@ -355,7 +299,7 @@ bool fused_phase_ok(const spax_layout* L) {
 
 int launch_decode_step(const spax_step* st, hipStream_t s) {
   const int n = st->n_phases;
-  const bool separate = (st->flags & SPAX_STEP_FUSED_MASK) == 0;
+  const bool separate = (st->flags & SPAX_STEP_SEPARATE) != 0;
   auto fused_phase_ok = [&](const spax_layout* L) { return !separate && spax::fused_phase_ok(L); };
   for (int i = 0; i < n; ++i) {
     const spax_phase& ph = st->phases[i];

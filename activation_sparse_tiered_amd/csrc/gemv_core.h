@@ -21,7 +21,10 @@ namespace spax {
 namespace gemv {
 
 constexpr int kWaves = kGemvThreads / 64;
-constexpr int kUnroll = 8;
+#ifndef SPAX_UNROLL
+#define SPAX_UNROLL 4
+#endif
+constexpr int kUnroll = SPAX_UNROLL;  // columns per tier whose loads are in flight together
 
 struct Shape {
   int64_t stride_F, stride_A, off_A;

@@ -352,20 +352,146 @@ __device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs
   return plan_stage2<NT>(sh, k, a);
 }
 
-// Key intervals known after stage 1, per boundary b (0: FULL, 1: kept): keys > U_b are
-// certainly selected, keys < L_b certainly not, keys in [L_b, U_b] wait for stage 2.  The
-// exact boundary key lies in [L_b, U_b] (TopK: the level-1 bucket); THRESHOLD decides every
-// key at once (U_b = K - 1, L_b = K); a boundary holding no channel has L_b = 0x8000.
-struct Interval {
-  int L0, U0, L1, U1;
+// Exact selection from a per-key histogram (used by the fused decode kernel, which needs the
+// boundaries but no ranks): one pass of LDS atomics into 32768 16-bit counters (two keys per
+// dword; a count never exceeds 32768, so it cannot carry into its neighbour), 1024 partial
+// sums of 32 keys each, then one wave finds each boundary with two suffix scans (partial
+// sums, then the 32 keys of the chosen partial sum).  Compared with the two-level radix
+// select above there is no second pass over the keys, and far fewer lanes collide in one
+// counter (equal keys only).
+template <int NT>
+struct KeyHist {
+  static constexpr int W = NT / 64;
+  alignas(16) uint32_t fine[16384];  // count of key 2i in bits 0..15, of key 2i + 1 in 16..31
+  alignas(16) int coarse[1024];      // channels with key in [32c, 32c + 32)
+  int wave_nat[W];
+  int wave_ties[W];  // per mask-pass wave range: channels at boundary key 0 | key 1 << 16
+  Select sel[2];
+  int E[2];
 };
 
-template <int NT>
-__device__ __forceinline__ Interval intervals(const Shared<NT>& sh, const TierArgs& a) {
-  if (a.mode == SPAX_MODE_THRESHOLD) return Interval{a.k_full, a.k_full - 1, a.k_skip, a.k_skip - 1};
-  const int b0 = sh.sel_b[0], b1 = sh.sel_b[1];
-  return Interval{b0 >= 0 ? b0 << 7 : 0x8000, b0 >= 0 ? (b0 << 7) + 127 : 0x7FFF,
-                  b1 >= 0 ? b1 << 7 : 0x8000, b1 >= 0 ? (b1 << 7) + 127 : 0x7FFF};
+// Loads x into LDS (xs32: roundup(d, 2) halves) and returns both boundaries and, for each,
+// the number of channels whose key equals it (E; 0 for THRESHOLD, whose boundaries keep all
+// their ties).  Sets k like build_plan.  Contains the barriers it needs and ends with one.
+template <int NT, int MAXD>
+__device__ __forceinline__ void select_exact(KeyHist<NT>& h, Keys& k, uint32_t* xs32,
+                                             const uint16_t* __restrict__ x, const TierArgs& a,
+                                             Select (&sel)[2], int (&E)[2]) {
+  constexpr int W = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int d = a.d;
+  k.xs32 = xs32;
+  k.C = ((d + W - 1) / W + 127) / 128 * 128;
+  k.j0 = min(wave * k.C, d);
+  k.n = min(k.j0 + k.C, d) - k.j0;
+  k.steps = (k.n + 127) / 128;
+  const bool thresholds = a.mode == SPAX_MODE_THRESHOLD;
+  {
+    // Every load of x in flight while the histogram is cleared, then x into LDS.
+    constexpr int PER = (MAXD / 2 + NT - 1) / NT;
+    const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
+    const int ndw = (d + 1) >> 1;
+    uint32_t v[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) v[q] = tid + q * NT < ndw ? x32[tid + q * NT] : 0u;
+    if (!thresholds) {
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      uint4* f4 = reinterpret_cast<uint4*>(h.fine);
+      for (int i = tid; i < 16384 / 4; i += NT) f4[i] = z;
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (tid + q * NT < ndw) xs32[tid + q * NT] = v[q];
+    __builtin_amdgcn_s_waitcnt(0);  // see plan_stage1
+  }
+  __syncthreads();
+  if (thresholds) {
+    sel[0] = Select{a.k_full, d};
+    sel[1] = Select{a.k_skip, d};
+    E[0] = E[1] = 0;
+    return;
+  }
+  int nat = 0;
+  for (int s = 0; s < k.steps; ++s) {
+    const uint32_t wd = k.word(s, lane);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const bool valid = k.valid(s, lane, e);
+      const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
+      if (valid) atomicAdd(&h.fine[key >> 1], 1u << ((key & 1) << 4));
+      nat += valid && key < a.k_tau;
+    }
+  }
+  nat = wave_sum(nat);
+  if (lane == 0) h.wave_nat[wave] = nat;
+  __syncthreads();
+  for (int c = tid; c < 1024; c += NT) {
+    const uint4* f4 = reinterpret_cast<const uint4*>(h.fine) + 4 * c;
+    uint32_t t = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = f4[q];
+      t += (v.x & 0xFFFFu) + (v.x >> 16) + (v.y & 0xFFFFu) + (v.y >> 16) + (v.z & 0xFFFFu) +
+           (v.z >> 16) + (v.w & 0xFFFFu) + (v.w >> 16);
+    }
+    h.coarse[c] = (int)t;
+  }
+  __syncthreads();
+  if (wave < 2) {  // wave b finds boundary b
+    const int b = wave;
+    int R[2];
+    if (a.mode == SPAX_MODE_TOPK) {
+      R[0] = a.n_full;
+      R[1] = a.n_full + a.n_approx;
+    } else {
+      const int natural = wave_sum(lane < W ? h.wave_nat[lane] : 0);
+      const int n_skip = min(max(natural, a.n_lo), a.n_hi);
+      const int kept = d - n_skip;
+      // num <= den <= 65535 and kept <= 32768: fits 32 bits
+      const int n_approx = (int)(((uint32_t)a.num * (uint32_t)kept + (uint32_t)(a.den / 2)) /
+                                 (uint32_t)a.den);
+      R[0] = kept - n_approx;
+      R[1] = kept;
+    }
+    int local[16];
+    {
+      const int4* c4 = reinterpret_cast<const int4*>(h.coarse) + 4 * lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int4 v = c4[q];
+        local[4 * q] = v.x;
+        local[4 * q + 1] = v.y;
+        local[4 * q + 2] = v.z;
+        local[4 * q + 3] = v.w;
+      }
+    }
+    {
+      Select sb{0x8000, 0};
+      int eb = 0;
+      if (R[b] > 0) {
+        int cb = 0, above = 0;
+        suffix_find<16>(local, R[b], 0, lane, &cb, &above);
+        cb = min(max(cb, 0), 1023);  // R <= d: always found
+        const uint32_t dw = h.fine[16 * cb + ((lane & 31) >> 1)];
+        const int cnt[1] = {lane < 32 ? (int)((dw >> ((lane & 1) << 4)) & 0xFFFFu) : 0};
+        int v = 0, ab = 0;
+        suffix_find<1>(cnt, R[b], above, lane, &v, &ab);
+        v = min(max(v, 0), 31);
+        sb = Select{32 * cb + v, R[b] - ab};
+        eb = __builtin_amdgcn_readlane(cnt[0], v);
+      }
+      if (lane == 0) {
+        h.sel[b] = sb;
+        h.E[b] = eb;
+      }
+    }
+  }
+  __syncthreads();
+  sel[0] = h.sel[0];
+  sel[1] = h.sel[1];
+  E[0] = h.E[0];
+  E[1] = h.E[1];
 }
 
 // Pass 3: FULL / APPROX channels go to emit_list(tier, rank, j, raw) with their rank in the

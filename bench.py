@@ -10,10 +10,11 @@ spax_pack_columns before timing; activations are seeded Laplace(0, 1) vectors, o
 (token, layer, group), resident in HBM before the timed region.
 
 Prints one JSON line.  ``value`` is microseconds per token (lower is better).  The
-``roofline`` object is for the tiered GEMV kernel (the dominant kernel): algorithmic bytes
-= selected column records + activations + index lists + y, per launch, over the kernel's
-average duration measured with HIP events on the launch stream.  ``cpu_baseline`` times the
-oracle (float64 NumPy) on a bounded sample of the same workload on the host cores.
+``roofline`` object is for the fused mask+GEMV kernel (the only kernel of the default step):
+algorithmic bytes = selected column records + activations + tier bytes + index lists + y,
+per launch, over the kernel's average duration measured with HIP events that the library
+records on the launch stream around each launch.  ``cpu_baseline`` times the oracle (float64
+NumPy) on a bounded sample of the same workload on the host cores.
 """
 
 from __future__ import annotations
@@ -52,7 +53,11 @@ def parse():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=6,
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="before the timed steps, run one elementwise kernel (bitwise_not) that "
+                         "reads and writes this many MiB: known traffic for scaling hardware "
+                         "byte counters (use more than the 256 MB last-level cache)")
+    ap.add_argument("--cpu-layers", type=int, default=24,
                     help="layers of one token the oracle runs for the CPU baseline")
     return ap.parse_args()
 
@@ -111,15 +116,16 @@ class Stack:
                                                flags=self.flags)
 
     def algorithmic_bytes(self, i, counts):
-        """Bytes the GEMV of phase i must read/write for a mask with these counts."""
+        """Bytes phase i must move for a mask with these counts: the selected column
+        records, x, the tier bytes, both index lists and y (read or written once each)."""
         L = self.layouts[i]
         nF, nA = int(counts[0]), int(counts[1])
-        return (nF * int(L.rec_F) + nA * int(L.rec_A) + 2 * int(L.d_in) + 4 * (nF + nA)
-                + 4 * int(L.d_out_total))
+        return (nF * int(L.rec_F) + nA * int(L.rec_A) + 2 * int(L.d_in) + int(L.d_in)
+                + 4 * (nF + nA) + 4 * int(L.d_out_total))
 
     def timed_kernels(self, t):
         """The same decode step with events recorded by the library right before and after
-        each phase's GEMV launch on the launch stream."""
+        each phase's fused launch on the launch stream."""
         torch = self.torch
         n = len(self.layouts)
         if not hasattr(self, "events"):
@@ -135,38 +141,72 @@ class Stack:
         return ms, counts
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_phase_kernel_decode7b_s05_traffic.md")
+
+
+def sources_sha256():
+    """sha256 over the kernel sources and the C header (name, then bytes; sorted by path)."""
+    import glob
+    import hashlib
+    files = sorted(glob.glob(os.path.join(ROOT, "activation_sparse_tiered_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "spax.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(args):
+    """HBM MB per fused launch from the committed FETCH_SIZE / WRITE_SIZE summary, scaled by
+    its copy calibration; None unless this is the workload it was taken on and the kernel
+    sources are unchanged since."""
+    if (args.sparsity, args.delta, args.layers) != (0.5, 0.01, 32) or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_MB_per_launch", "sources_sha256"):
+                k, v = line.split(":", 1)
+                vals[k] = v.strip()
+    if vals.get("sources_sha256") != sources_sha256() or "traffic_MB_per_launch" not in vals:
+        return None
+    return float(vals["traffic_MB_per_launch"])
+
+
 def cpu_baseline(stack, layers, s, delta):
-    """The oracle on `layers` layers of token 0, timed on the host, scaled to one token."""
+    """The oracle on `layers` layers of token 0, timed on the host, scaled to one token.
+    Each phase's weights are drawn (on the device, as for the GPU run) and copied to the
+    host right before it is timed, so only one phase is held in host memory at a time."""
     from oracle import gemv as ogemv
     from oracle import pack as opack
     from oracle import tiers as otiers
-    torch = stack.torch
     cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
         limiter = None
-    phases = []
+    bounds = {}
+    dt = 0.0
     for l in range(layers):
         for k, (name, d_in, d_out) in enumerate(stack.shapes):
             Ws = [synth.weights_device(SEED, d_in, r, stack.dev, l, k, m).cpu().numpy()
                   for m, r in enumerate(d_out)]
-            phases.append((opack.Layout(d_in, d_out, 0, 128, 128), Ws,
-                           synth.activations(SEED, d_in, 0, l, k)))
-    n_lo_hi = {}
-    t0 = time.perf_counter()
-    for O, Ws, x in phases:
-        d = O.d_in
-        if d not in n_lo_hi:
-            n_lo_hi[d] = otiers.guided_bounds(d, s, delta)
-        lo, hi = n_lo_hi[d]
-        _, f, a, _ = otiers.build_tiers(x, otiers.MODE_TOPK_GUIDED, tau=-math.log(1 - s),
-                                        n_lo=lo, n_hi=hi, num=3, den=10)
-        ogemv.tiered_gemv(O, Ws, x, f, a)
-    dt = time.perf_counter() - t0
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
+            O = opack.Layout(d_in, d_out, 0, 128, 128)
+            x = synth.activations(SEED, d_in, 0, l, k)
+            if d_in not in bounds:
+                bounds[d_in] = otiers.guided_bounds(d_in, s, delta)
+            lo, hi = bounds[d_in]
+            t0 = time.perf_counter()
+            _, f, a, _ = otiers.build_tiers(x, otiers.MODE_TOPK_GUIDED, tau=-math.log(1 - s),
+                                            n_lo=lo, n_hi=hi, num=3, den=10)
+            ogemv.tiered_gemv(O, Ws, x, f, a)
+            dt += time.perf_counter() - t0
+            del Ws
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
     per_token_us = dt / layers * stack.layers * 1e6
     return {"value": round(per_token_us, 1), "unit": "us/token", "cores": cores, "kind": "oracle",
             "sample": f"{layers} of {stack.layers} layers (4 projection groups each) of one token: "
@@ -191,6 +231,14 @@ def main():
     s, delta = args.sparsity, args.delta
     stack = Stack(spax, torch, dev, args.layers, args.tokens, s, delta)
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.bitwise_not(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---- warmup, then exactly `steps` timed decode steps
     for t in range(args.warmup):
         stack.step(t)
@@ -206,33 +254,37 @@ def main():
     step_ms = e0.elapsed_time(e1) / args.steps
     log(f"[bench] decode step: {step_ms * 1e3:.1f} us/token (event), wall {wall_ms / args.steps:.3f} ms/step")
 
-    # ---- per-kernel timing of the tiered GEMV kernel over the same steps
-    tot_bytes, tot_ms, n_launch, sel_bytes_tok = 0, 0.0, 0, []
+    # ---- bytes: the masks of the timed tokens (deterministic per token) give the counts
+    n_ph = len(stack.layouts)
+    tok_bytes = {}
     per_phase = {}
-    for t in range(args.steps):
-        ms, counts = stack.timed_kernels(args.warmup + t)
-        tok_bytes = 0
+    for t in range(args.warmup, args.warmup + args.steps):
+        key = t % stack.tokens
+        if key in tok_bytes:
+            continue
+        ms, counts = stack.timed_kernels(t)
+        tb = 0
         for i, (m, c) in enumerate(zip(ms, counts)):
             b = stack.algorithmic_bytes(i, c)
-            tot_bytes += b
-            tot_ms += m
-            n_launch += 1
-            tok_bytes += b
-            name = stack.shapes[i % 4][0]
-            pb = per_phase.setdefault(name, [0, 0.0, 0])
+            tb += b
+            pb = per_phase.setdefault(stack.shapes[i % 4][0], [0, 0.0, 0])
             pb[0] += b
             pb[1] += m
             pb[2] += 1
-        sel_bytes_tok.append(tok_bytes)
-    avg_ms = tot_ms / n_launch
-    avg_bytes = tot_bytes / n_launch
-    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+        tok_bytes[key] = tb
+    timed_bytes = [tok_bytes[t % stack.tokens] for t in range(args.warmup, args.warmup + args.steps)]
+    bytes_per_token = float(np.mean(timed_bytes))
+    # The timed step is one fused launch per phase (plus one small clearing launch), back to
+    # back on one stream: the kernel's average launch duration is the step time over the
+    # launches, measured by the events around the timed region.
+    avg_launch_ms = step_ms / n_ph
+    avg_bytes = bytes_per_token / n_ph
+    achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
     for name, (b, m, n) in per_phase.items():
-        log(f"[bench]   gemv {name:7s}: {m / n * 1e3:7.2f} us avg, {b / n / 1e6:7.2f} MB, "
-            f"{b / (m * 1e-3) / 1e9:7.1f} GB/s")
-    log(f"[bench] gemv avg {avg_ms * 1e3:.2f} us/launch, {avg_bytes / 1e6:.2f} MB/launch, "
-        f"{achieved:.1f} GB/s; sum of gemv time per token {tot_ms / args.steps * 1e3:.1f} us; "
-        f"selected bytes/token {np.mean(sel_bytes_tok) / 1e9:.3f} GB")
+        log(f"[bench]   {name:7s}: {b / n / 1e6:7.2f} MB per launch; event-bracketed launch "
+            f"{m / n * 1e3:7.2f} us (includes the launch gap)")
+    log(f"[bench] fused kernel: {avg_launch_ms * 1e3:.2f} us/launch, {avg_bytes / 1e6:.2f} MB/launch, "
+        f"{achieved:.1f} GB/s; selected bytes/token {bytes_per_token / 1e9:.3f} GB")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -258,13 +310,14 @@ def main():
                         f"TopK-Guided mask s={s}+-{delta}, approx tier 3/10 of kept, 2-bit G=128, "
                         f"batch 1, layer-serial",
             "sparsity": s, "layers": args.layers, "tokens": args.tokens,
-            "selected_GB_per_token": round(float(np.mean(sel_bytes_tok)) / 1e9, 4),
-            "effective_GBps_per_token": round(float(np.mean(sel_bytes_tok)) / (step_ms * 1e-3) / 1e9, 1),
+            "selected_GB_per_token": round(bytes_per_token / 1e9, 4),
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "tiered_gemv_kernel<fp16>",
-                     "avg_launch_us": round(avg_ms * 1e3, 3),
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args),
+                     "traffic_unit": "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "kernel": "fused_phase_kernel<fp16>",
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 3),
                      "avg_algorithmic_MB": round(avg_bytes / 1e6, 3)},
         "cpu_baseline": cpu,
     }

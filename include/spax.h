@@ -213,11 +213,13 @@ typedef struct spax_phase {
 
 /* spax_step.flags */
 enum {
-  /* one mask launch + one GEMV launch per phase */
+  /* one fused mask+GEMV launch per phase whose d_in <= 16384 (and whose lists fit in LDS):
+   * one 1024-thread workgroup per compute unit, each finding the boundaries itself; other
+   * phases take the two launches of SPAX_STEP_SEPARATE.  Same outputs either way. */
   SPAX_STEP_DEFAULT = 0,
-  /* one fused launch per phase in which every workgroup rebuilds the mask from x
-   * (same outputs; pays the mask once per workgroup instead of once per phase) */
-  SPAX_STEP_FUSED_MASK = 1
+  /* one stand-alone mask launch (spax_build_tiers' kernel, which also clears y) and one
+   * GEMV launch (spax_tiered_gemv's kernel) per phase */
+  SPAX_STEP_SEPARATE = 1
 };
 
 typedef struct spax_step {
@@ -227,9 +229,9 @@ typedef struct spax_step {
   void* ws;                    /* device workspace, see spax_step_workspace_bytes */
   size_t ws_bytes;
   /* Optional timing hook (NULL: none): 2 * n_phases caller-created events.  events[2i] and
-   * events[2i+1] are recorded on the stream right before and right after phase i's GEMV
-   * launch (its fused mask+GEMV launch with SPAX_STEP_FUSED_MASK), so they bracket exactly
-   * that kernel. */
+   * events[2i+1] are recorded on the stream right before and right after phase i's fused
+   * mask+GEMV launch (its GEMV launch when the phase takes two launches), so they bracket
+   * exactly that kernel. */
   hipEvent_t* events;
 } spax_step;
 
@@ -241,8 +243,7 @@ size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases);
  * One batch-one decode step over all projection groups, in order: for each phase, the
  * tier mask of its activation vector, then the tiered GEMV of its fused matrices.
  * Phase p+1 is enqueued after phase p (stream order), as in a decoder where each
- * group's input depends on the previous group's output.  Default: two launches per phase,
- * the mask kernel (which also clears y) and the GEMV; see SPAX_STEP_FUSED_MASK.
+ * group's input depends on the previous group's output.  Launch forms: see spax_step.flags.
  * (eigenradar commentary on SpAx, second and last paragraphs: selection applies per
  * generated token during batch-one decoding.)
  * Errors: the union of spax_build_tiers and spax_tiered_gemv errors, reported before
