@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes as C
 
-STEP_DEFAULT, STEP_SEPARATE = 0, 1
+STEP_DEFAULT, STEP_SEPARATE, STEP_BATCHED = 0, 1, 2
 
 from ._lib import (FMT_FP16, FMT_INT4, MAX_DIN, MAX_MATS, MODE_THRESHOLD, MODE_TOPK,  # noqa: F401
                    MODE_TOPK_GUIDED, TIER_APPROX, TIER_FULL, TIER_SKIP, Layout, Phase,

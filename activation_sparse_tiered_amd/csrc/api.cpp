@@ -1,5 +1,7 @@
 // Entry points of libspax: argument validation, then kernel launches.
 // Every check runs before anything is enqueued; on error no output is touched.
+#include <algorithm>
+#include <vector>
 #include <cstdio>
 #include <cstring>
 
@@ -24,6 +26,41 @@ int check_tier_outputs(const uint16_t* x, int32_t d_in, const int32_t* full_idx,
     return fail(SPAX_ERR_SHAPE, "d_in %d outside 1..%d", d_in, SPAX_MAX_DIN);
   if (!aligned(x, 4) || !aligned(full_idx, 4) || !aligned(approx_idx, 4) || !aligned(counts, 4))
     return fail(SPAX_ERR_ALIGN, "x, lists and counts must be 4-byte aligned");
+  return SPAX_OK;
+}
+
+// SPAX_STEP_BATCHED runs all phases at once: no output may overlap another output or any
+// input x.
+int check_independent(const spax_step* st) {
+  struct Range {
+    uintptr_t b, e;
+    int phase;
+    bool out;
+  };
+  std::vector<Range> r;
+  for (int i = 0; i < st->n_phases; ++i) {
+    const spax_phase& ph = st->phases[i];
+    const spax_layout* L = ph.layout;
+    const auto add = [&](const void* p, size_t n, bool out) {
+      if (p && n) r.push_back(Range{(uintptr_t)p, (uintptr_t)p + n, i, out});
+    };
+    add(ph.x, 2 * (size_t)L->d_in, false);
+    add(ph.tier, (size_t)L->d_in, true);
+    add(ph.full_idx, 4 * (size_t)L->d_in, true);
+    add(ph.approx_idx, 4 * (size_t)L->d_in, true);
+    add(ph.counts, 12, true);
+    add(ph.y, 4 * (size_t)L->d_out_total, true);
+  }
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.b < b.b; });
+  // any overlap involving an output is an error (two inputs may share memory)
+  uintptr_t end_out = 0, end_any = 0;
+  int ph_out = -1, ph_any = -1;
+  for (const Range& x : r) {
+    if (x.b < end_out) return fail(SPAX_ERR_PARAM, "batched step: phase %d overlaps an output of phase %d", x.phase, ph_out);
+    if (x.out && x.b < end_any) return fail(SPAX_ERR_PARAM, "batched step: an output of phase %d overlaps phase %d", x.phase, ph_any);
+    if (x.out && x.e > end_out) { end_out = x.e; ph_out = x.phase; }
+    if (x.e > end_any) { end_any = x.e; ph_any = x.phase; }
+  }
   return SPAX_OK;
 }
 
@@ -91,7 +128,7 @@ int spax_tiered_gemv(const spax_layout* L, const void* packed, const uint16_t* x
 
 size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases) {
   if (!phases || n_phases < 1) return 0;
-  size_t mx = 0;
+  size_t mx = batched_workspace_bytes(n_phases);
   for (int i = 0; i < n_phases; ++i) {
     if (!layout_ok(phases[i].layout)) return 0;
     const size_t b = gemv_plan(phases[i].layout).ws_bytes;
@@ -104,7 +141,11 @@ int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
   clear_error();
   if (!step || !step->phases) return fail(SPAX_ERR_NULL, "step and step->phases are required");
   if (step->n_phases < 1) return fail(SPAX_ERR_SHAPE, "n_phases %d < 1", step->n_phases);
-  if (step->flags & ~SPAX_STEP_SEPARATE) return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags");
+  if (step->flags & ~(SPAX_STEP_SEPARATE | SPAX_STEP_BATCHED))
+    return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags 0x%x", step->flags);
+  const bool batched = (step->flags & SPAX_STEP_BATCHED) != 0;
+  if (batched && (step->flags & SPAX_STEP_SEPARATE))
+    return fail(SPAX_ERR_PARAM, "SPAX_STEP_BATCHED cannot be combined with SPAX_STEP_SEPARATE");
   // Validate every phase before enqueueing anything.
   for (int i = 0; i < step->n_phases; ++i) {
     const spax_phase& ph = step->phases[i];
@@ -118,6 +159,13 @@ int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
     st = check_gemv_args(ph.layout, ph.packed, ph.x, ph.full_idx, ph.approx_idx, ph.counts, ph.y,
                          step->ws, step->ws_bytes, &plan);
     if (st) return phase_fail(st, i);
+  }
+  if (batched) {
+    const size_t need = batched_workspace_bytes(step->n_phases);
+    if (!step->ws || step->ws_bytes < need)
+      return fail(SPAX_ERR_WORKSPACE, "SPAX_STEP_BATCHED needs a workspace of %zu bytes", need);
+    int st = check_independent(step);
+    if (st) return st;
   }
   return launch_decode_step(step, stream);
 }

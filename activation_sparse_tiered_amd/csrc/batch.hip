@@ -1,0 +1,219 @@
+// Batched decode step (SPAX_STEP_BATCHED): every phase's mask in one launch, then every
+// phase's tiered GEMV in one persistent launch.
+//
+// Pages: eigenradar commentary on SpAx, second and last paragraphs (per-token selection at
+// batch one); ByteCross abstract (fixed kernel costs on top of the byte account).  Legal only
+// when all activation vectors are ready when the step is enqueued and no phase reads another
+// phase's output; the layer-serial forms make no such assumption.  It removes the per-phase
+// launch and ramp cost, so it shows what the byte account alone allows.
+//
+// Launch 1: one 1024-thread workgroup per phase runs the stand-alone mask (mask_core.h,
+// tiers_to_global) and clears the phase's y.  Launch 2: a persistent grid walks the work items
+// of all phases, (row tile, column chunk) pairs numbered phase after phase, each handled like
+// one workgroup of the stand-alone GEMV (gemv_core.h, gemv_item).  The per-phase arguments
+// reach the device as two descriptor tables copied into the caller's workspace from a
+// library-owned ring of pinned host buffers.
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "gemv_core.h"
+#include "mask_core.h"
+
+namespace spax {
+namespace {
+
+constexpr int kMaskThreads = 1024;
+constexpr int kRingSlots = 4;
+
+struct MaskDesc {
+  TierArgs ta;
+  const uint16_t* x;
+  uint8_t* tier;
+  int32_t* full_idx;
+  int32_t* approx_idx;
+  int32_t* counts;
+  float4* y;
+  int32_t n_zero4;
+  int32_t pad;
+};
+
+struct GemvDesc {
+  gemv::Shape sh;
+  const uint8_t* packed;
+  const uint32_t* x32;
+  const int32_t* full_idx;
+  const int32_t* approx_idx;
+  const int32_t* counts;
+  float* y;
+  int32_t item0;  // first work item of this phase
+  int32_t fmt;
+};
+
+__global__ __launch_bounds__(kMaskThreads) void batched_mask_kernel(const MaskDesc* __restrict__ md) {
+  __shared__ mask::Shared<kMaskThreads> sh;
+  __shared__ uint32_t xs32[SPAX_MAX_DIN / 2];
+  const MaskDesc& m = md[blockIdx.x];
+  mask::tiers_to_global<kMaskThreads, SPAX_MAX_DIN>(sh, xs32, m.ta, m.x, m.tier, m.full_idx,
+                                                    m.approx_idx, m.counts);
+  for (int i = threadIdx.x; i < m.n_zero4; i += kMaskThreads)
+    m.y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Work item -> phase by binary search over the phases' first items (wave-uniform).
+__device__ __forceinline__ int phase_of(const GemvDesc* __restrict__ gd, int n, int item) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gd[mid].item0 <= item) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDesc* __restrict__ gd,
+                                                                    int n_phases, int n_items) {
+  __shared__ float red[gemv::kWaves][kTileRows];
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int p = phase_of(gd, n_phases, item);
+    const GemvDesc& g = gd[p];
+    const int local = item - g.item0;
+    const int tile = (int)((uint32_t)local % (uint32_t)g.sh.n_tiles);
+    const int chunk = (int)((uint32_t)local / (uint32_t)g.sh.n_tiles);
+    if (g.fmt == SPAX_FMT_FP16)
+      gemv::gemv_item<SPAX_FMT_FP16>(g.sh, g.packed, g.x32, g.full_idx, g.approx_idx, g.counts,
+                                     g.y, tile, chunk, red);
+    else
+      gemv::gemv_item<SPAX_FMT_INT4>(g.sh, g.packed, g.x32, g.full_idx, g.approx_idx, g.counts,
+                                     g.y, tile, chunk, red);
+    __syncthreads();  // red is reused by the next item
+  }
+}
+
+// Column chunks of a batched phase: about kBatchChannels input channels each (at least 16).
+constexpr int kBatchChannels = 256;
+
+GemvPlan batched_plan(const spax_layout* L) {
+  GemvPlan p{};
+  p.n_tiles = (int32_t)((L->d_out_total + kTileRows - 1) / kTileRows);
+  int k = (L->d_in + kBatchChannels - 1) / kBatchChannels;
+  const int kmax = L->d_in / 16 > 1 ? L->d_in / 16 : 1;
+  p.n_chunks = k < 1 ? 1 : (k > kmax ? kmax : k);
+  p.ws_bytes = 0;
+  return p;
+}
+
+size_t table_bytes(int n) {
+  return aligned_size((size_t)n * sizeof(MaskDesc)) + (size_t)n * sizeof(GemvDesc);
+}
+
+// Library-owned pinned staging: kRingSlots slots per device, each reused only after the copy
+// that last read it has completed.
+struct Ring {
+  std::mutex mu;
+  char* host = nullptr;
+  size_t slot_bytes = 0;
+  hipEvent_t ev[kRingSlots] = {};
+  bool pending[kRingSlots] = {};
+  int next = 0;
+};
+Ring g_rings[64];
+
+int stage_and_copy(const void* src, size_t bytes, void* dst, hipStream_t s) {
+  int dev = 0;
+  SPAX_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(SPAX_ERR_UNSUPPORTED, "device index %d", dev);
+  Ring& r = g_rings[dev];
+  std::lock_guard<std::mutex> lock(r.mu);
+  if (r.slot_bytes < bytes) {
+    for (int i = 0; i < kRingSlots; ++i)
+      if (r.pending[i]) {
+        SPAX_HIP_CHECK(hipEventSynchronize(r.ev[i]));
+        r.pending[i] = false;
+      }
+    if (r.host) SPAX_HIP_CHECK(hipHostFree(r.host));
+    r.host = nullptr;
+    r.slot_bytes = 0;
+    const size_t sb = (bytes + 4095) / 4096 * 4096;
+    void* h = nullptr;
+    SPAX_HIP_CHECK(hipHostMalloc(&h, sb * kRingSlots, hipHostMallocDefault));
+    r.host = static_cast<char*>(h);
+    r.slot_bytes = sb;
+  }
+  const int k = r.next;
+  if (!r.ev[k]) SPAX_HIP_CHECK(hipEventCreateWithFlags(&r.ev[k], hipEventDisableTiming));
+  if (r.pending[k]) SPAX_HIP_CHECK(hipEventSynchronize(r.ev[k]));
+  char* slot = r.host + (size_t)k * r.slot_bytes;
+  std::memcpy(slot, src, bytes);
+  SPAX_HIP_CHECK(hipMemcpyAsync(dst, slot, bytes, hipMemcpyHostToDevice, s));
+  SPAX_HIP_CHECK(hipEventRecord(r.ev[k], s));
+  r.pending[k] = true;
+  r.next = (k + 1) % kRingSlots;
+  return SPAX_OK;
+}
+
+}  // namespace
+
+size_t batched_workspace_bytes(int n_phases) { return n_phases > 0 ? table_bytes(n_phases) : 0; }
+
+int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s) {
+  const int n = st->n_phases;
+  std::vector<char> table(table_bytes(n));
+  MaskDesc* md = reinterpret_cast<MaskDesc*>(table.data());
+  GemvDesc* gd = reinterpret_cast<GemvDesc*>(table.data() + aligned_size((size_t)n * sizeof(MaskDesc)));
+  int64_t items = 0;
+  for (int i = 0; i < n; ++i) {
+    const spax_phase& ph = st->phases[i];
+    const spax_layout* L = ph.layout;
+    MaskDesc m{};
+    tier_args_from_params(&ph.params, L->d_in, &m.ta);
+    m.x = ph.x;
+    m.tier = ph.tier;
+    m.full_idx = ph.full_idx;
+    m.approx_idx = ph.approx_idx;
+    m.counts = ph.counts;
+    m.y = reinterpret_cast<float4*>(ph.y);
+    m.n_zero4 = (int32_t)((L->d_out_total + 3) / 4);
+    md[i] = m;
+    const GemvPlan plan = batched_plan(L);
+    GemvDesc g{};
+    g.sh = gemv_shape(L, plan);
+    g.packed = static_cast<const uint8_t*>(ph.packed);
+    g.x32 = reinterpret_cast<const uint32_t*>(ph.x);
+    g.full_idx = ph.full_idx;
+    g.approx_idx = ph.approx_idx;
+    g.counts = ph.counts;
+    g.y = ph.y;
+    g.item0 = (int32_t)items;
+    g.fmt = L->base_fmt;
+    gd[i] = g;
+    items += (int64_t)plan.n_tiles * plan.n_chunks;
+  }
+  if (items > INT32_MAX) return fail(SPAX_ERR_SHAPE, "too many work items (%lld)", (long long)items);
+  int rc = stage_and_copy(table.data(), table.size(), st->ws, s);
+  if (rc) return rc;
+  const auto* dmd = static_cast<const MaskDesc*>(st->ws);
+  const auto* dgd = reinterpret_cast<const GemvDesc*>(static_cast<const char*>(st->ws) +
+                                                      aligned_size((size_t)n * sizeof(MaskDesc)));
+  // events (optional): [0, 1] bracket the mask launch and [2, 3] the GEMV launch; with one
+  // phase, [0, 1] bracket both.
+  const bool four = st->events && n >= 2;
+  if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[0], s));
+  hipLaunchKernelGGL(batched_mask_kernel, dim3((unsigned)n), dim3(kMaskThreads), 0, s, dmd);
+  SPAX_HIP_CHECK(hipGetLastError());
+  if (four) {
+    SPAX_HIP_CHECK(hipEventRecord(st->events[1], s));
+    SPAX_HIP_CHECK(hipEventRecord(st->events[2], s));
+  }
+  const int64_t grid = items < (int64_t)n_cu * 4 ? items : (int64_t)n_cu * 4;
+  if (grid > 0) {
+    hipLaunchKernelGGL(batched_gemv_kernel, dim3((unsigned)grid), dim3(kGemvThreads), 0, s, dgd,
+                       n, (int)items);
+    SPAX_HIP_CHECK(hipGetLastError());
+  }
+  if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[four ? 3 : 1], s));
+  return SPAX_OK;
+}
+
+}  // namespace spax

@@ -77,6 +77,11 @@ constexpr size_t kFusedMaxDynLds = 48 * 1024;
 bool fused_phase_ok(const spax_layout* L);
 // Enqueue a validated step.
 int launch_decode_step(const spax_step* st, hipStream_t s);
+// SPAX_STEP_BATCHED: workspace for the descriptor tables, and the two launches.
+size_t batched_workspace_bytes(int n_phases);
+int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s);
+
+inline size_t aligned_size(size_t b) { return (b + 255) / 256 * 256; }
 
 // y_zeroed: y already holds zeros (stream-ordered); otherwise a zero fill is enqueued first
 // whenever the plan splits K.

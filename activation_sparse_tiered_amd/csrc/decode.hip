@@ -118,28 +118,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
 
   if (blockIdx.x == gridDim.x - 1) {
     // ---- writer: tier bytes, ascending lists, counts
-    mask::Shared<kFusedThreads>& msh = u.msh;
-    const mask::Plan p = mask::build_plan<kFusedThreads, MAXD>(msh, k, xs32, a.x, a.ta);
-    const bool tier_even = ((uintptr_t)a.tier & 1) == 0;  // channel pairs start at even j
-    mask::emit<kFusedThreads>(
-        msh, k, p, true, 0, INT_MAX, 0, INT_MAX,
-        [&](int t, int rank, int j, uint32_t) {
-          if (t == SPAX_TIER_FULL) a.full_idx[rank] = j;
-          else a.approx_idx[rank] = j;
-        },
-        [&](int j, uint32_t t0, uint32_t t1, int n) {
-          if (!a.tier) return;
-          if (n == 2 && tier_even) *reinterpret_cast<uint16_t*>(a.tier + j) = (uint16_t)(t0 | t1 << 8);
-          else {
-            a.tier[j] = (uint8_t)t0;
-            if (n == 2) a.tier[j + 1] = (uint8_t)t1;
-          }
-        });
-    if (tid == 0) {
-      a.counts[0] = p.n_full;
-      a.counts[1] = p.n_kept - p.n_full;
-      a.counts[2] = d - p.n_kept;
-    }
+    mask::tiers_to_global<kFusedThreads, MAXD>(u.msh, xs32, a.ta, a.x, a.tier, a.full_idx,
+                                               a.approx_idx, a.counts);
     clear_next(a);
     return;
   }
@@ -298,6 +278,7 @@ bool fused_phase_ok(const spax_layout* L) {
 }
 
 int launch_decode_step(const spax_step* st, hipStream_t s) {
+  if (st->flags & SPAX_STEP_BATCHED) return launch_decode_step_batched(st, cu_count(), s);
   const int n = st->n_phases;
   const bool separate = (st->flags & SPAX_STEP_SEPARATE) != 0;
   auto fused_phase_ok = [&](const spax_layout* L) { return !separate && spax::fused_phase_ok(L); };

@@ -26,37 +26,9 @@ __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
     const int32_t* __restrict__ full_idx, const int32_t* __restrict__ approx_idx,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
   __shared__ float red[kWaves][kTileRows];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = (int)(blockIdx.x % (uint32_t)sh.n_tiles);
   const int chunk = (int)(blockIdx.x / (uint32_t)sh.n_tiles);
-  const int T = sh.T;
-  const int row0 = tile * kTileRows;
-  // Lanes past the last row (ragged last tile) read the record's first rows instead, which
-  // is always in bounds; their sums land in rows >= T and are never stored.
-  const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
-
-  // Counts and indices come from device memory; they are clamped so that even malformed
-  // lists cannot address outside the blob (the result is then unspecified).
-  const int nF = min(max(counts[0], 0), sh.d_in);
-  const int nA = min(max(counts[1], 0), sh.d_in);
-  const uint32_t jmax = (uint32_t)sh.d_in - 1u;
-  const int fb = gemv::split_at(nF, chunk, sh.n_chunks);
-  const int fe = gemv::split_at(nF, chunk + 1, sh.n_chunks);
-  const int ab = gemv::split_at(nA, chunk, sh.n_chunks);
-  const int ae = gemv::split_at(nA, chunk + 1, sh.n_chunks);
-  int wfb, wfe, wab, wae;
-  gemv::wave_range<kWaves>(fb, fe, wave, wfb, wfe);
-  gemv::wave_range<kWaves>(ab, ae, wave, wab, wae);
-
-  float acc[8];
-#pragma unroll
-  for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
-  float zsum = 0.0f;
-  gemv::stream_columns<FMT>(sh, packed, row, wfb, wfe, gemv::GlobalList{full_idx, x32, jmax}, wab, wae,
-                            gemv::GlobalList{approx_idx, x32, jmax}, acc, zsum);
-  gemv::finish_tile<kWaves>(red, acc, zsum, wave, lane, row0, T, sh.n_chunks, y);
+  gemv::gemv_item<FMT>(sh, packed, x32, full_idx, approx_idx, counts, y, tile, chunk, red);
 }
 
 __global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ p, int64_t n4) {

@@ -88,18 +88,31 @@ __device__ __forceinline__ void fma_int2x8(float (&acc)[8], float a, uint32_t c)
   acc[7] = fmaf(a, (float)(t3 >> 8), acc[7]);
 }
 
-// Column lists in global memory (stand-alone GEMV): indices clamped to [0, d_in), the
-// activation read with a wave-uniform scalar dword load.
-struct GlobalList {
-  const int32_t* __restrict__ idx;
-  const uint32_t* __restrict__ x32;
-  uint32_t jmax;
+// A block of up to 64 entries of a column list held in registers, one per lane: entry =
+// channel | (fp16 bits of x_j) << 16, for list positions [base, base + 64).  Loaded with one
+// vector load of the indices and one gather of the activations (two dependent round trips per
+// 64 columns instead of two per column); get() broadcasts one entry with readlane.  Indices
+// are clamped to [0, d_in), so malformed lists cannot address outside the blob.
+struct RegBlock {
+  uint32_t e;
+  int base;
   __device__ __forceinline__ void get(int i, int& j, float& xv) const {
-    j = (int)min((uint32_t)idx[i], jmax);
-    const uint32_t w = x32[j >> 1];
-    xv = (j & 1) ? half_hi(w) : half_lo(w);
+    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)e, i - base);
+    j = (int)(v & 0xFFFFu);
+    xv = half_hi(v);
   }
 };
+
+__device__ __forceinline__ RegBlock load_block(const int32_t* __restrict__ idx,
+                                               const uint16_t* __restrict__ x16, int base,
+                                               int end, uint32_t jmax) {
+  const int lane = threadIdx.x & 63;
+  const int i = base + lane;
+  uint32_t j = 0;
+  if (i < end) j = min((uint32_t)idx[i], jmax);
+  const uint32_t xb = i < end ? (uint32_t)x16[j] : 0u;
+  return RegBlock{j | (xb << 16), base};
+}
 
 // Column lists in LDS (fused kernel): entry = channel | (fp16 bits of x_j) << 16, indexed
 // from the workgroup's first rank `base`.  The channel is clamped to [0, d_in) like the
@@ -228,6 +241,49 @@ __device__ __forceinline__ void finish_tile(float (*red)[kTileRows], const float
     if (n_chunks == 1) y[grow] = sum;
     else unsafeAtomicAdd(&y[grow], sum);
   }
+}
+
+// One work item of the stand-alone GEMV: row tile `tile`, column chunk `chunk` of the lists
+// in global memory (counts and indices clamped to [0, d_in], so malformed lists cannot
+// address outside the blob).  A workgroup of kWaves waves; ends after the tile's atomics.
+template <int FMT>
+__device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __restrict__ packed,
+                                          const uint32_t* __restrict__ x32,
+                                          const int32_t* __restrict__ full_idx,
+                                          const int32_t* __restrict__ approx_idx,
+                                          const int32_t* __restrict__ counts,
+                                          float* __restrict__ y, int tile, int chunk,
+                                          float (*red)[kTileRows]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = sh.T;
+  const int row0 = tile * kTileRows;
+  // Lanes past the last row (ragged last tile) read the record's first rows instead, which
+  // is always in bounds; their sums land in rows >= T and are never stored.
+  const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
+  const int nF = min(max(counts[0], 0), sh.d_in);
+  const int nA = min(max(counts[1], 0), sh.d_in);
+  const uint32_t jmax = (uint32_t)sh.d_in - 1u;
+  const int fb = split_at(nF, chunk, sh.n_chunks);
+  const int fe = split_at(nF, chunk + 1, sh.n_chunks);
+  const int ab = split_at(nA, chunk, sh.n_chunks);
+  const int ae = split_at(nA, chunk + 1, sh.n_chunks);
+  int wfb, wfe, wab, wae;
+  wave_range<kWaves>(fb, fe, wave, wfb, wfe);
+  wave_range<kWaves>(ab, ae, wave, wab, wae);
+  float acc[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
+  float zsum = 0.0f;
+  const uint16_t* x16 = reinterpret_cast<const uint16_t*>(x32);
+  // 64 list entries per tier and block; the channels fit the 16-bit entry field (d_in <= 32768)
+  for (int fi = wfb, ai = wab; fi < wfe || ai < wae; fi += 64, ai += 64) {
+    const int fend = min(fi + 64, wfe), aend = min(ai + 64, wae);
+    const RegBlock bf = load_block(full_idx, x16, fi, fend, jmax);
+    const RegBlock ba = load_block(approx_idx, x16, ai, aend, jmax);
+    stream_columns<FMT>(sh, packed, row, fi, max(fi, fend), bf, ai, max(ai, aend), ba, acc, zsum);
+  }
+  finish_tile<kWaves>(red, acc, zsum, wave, lane, row0, T, sh.n_chunks, y);
 }
 
 }  // namespace gemv

@@ -563,5 +563,38 @@ __device__ __forceinline__ void emit(const Shared<NT>& sh, const Keys& k, const 
   }
 }
 
+// A whole mask in one workgroup with its outputs in global memory: tier bytes (tier may be
+// NULL), both ascending lists and the counts {n_full, n_approx, n_skip}.  Used by the
+// stand-alone mask kernel, the writer workgroup of the fused decode kernel and the batched
+// mask launch.  d <= MAXD.
+template <int NT, int MAXD>
+__device__ __forceinline__ void tiers_to_global(Shared<NT>& sh, uint32_t* xs32, const TierArgs& a,
+                                                const uint16_t* __restrict__ x, uint8_t* tier,
+                                                int32_t* full_idx, int32_t* approx_idx,
+                                                int32_t* counts) {
+  Keys k;
+  const Plan p = build_plan<NT, MAXD>(sh, k, xs32, x, a);
+  const bool tier_even = ((uintptr_t)tier & 1) == 0;  // channel pairs start at even j
+  emit<NT>(
+      sh, k, p, true, 0, INT_MAX, 0, INT_MAX,
+      [&](int t, int rank, int j, uint32_t) {
+        if (t == SPAX_TIER_FULL) full_idx[rank] = j;
+        else approx_idx[rank] = j;
+      },
+      [&](int j, uint32_t t0, uint32_t t1, int n) {
+        if (!tier) return;
+        if (n == 2 && tier_even) *reinterpret_cast<uint16_t*>(tier + j) = (uint16_t)(t0 | t1 << 8);
+        else {
+          tier[j] = (uint8_t)t0;
+          if (n == 2) tier[j + 1] = (uint8_t)t1;
+        }
+      });
+  if (threadIdx.x == 0) {
+    counts[0] = p.n_full;
+    counts[1] = p.n_kept - p.n_full;
+    counts[2] = a.d - p.n_kept;
+  }
+}
+
 }  // namespace mask
 }  // namespace spax

@@ -21,33 +21,10 @@ __global__ __launch_bounds__(NT) void build_tiers_kernel(
     int32_t* __restrict__ counts, float4* __restrict__ y_zero, int32_t n_zero4) {
   __shared__ mask::Shared<NT> sh;
   __shared__ uint32_t xs32[SPAX_MAX_DIN / 2];
-  const int tid = threadIdx.x;
-
-  mask::Keys k;
-  const mask::Plan p = mask::build_plan<NT, SPAX_MAX_DIN>(sh, k, xs32, x, a);
-  const bool tier_even = ((uintptr_t)tier & 1) == 0;  // channel pairs start at even j
-  mask::emit<NT>(
-      sh, k, p, true, 0, INT_MAX, 0, INT_MAX,
-      [&](int t, int rank, int j, uint32_t) {
-        if (t == SPAX_TIER_FULL) full_idx[rank] = j;
-        else approx_idx[rank] = j;
-      },
-      [&](int j, uint32_t t0, uint32_t t1, int n) {
-        if (!tier) return;
-        if (n == 2 && tier_even) *reinterpret_cast<uint16_t*>(tier + j) = (uint16_t)(t0 | t1 << 8);
-        else {
-          tier[j] = (uint8_t)t0;
-          if (n == 2) tier[j + 1] = (uint8_t)t1;
-        }
-      });
-  if (tid == 0) {
-    counts[0] = p.n_full;
-    counts[1] = p.n_kept - p.n_full;
-    counts[2] = a.d - p.n_kept;
-  }
+  mask::tiers_to_global<NT, SPAX_MAX_DIN>(sh, xs32, a, x, tier, full_idx, approx_idx, counts);
   // Side job: clear the fp32 output the following GEMV accumulates into.  Issued last, so
   // that waiting for the activation loads never includes these stores.
-  for (int i = tid; i < n_zero4; i += NT) y_zero[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = threadIdx.x; i < n_zero4; i += NT) y_zero[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 }  // namespace

@@ -219,7 +219,15 @@ enum {
   SPAX_STEP_DEFAULT = 0,
   /* one stand-alone mask launch (spax_build_tiers' kernel, which also clears y) and one
    * GEMV launch (spax_tiered_gemv's kernel) per phase */
-  SPAX_STEP_SEPARATE = 1
+  SPAX_STEP_SEPARATE = 1,
+  /* every phase's mask in one launch, then every phase's GEMV in one persistent launch.
+   * Only for phases that are independent: all x ready when the step is enqueued, and no
+   * phase's outputs (tier, lists, counts, y) overlapping another phase's inputs or outputs
+   * (checked; SPAX_ERR_PARAM).  Needs ws of spax_step_workspace_bytes bytes (per-phase
+   * descriptor tables, copied from a library-owned pinned ring of host buffers, so not
+   * capturable in a graph).  events: [0, 1] bracket the mask launch, [2, 3] the GEMV launch
+   * (one phase: [0, 1] bracket both).  Cannot be combined with SPAX_STEP_SEPARATE. */
+  SPAX_STEP_BATCHED = 2
 };
 
 typedef struct spax_step {
@@ -235,8 +243,9 @@ typedef struct spax_step {
   hipEvent_t* events;
 } spax_step;
 
-/* Workspace bytes for spax_decode_step_projections over these phases (the maximum of
- * the per-phase GEMV workspaces; currently 0). */
+/* Workspace bytes for spax_decode_step_projections over these phases: the larger of the
+ * per-phase GEMV workspaces (currently 0) and the SPAX_STEP_BATCHED descriptor tables
+ * (a few hundred bytes per phase).  0 for invalid input. */
 size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases);
 
 /*

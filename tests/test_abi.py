@@ -180,7 +180,8 @@ def test_decode_step_validates_all_phases_first():
     bad = spax.make_phase(L, FAKE, FAKE, spax.topk_params(40, 40), 0, FAKE, FAKE, FAKE, FAKE)
     arr = spax.phase_array([good, good, bad])
     ws = spax.spax_step_workspace_bytes(arr)
-    assert ws == spax.spax_gemv_workspace_bytes(L) == 0
+    assert spax.spax_gemv_workspace_bytes(L) == 0
+    assert 0 < ws < 3 * 1024  # the batched form's descriptor tables
     with pytest.raises(spax.SpaxError) as e:
         spax.spax_decode_step_projections(arr, FAKE, ws_bytes=ws, stream=0)
     assert e.value.status == _lib.SPAX_ERR_PARAM and "phase 2" in str(e.value)
@@ -188,3 +189,37 @@ def test_decode_step_validates_all_phases_first():
         spax.spax_decode_step_projections(spax.phase_array([good]), FAKE, ws_bytes=ws, flags=6,
                                           stream=0)
     assert e.value.status == _lib.SPAX_ERR_UNSUPPORTED
+
+
+@needs_no_gpu
+def test_batched_step_validation():
+    """SPAX_STEP_BATCHED: flag combination, workspace size and independent buffers are
+    checked before anything is enqueued."""
+    L = spax.spax_layout_init(64, [512], 0, 128, 64)
+    MB = 1 << 20
+
+    def phase(i, y=None):
+        base = FAKE + i * 16 * MB
+        return spax.make_phase(L, base, base + MB, spax.topk_params(4, 4), base + 2 * MB,
+                               base + 3 * MB, base + 4 * MB, base + 5 * MB,
+                               y if y is not None else base + 6 * MB)
+    arr = spax.phase_array([phase(0), phase(1)])
+    ws = spax.spax_step_workspace_bytes(arr)
+    assert ws > 0
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections(arr, FAKE + 512 * MB, ws_bytes=ws, flags=3, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_PARAM
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections(arr, None, ws_bytes=0, flags=2, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_WORKSPACE
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections(arr, FAKE + 512 * MB, ws_bytes=ws - 1, flags=2, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_WORKSPACE
+    shared_y = spax.phase_array([phase(0, y=FAKE + 100 * MB), phase(1, y=FAKE + 100 * MB)])
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections(shared_y, FAKE + 512 * MB, ws_bytes=ws, flags=2, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_PARAM and "overlap" in str(e.value)
+    y_on_x = spax.phase_array([phase(0), phase(1, y=FAKE + MB)])  # phase 1's y = phase 0's x
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections(y_on_x, FAKE + 512 * MB, ws_bytes=ws, flags=2, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_PARAM

@@ -1,5 +1,7 @@
 """GPU parity of spax_decode_step_projections: every path the step can take.
 
+flags 0 (fused launches), 1 (mask launch + GEMV launch per phase), 2 (batched: all masks in
+one launch, all GEMVs in one launch) wherever the phases are independent.
 * fused mask+GEMV launches (d_in <= 16384), fp16 and int4 base formats;
 * the two-kernel fallback (d_in > 16384) mixed into the same step;
 * a single column chunk (tiny d_in: plain stores instead of atomics);
@@ -114,7 +116,7 @@ def check(keep, skip_y=()):
         assert err <= REL_L2, (i, err)
 
 
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_fp16_and_int4(env, flags):
     specs = [(1024, [1024, 512, 512], 0, 128, ("guided", 0.5, 0.01)),
              (1024, [1024], 0, 128, ("guided", 0.3, 0.01)),
@@ -124,7 +126,7 @@ def test_step_fp16_and_int4(env, flags):
     check(run_step(env, specs, 101, flags=flags))
 
 
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_both_paths_same_outputs(env, flags):
     """The separate mask + GEMV launches and the fused launch give the same masks."""
     specs = [(4096, [1024, 512, 512], 0, 128, ("guided", 0.5, 0.01)),
@@ -133,7 +135,7 @@ def test_step_both_paths_same_outputs(env, flags):
     check(run_step(env, specs, 707, flags=flags))
 
 
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_wide_input(env, flags):
     """Fused phases whose activation vector needs more LDS than the reduction buffer
     (d_in > 8192): the activations, list slices and reduction area must not overlap."""
@@ -144,7 +146,7 @@ def test_step_wide_input(env, flags):
     check(run_step(env, specs, 606, flags=flags))
 
 
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_fallback_large_din(env, flags):
     specs = [(512, [512], 0, 64, ("guided", 0.5, 0.05)),
              (20000, [256], 0, 128, ("guided", 0.7, 0.01)),     # > 16384: two-kernel path
@@ -153,7 +155,7 @@ def test_step_fallback_large_din(env, flags):
     check(run_step(env, specs, 202, flags=flags))
 
 
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_single_chunk_phases(env, flags):
     specs = [(8, [4096], 0, 128, ("topk", 0.5, 0.25)),   # d_in < 32: one chunk, plain stores
              (20, [64], 0, 64, ("topk", 1.0, 0.0)),
@@ -172,7 +174,7 @@ def test_step_shared_y_buffers(env, flags):
     check(keep, skip_y={1})
 
 
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_repeated_calls_stable(env, flags):
     torch, spax, dev = env
     specs = [(2048, [1536, 512], 0, 128, ("guided", 0.5, 0.01)), (1536, [2048], 0, 128, ("topk", 0.3, 0.3))]
@@ -181,8 +183,10 @@ def test_step_repeated_calls_stable(env, flags):
     # run the same phases again through a fresh step call on the same buffers
     phases = [spax.make_phase(L, packed, b["x"], _params(spax, oa), b["tier"], b["f"], b["a"],
                               b["c"], b["y"]) for (L, O, Ws, x16, oa, packed, b) in keep]
+    arr = spax.phase_array(phases)
+    ws = torch.zeros(max(1, spax.spax_step_workspace_bytes(arr)), dtype=torch.uint8, device=dev)
     for _ in range(5):
-        spax.spax_decode_step_projections(spax.phase_array(phases), None, ws_bytes=0, flags=flags)
+        spax.spax_decode_step_projections(arr, ws, flags=flags)
     torch.cuda.synchronize()
     for f0, (*_, b) in zip(first, keep):
         assert rel_l2(b["y"].cpu().numpy(), f0) <= 1e-6
@@ -206,7 +210,7 @@ def _tie_inputs(seed):
     return {0: x0, 1: x1, 2: x2, 3: x3, 4: x4}
 
 
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_ties(env, flags):
     """Boundaries that keep some but not all channels of one magnitude: ties go by channel
     order in both launch forms."""
@@ -218,7 +222,7 @@ def test_step_ties(env, flags):
     check(run_step(env, specs, 808, flags=flags, xs=_tie_inputs(808)))
 
 
-@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_special_values(env, flags):
     """-0, subnormals, infinities and NaN order by their key; masks and lists stay exact
     (y is not compared where x holds infinities or NaN)."""
@@ -235,3 +239,11 @@ def test_step_special_values(env, flags):
              (4096, [512], 1, 128, ("threshold", 0.5, 1.5))]
     keep = run_step(env, specs, 909, flags=flags, xs={0: x0, 1: x1, 2: x1})
     check(keep, skip_y={1, 2})
+
+
+def test_step_batched_rejects_shared_outputs(env):
+    torch, spax, dev = env
+    specs = [(512, [1024], 0, 128, ("guided", 0.5, 0.05)), (640, [1024], 0, 128, ("topk", 0.3, 0.3))]
+    with pytest.raises(spax.SpaxError) as e:
+        run_step(env, specs, 405, share_y={1}, flags=2)
+    assert "overlap" in str(e.value)
