@@ -14,6 +14,7 @@
 // reach the device as two descriptor tables copied into the caller's workspace from a
 // library-owned ring of pinned host buffers.
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -91,13 +92,20 @@ __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDe
   }
 }
 
-// Column chunks of a batched phase: about kBatchChannels input channels each (at least 16).
-constexpr int kBatchChannels = 256;
+int env_or(const char* name, int dflt) {
+  const char* v = getenv(name);
+  const int x = v ? atoi(v) : 0;
+  return x > 0 ? x : dflt;
+}
 
+// Column chunks of a batched phase: about 2048 input channels each, so a work item streams
+// hundreds of columns and its fixed cost (lists, reduction, atomics) stays small;
+// SPAX_BATCH_CHANNELS overrides.
 GemvPlan batched_plan(const spax_layout* L) {
+  static const int channels = env_or("SPAX_BATCH_CHANNELS", 2048);
   GemvPlan p{};
   p.n_tiles = (int32_t)((L->d_out_total + kTileRows - 1) / kTileRows);
-  int k = (L->d_in + kBatchChannels - 1) / kBatchChannels;
+  int k = (L->d_in + channels - 1) / channels;
   const int kmax = L->d_in / 16 > 1 ? L->d_in / 16 : 1;
   p.n_chunks = k < 1 ? 1 : (k > kmax ? kmax : k);
   p.ws_bytes = 0;
@@ -206,7 +214,16 @@ int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s) {
     SPAX_HIP_CHECK(hipEventRecord(st->events[1], s));
     SPAX_HIP_CHECK(hipEventRecord(st->events[2], s));
   }
-  const int64_t grid = items < (int64_t)n_cu * 4 ? items : (int64_t)n_cu * 4;
+  // as many workgroups as can be resident at once (SPAX_BATCH_WGS_PER_CU overrides)
+  static const int per_cu = [] {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, batched_gemv_kernel, kGemvThreads, 0) !=
+            hipSuccess || occ < 1)
+      occ = 2;
+    return env_or("SPAX_BATCH_WGS_PER_CU", occ);
+  }();
+  const int64_t cap = (int64_t)n_cu * per_cu;
+  const int64_t grid = items < cap ? items : cap;
   if (grid > 0) {
     hipLaunchKernelGGL(batched_gemv_kernel, dim3((unsigned)grid), dim3(kGemvThreads), 0, s, dgd,
                        n, (int)items);

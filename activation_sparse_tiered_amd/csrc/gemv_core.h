@@ -88,6 +88,27 @@ __device__ __forceinline__ void fma_int2x8(float (&acc)[8], float a, uint32_t c)
   acc[7] = fmaf(a, (float)(t3 >> 8), acc[7]);
 }
 
+// Weight codes are read once per token: optionally as non-temporal loads.
+#ifndef SPAX_NT_LOADS
+#define SPAX_NT_LOADS 1
+#endif
+__device__ __forceinline__ uint32_t load_stream(const uint32_t* p) {
+#if SPAX_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+#if SPAX_NT_LOADS
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+
 // A block of up to 64 entries of a column list held in registers, one per lane: entry =
 // channel | (fp16 bits of x_j) << 16, for list positions [base, base + 64).  Loaded with one
 // vector load of the indices and one gather of the activations (two dependent round trips per
@@ -170,9 +191,9 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
         srcF.get(fi + u, j, xf[u]);
         const uint8_t* col = packed + (int64_t)j * sh.stride_F;
         if (FMT == SPAX_FMT_FP16) {
-          vf[u] = *reinterpret_cast<const uint4*>(col + loffF);
+          vf[u] = load_stream(reinterpret_cast<const uint4*>(col + loffF));
         } else {
-          cf[u] = *reinterpret_cast<const uint32_t*>(col + loffF);
+          cf[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffF));
           sf[u] = *reinterpret_cast<const uint32_t*>(col + szoffF);
         }
       }
@@ -183,7 +204,7 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
         int j;
         srcA.get(ai + u, j, xa[u]);
         const uint8_t* col = regionA + (int64_t)j * sh.stride_A;
-        ca[u] = *reinterpret_cast<const uint32_t*>(col + loffA4);
+        ca[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffA4));
         sa[u] = *reinterpret_cast<const uint32_t*>(col + szoffA);
       }
     }
