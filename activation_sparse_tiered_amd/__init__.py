@@ -13,13 +13,14 @@ import ctypes as C
 STEP_DEFAULT, STEP_SEPARATE, STEP_BATCHED = 0, 1, 2
 
 from ._lib import (FMT_FP16, FMT_INT4, MAX_DIN, MAX_MATS, MODE_THRESHOLD, MODE_TOPK,  # noqa: F401
-                   MODE_TOPK_GUIDED, TIER_APPROX, TIER_FULL, TIER_SKIP, Layout, Phase,
-                   SpaxError, Step, TierParams, check, lib, LIB_PATH)
+                   MODE_TOPK_GUIDED, TIER_APPROX, TIER_FULL, TIER_SKIP, Layout, MoveStats,
+                   Phase, SpaxError, Step, TierParams, check, lib, LIB_PATH)
 
 __all__ = [
     "spax_layout_init", "spax_pack_columns", "spax_build_tiers", "spax_gemv_workspace_bytes",
     "spax_tiered_gemv", "spax_step_workspace_bytes", "spax_decode_step_projections",
     "spax_key_threshold", "spax_counts_from_fractions", "spax_guided_bounds", "spax_version",
+    "spax_column_ranges", "spax_pinned_workspace_bytes", "spax_tiered_gemv_pinned", "MoveStats",
     "topk_params", "threshold_params", "guided_params", "make_phase", "Layout", "TierParams",
     "Phase", "Step", "SpaxError", "LIB_PATH",
 ]
@@ -113,6 +114,39 @@ def spax_tiered_gemv(layout: Layout, packed, x, full_idx, approx_idx, counts, y,
                                _ptr(approx_idx), _ptr(counts), _ptr(y), _ptr(ws), int(ws_bytes),
                                _stream(stream)),
           "spax_tiered_gemv")
+
+
+# ------------------------------------------------------------------ pinned-host path
+
+def spax_column_ranges(idx, gap: int = 0):
+    """Ascending channel indices -> [(first, count), ...] after merging gaps of <= gap."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    n = int(a.size)
+    first = np.zeros(max(n, 1), dtype=np.int32)
+    count = np.zeros(max(n, 1), dtype=np.int32)
+    nr = C.c_int32()
+    check(lib.spax_column_ranges(a.ctypes.data if n else None, n, int(gap), first.ctypes.data,
+                                 count.ctypes.data, C.byref(nr)), "spax_column_ranges")
+    return [(int(first[i]), int(count[i])) for i in range(nr.value)]
+
+
+def spax_pinned_workspace_bytes(layout: Layout) -> int:
+    return int(lib.spax_pinned_workspace_bytes(C.byref(layout)))
+
+
+def spax_tiered_gemv_pinned(layout: Layout, packed_host, x, full_idx, approx_idx, counts, y,
+                            gap: int, ws, ws_bytes: int | None = None, stream=None) -> MoveStats:
+    """The blob in pinned host memory (e.g. a torch tensor with pin_memory=True); returns the
+    byte account of the call."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    st = MoveStats()
+    check(lib.spax_tiered_gemv_pinned(C.byref(layout), _ptr(packed_host), _ptr(x), _ptr(full_idx),
+                                      _ptr(approx_idx), _ptr(counts), _ptr(y), int(gap), _ptr(ws),
+                                      int(ws_bytes), C.byref(st), _stream(stream)),
+          "spax_tiered_gemv_pinned")
+    return st
 
 
 # ------------------------------------------------------------------ decode step

@@ -57,6 +57,12 @@ class Step(C.Structure):
                 ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("events", C.POINTER(C.c_void_p))]
 
 
+class MoveStats(C.Structure):
+    _fields_ = [("selected_bytes", C.c_int64), ("moved_bytes", C.c_int64),
+                ("list_bytes", C.c_int64), ("n_ranges", C.c_int32), ("n_full", C.c_int32),
+                ("n_approx", C.c_int32), ("reserved0", C.c_int32)]
+
+
 def _hip_runtimes():
     """Paths of the HIP runtime libraries mapped into this process."""
     out = set()
@@ -92,6 +98,10 @@ def _load():
         "spax_tiered_gemv": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, P, C.c_size_t, P]),
         "spax_step_workspace_bytes": (C.c_size_t, [C.POINTER(Phase), C.c_int32]),
         "spax_decode_step_projections": (C.c_int, [C.POINTER(Step), P]),
+        "spax_column_ranges": (C.c_int, [P, C.c_int32, C.c_int32, P, P, C.POINTER(C.c_int32)]),
+        "spax_pinned_workspace_bytes": (C.c_size_t, [C.POINTER(Layout)]),
+        "spax_tiered_gemv_pinned": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, C.c_int32, P,
+                                              C.c_size_t, C.POINTER(MoveStats), P]),
         "spax_key_threshold": (C.c_int32, [C.c_double]),
         "spax_counts_from_fractions": (C.c_int, [C.c_int32, C.c_double, C.c_double,
                                                  C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),

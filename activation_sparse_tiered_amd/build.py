@@ -29,7 +29,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["host.cpp", "api.cpp", "pack.hip", "tiers.hip", "gemv.hip", "decode.hip", "batch.hip"]
+SOURCES = ["host.cpp", "api.cpp", "pack.hip", "tiers.hip", "gemv.hip", "decode.hip", "batch.hip", "pinned.cpp"]
 
 
 def hipcc() -> str:

@@ -126,6 +126,45 @@ int spax_tiered_gemv(const spax_layout* L, const void* packed, const uint16_t* x
   return launch_tiered_gemv(L, plan, packed, x, full_idx, approx_idx, counts, y, false, stream);
 }
 
+int spax_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* first,
+                       int32_t* count, int32_t* n_ranges) {
+  clear_error();
+  if (!n_ranges || (n > 0 && !idx)) return fail(SPAX_ERR_NULL, "idx and n_ranges are required");
+  if (n < 0 || gap < 0) return fail(SPAX_ERR_PARAM, "n %d and gap %d must be >= 0", n, gap);
+  const int32_t r = build_column_ranges(idx, n, gap, first, count);
+  if (r < 0) return fail(SPAX_ERR_PARAM, "idx must be ascending, distinct and non-negative");
+  *n_ranges = r;
+  return SPAX_OK;
+}
+
+size_t spax_pinned_workspace_bytes(const spax_layout* L) {
+  if (!L || !layout_ok(L)) return 0;
+  return pinned_workspace_bytes(L);
+}
+
+int spax_tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
+                            const int32_t* full_idx, const int32_t* approx_idx,
+                            const int32_t* counts, float* y, int32_t gap, void* ws,
+                            size_t ws_bytes, spax_move_stats* stats, hipStream_t stream) {
+  clear_error();
+  GemvPlan plan;
+  // the device-side arguments as for spax_tiered_gemv (packed_host stands in for packed)
+  int st = check_gemv_args(L, packed_host, x, full_idx, approx_idx, counts, y, nullptr, 0, &plan);
+  if (st) return st;
+  if (gap < 0) return fail(SPAX_ERR_PARAM, "gap %d < 0", gap);
+  if (!ws) return fail(SPAX_ERR_NULL, "ws is required");
+  if (!aligned(ws, 256)) return fail(SPAX_ERR_ALIGN, "ws must be 256-byte aligned");
+  if (ws_bytes < pinned_workspace_bytes(L))
+    return fail(SPAX_ERR_WORKSPACE, "ws_bytes %zu < %zu", ws_bytes, pinned_workspace_bytes(L));
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, packed_host) != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(SPAX_ERR_PARAM, "packed_host is not pinned host memory");
+  }
+  return tiered_gemv_pinned(L, packed_host, x, full_idx, approx_idx, counts, y, gap, ws, stats,
+                            stream);
+}
+
 size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases) {
   if (!phases || n_phases < 1) return 0;
   size_t mx = batched_workspace_bytes(n_phases);

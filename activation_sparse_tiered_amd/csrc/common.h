@@ -83,10 +83,24 @@ int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s);
 
 inline size_t aligned_size(size_t b) { return (b + 255) / 256 * 256; }
 
+// ------------------------------------------------------------------ pinned-host path
+// Ranges of an ascending list (-1 if it is not ascending / distinct / non-negative).
+int32_t build_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* first,
+                            int32_t* count);
+size_t pinned_workspace_bytes(const spax_layout* L);
+// Validated arguments; see spax_tiered_gemv_pinned.
+int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
+                       const int32_t* full_idx, const int32_t* approx_idx,
+                       const int32_t* counts, float* y, int32_t gap, void* ws,
+                       spax_move_stats* stats, hipStream_t s);
+
 // y_zeroed: y already holds zeros (stream-ordered); otherwise a zero fill is enqueued first
 // whenever the plan splits K.
+// compact: the lists hold slot | channel << 16 entries into a compacted staging copy of the
+// records, which `packed` then points to (pinned-host path).
 int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* packed,
                        const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
-                       const int32_t* counts, float* y, bool y_zeroed, hipStream_t s);
+                       const int32_t* counts, float* y, bool y_zeroed, hipStream_t s,
+                       bool compact = false);
 
 }  // namespace spax

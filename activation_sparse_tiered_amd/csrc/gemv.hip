@@ -20,7 +20,7 @@ namespace {
 
 using gemv::kWaves;
 
-template <int FMT>
+template <int FMT, bool kCompact>
 __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
     gemv::Shape sh, const uint8_t* __restrict__ packed, const uint32_t* __restrict__ x32,
     const int32_t* __restrict__ full_idx, const int32_t* __restrict__ approx_idx,
@@ -28,7 +28,8 @@ __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
   __shared__ float red[kWaves][kTileRows];
   const int tile = (int)(blockIdx.x % (uint32_t)sh.n_tiles);
   const int chunk = (int)(blockIdx.x / (uint32_t)sh.n_tiles);
-  gemv::gemv_item<FMT>(sh, packed, x32, full_idx, approx_idx, counts, y, tile, chunk, red);
+  gemv::gemv_item<FMT, kCompact>(sh, packed, x32, full_idx, approx_idx, counts, y, tile, chunk,
+                                 red);
 }
 
 __global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ p, int64_t n4) {
@@ -85,7 +86,8 @@ int launch_zero_f32(float* y, int64_t n, hipStream_t s) {
 
 int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* packed,
                        const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
-                       const int32_t* counts, float* y, bool y_zeroed, hipStream_t s) {
+                       const int32_t* counts, float* y, bool y_zeroed, hipStream_t s,
+                       bool compact) {
   if (plan.n_chunks > 1 && !y_zeroed) {
     int st = launch_zero_f32(y, L->d_out_total, s);
     if (st) return st;
@@ -94,12 +96,17 @@ int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* p
   const dim3 grid((unsigned)(plan.n_tiles * plan.n_chunks));
   const auto* pk = static_cast<const uint8_t*>(packed);
   const auto* x32 = reinterpret_cast<const uint32_t*>(x);
-  if (L->base_fmt == SPAX_FMT_FP16)
-    hipLaunchKernelGGL(tiered_gemv_kernel<SPAX_FMT_FP16>, grid, dim3(kGemvThreads), 0, s, sh, pk,
-                       x32, full_idx, approx_idx, counts, y);
-  else
-    hipLaunchKernelGGL(tiered_gemv_kernel<SPAX_FMT_INT4>, grid, dim3(kGemvThreads), 0, s, sh, pk,
-                       x32, full_idx, approx_idx, counts, y);
+#define SPAX_GEMV_LAUNCH(F, C)                                                              \
+  hipLaunchKernelGGL((tiered_gemv_kernel<F, C>), grid, dim3(kGemvThreads), 0, s, sh, pk, x32, \
+                     full_idx, approx_idx, counts, y)
+  if (L->base_fmt == SPAX_FMT_FP16) {
+    if (compact) SPAX_GEMV_LAUNCH(SPAX_FMT_FP16, true);
+    else SPAX_GEMV_LAUNCH(SPAX_FMT_FP16, false);
+  } else {
+    if (compact) SPAX_GEMV_LAUNCH(SPAX_FMT_INT4, true);
+    else SPAX_GEMV_LAUNCH(SPAX_FMT_INT4, false);
+  }
+#undef SPAX_GEMV_LAUNCH
   SPAX_HIP_CHECK(hipGetLastError());
   return SPAX_OK;
 }

@@ -135,6 +135,20 @@ __device__ __forceinline__ RegBlock load_block(const int32_t* __restrict__ idx,
   return RegBlock{j | (xb << 16), base};
 }
 
+// The same for a compacted list (pinned-host path): entry = staging slot | channel << 16; the
+// returned entry holds the slot (the record to read) and x of the channel.
+__device__ __forceinline__ RegBlock load_block_compact(const uint32_t* __restrict__ ent,
+                                                       const uint16_t* __restrict__ x16,
+                                                       int base, int end, uint32_t jmax) {
+  const int lane = threadIdx.x & 63;
+  const int i = base + lane;
+  uint32_t v = 0;
+  if (i < end) v = ent[i];
+  const uint32_t slot = min(v & 0xFFFFu, jmax), j = min(v >> 16, jmax);
+  const uint32_t xb = i < end ? (uint32_t)x16[j] : 0u;
+  return RegBlock{slot | (xb << 16), base};
+}
+
 // Column lists in LDS (fused kernel): entry = channel | (fp16 bits of x_j) << 16, indexed
 // from the workgroup's first rank `base`.  The channel is clamped to [0, d_in) like the
 // global lists, so a corrupted entry can never address outside the blob.
@@ -266,8 +280,10 @@ __device__ __forceinline__ void finish_tile(float (*red)[kTileRows], const float
 
 // One work item of the stand-alone GEMV: row tile `tile`, column chunk `chunk` of the lists
 // in global memory (counts and indices clamped to [0, d_in], so malformed lists cannot
-// address outside the blob).  A workgroup of kWaves waves; ends after the tile's atomics.
-template <int FMT>
+// address outside the blob).  kCompact: the lists hold slot | channel << 16 entries into a
+// compacted staging copy of the records (`packed` is then the staging buffer).  A workgroup
+// of kWaves waves; ends after the tile's atomics.
+template <int FMT, bool kCompact = false>
 __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __restrict__ packed,
                                           const uint32_t* __restrict__ x32,
                                           const int32_t* __restrict__ full_idx,
@@ -300,8 +316,14 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
   // 64 list entries per tier and block; the channels fit the 16-bit entry field (d_in <= 32768)
   for (int fi = wfb, ai = wab; fi < wfe || ai < wae; fi += 64, ai += 64) {
     const int fend = min(fi + 64, wfe), aend = min(ai + 64, wae);
-    const RegBlock bf = load_block(full_idx, x16, fi, fend, jmax);
-    const RegBlock ba = load_block(approx_idx, x16, ai, aend, jmax);
+    RegBlock bf, ba;
+    if (kCompact) {
+      bf = load_block_compact(reinterpret_cast<const uint32_t*>(full_idx), x16, fi, fend, jmax);
+      ba = load_block_compact(reinterpret_cast<const uint32_t*>(approx_idx), x16, ai, aend, jmax);
+    } else {
+      bf = load_block(full_idx, x16, fi, fend, jmax);
+      ba = load_block(approx_idx, x16, ai, aend, jmax);
+    }
     stream_columns<FMT>(sh, packed, row, fi, max(fi, fend), bf, ai, max(ai, aend), ba, acc, zsum);
   }
   finish_tile<kWaves>(red, acc, zsum, wave, lane, row0, T, sh.n_chunks, y);

@@ -193,6 +193,63 @@ int spax_tiered_gemv(const spax_layout* L, const void* packed, const uint16_t* x
                      const int32_t* counts, float* y, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/* ---------------------------------------------------------------- pinned-host path */
+
+/*
+ * Read ranges of one column list (host helper).  Pages: eigenradar commentary on SpAx, "The
+ * route outside GPU memory", third paragraph (adjacent read ranges are merged; coarse
+ * granularity can move more bytes than were selected).
+ *   idx      : host array of n ascending, distinct, non-negative channel indices.
+ *   gap      : runs of consecutive channels separated by at most `gap` unselected channels
+ *              are merged into one range (the gap columns are moved too); 0 merges only
+ *              adjacent channels.
+ *   first, count : host arrays of capacity n receiving each range (may be NULL to count only).
+ *   n_ranges : receives the number of ranges.
+ * Errors: SPAX_ERR_NULL, SPAX_ERR_PARAM (n < 0, gap < 0, idx not ascending / distinct /
+ * non-negative).
+ */
+int spax_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* first,
+                       int32_t* count, int32_t* n_ranges);
+
+/* Byte account of one spax_tiered_gemv_pinned call. */
+typedef struct spax_move_stats {
+  int64_t selected_bytes;  /* n_full * stride_F + n_approx * stride_A                   */
+  int64_t moved_bytes;     /* record bytes copied host -> device (selected + merged gaps) */
+  int64_t list_bytes;      /* compacted list bytes copied host -> device                 */
+  int32_t n_ranges;        /* record copies enqueued (FULL ranges + APPROX ranges)       */
+  int32_t n_full, n_approx;
+  int32_t reserved0;
+} spax_move_stats;
+
+/* Device workspace for spax_tiered_gemv_pinned: a compacted staging copy of the blob's
+ * records (total_bytes, for the case that every column is selected) and two compacted lists
+ * (4 * d_in bytes each); 0 if *L is not initialised. */
+size_t spax_pinned_workspace_bytes(const spax_layout* L);
+
+/*
+ * Tiered GEMV with the packed blob in pinned host memory (allocated with hipHostMalloc).
+ *   packed_host : the blob laid out by *L (e.g. a copy of spax_pack_columns' output).
+ *   x, full_idx, approx_idx, counts, y : device, as for spax_tiered_gemv (the lists as
+ *                 written by spax_build_tiers: ascending).
+ *   gap   : range merging, as for spax_column_ranges.
+ *   ws    : device, >= spax_pinned_workspace_bytes(L) bytes, 256-byte aligned.
+ *   stats : may be NULL.
+ * Reads counts and lists back to the host (this synchronizes `stream`), merges the selected
+ * columns of each region into ranges, copies each range host -> device with hipMemcpyAsync
+ * into a compacted staging area of ws (selected column t of a region lands in slot t plus the
+ * merged gap columns before it), copies the compacted lists (staging slot | channel << 16),
+ * then runs the tiered GEMV over the staged records.  y equals spax_tiered_gemv's on a device
+ * copy of the blob up to the order of fp32 additions.  Returns with the copies and the GEMV
+ * enqueued on `stream`.  Library-owned pinned buffers hold the lists; a later call waits until
+ * the previous call's list copy has completed before reusing them.
+ * Errors: as spax_tiered_gemv, plus SPAX_ERR_PARAM (gap < 0, packed_host not pinned host
+ * memory, lists read back not ascending) and SPAX_ERR_WORKSPACE.
+ */
+int spax_tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
+                            const int32_t* full_idx, const int32_t* approx_idx,
+                            const int32_t* counts, float* y, int32_t gap, void* ws,
+                            size_t ws_bytes, spax_move_stats* stats, hipStream_t stream);
+
 /* ---------------------------------------------------------------- decode step */
 
 /*

@@ -42,6 +42,7 @@ def test_struct_sizes_match_c():
     assert C.sizeof(_lib.TierParams) == 56
     assert C.sizeof(_lib.Phase) == 120
     assert C.sizeof(_lib.Step) == 40
+    assert C.sizeof(_lib.MoveStats) == 40
 
 
 def test_key_threshold_golden_and_oracle():
@@ -223,3 +224,46 @@ def test_batched_step_validation():
     with pytest.raises(spax.SpaxError) as e:
         spax.spax_decode_step_projections(y_on_x, FAKE + 512 * MB, ws_bytes=ws, flags=2, stream=0)
     assert e.value.status == _lib.SPAX_ERR_PARAM
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_column_ranges_match_oracle(seed):
+    """Host range builder of the pinned path against oracle/ranges.py (integer, exact)."""
+    from oracle import ranges as orng
+    r = np.random.default_rng(seed)
+    d = int(r.integers(1, 3000))
+    p = float(r.choice([0.02, 0.2, 0.5, 0.9, 1.0]))
+    idx = np.flatnonzero(r.random(d) < p).astype(np.int32)
+    for gap in (0, 1, 3, 17, 10**6):
+        assert spax.spax_column_ranges(idx, gap) == orng.runs(idx, gap), (seed, gap)
+
+
+def test_column_ranges_errors():
+    for bad in ([3, 2], [1, 1], [-1, 4]):
+        with pytest.raises(spax.SpaxError) as e:
+            spax.spax_column_ranges(bad, 0)
+        assert e.value.status == _lib.SPAX_ERR_PARAM
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_column_ranges([1, 2], -1)
+    assert e.value.status == _lib.SPAX_ERR_PARAM
+
+
+@needs_no_gpu
+def test_pinned_gemv_validation():
+    L = spax.spax_layout_init(64, [512], 0, 128, 64)
+    need = spax.spax_pinned_workspace_bytes(L)
+    assert need >= int(L.total_bytes) + 8 * 64
+    args = dict(x=FAKE, full_idx=FAKE, approx_idx=FAKE, counts=FAKE, y=FAKE)
+
+    def call(packed=FAKE, gap=0, ws=FAKE, ws_bytes=need):
+        return spax.spax_tiered_gemv_pinned(L, packed, args["x"], args["full_idx"],
+                                            args["approx_idx"], args["counts"], args["y"], gap,
+                                            ws, ws_bytes=ws_bytes, stream=0)
+    for kw, status in ((dict(gap=-1), _lib.SPAX_ERR_PARAM), (dict(ws=0), _lib.SPAX_ERR_NULL),
+                       (dict(ws_bytes=need - 1), _lib.SPAX_ERR_WORKSPACE),
+                       (dict(ws=FAKE + 64), _lib.SPAX_ERR_ALIGN),
+                       (dict(packed=FAKE + 64), _lib.SPAX_ERR_ALIGN),
+                       (dict(), _lib.SPAX_ERR_PARAM)):   # FAKE is not pinned host memory
+        with pytest.raises(spax.SpaxError) as e:
+            call(**kw)
+        assert e.value.status == status, kw

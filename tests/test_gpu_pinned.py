@@ -1,0 +1,128 @@
+"""GPU parity of the pinned-host path (spax_tiered_gemv_pinned): the blob in pinned host
+memory, merged record ranges copied over PCIe into a compacted staging area, then the GEMV.
+
+y against the oracle (rel-L2 <= 1e-3) and against spax_tiered_gemv on the device copy of the
+same blob; the byte account (selected / moved bytes, number of ranges) against
+oracle/ranges.py exactly.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import gemv as ogemv
+from oracle import pack as opack
+from oracle import ranges as orng
+from oracle import tiers as otiers
+
+pytestmark = pytest.mark.gpu
+REL_L2 = 1e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import activation_sparse_tiered_amd as spax
+    return torch, spax, torch.device("cuda:0")
+
+
+def rel_l2(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(np.asarray(got, dtype=np.float64) - ref)
+    return num / den if den > 0 else num
+
+
+def setup(env, d_in, d_out, fmt, G, seed, n_full, n_approx, x16=None):
+    torch, spax, dev = env
+    L = spax.spax_layout_init(d_in, d_out, fmt, 128, G)
+    O = opack.Layout(d_in, d_out, fmt, 128, G)
+    Ws = [synth.weights(seed, d_in, r, m) for m, r in enumerate(d_out)]
+    packed = torch.empty(int(L.total_bytes), dtype=torch.uint8, device=dev)
+    spax.spax_pack_columns(L, [torch.from_numpy(w).to(dev) for w in Ws], packed)
+    host = torch.empty(int(L.total_bytes), dtype=torch.uint8, pin_memory=True)
+    host.copy_(packed)
+    if x16 is None:
+        x16 = synth.activations(seed, d_in, 7, channel_scaled=True)
+    b = dict(x=torch.from_numpy(x16).to(dev),
+             f=torch.full((d_in,), -1, dtype=torch.int32, device=dev),
+             a=torch.full((d_in,), -1, dtype=torch.int32, device=dev),
+             c=torch.zeros(3, dtype=torch.int32, device=dev))
+    spax.spax_build_tiers(b["x"], d_in, spax.topk_params(n_full, n_approx), None, b["f"], b["a"],
+                          b["c"])
+    torch.cuda.synchronize()
+    return L, O, Ws, x16, packed, host, b
+
+
+def run_pinned(env, L, host, b, gap):
+    torch, spax, dev = env
+    y = torch.full((int(L.d_out_total),), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(spax.spax_pinned_workspace_bytes(L), dtype=torch.uint8, device=dev)
+    st = spax.spax_tiered_gemv_pinned(L, host, b["x"], b["f"], b["a"], b["c"], y, gap, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), st
+
+
+@pytest.mark.parametrize("fmt,G", [(0, 128), (1, 128), (0, 64)])
+@pytest.mark.parametrize("gap", [0, 3])
+def test_pinned_matches_oracle_and_device_path(env, fmt, G, gap):
+    torch, spax, dev = env
+    d_in, d_out = 2048, [1024, 512, 512]
+    nF, nA = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
+    L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, fmt, G, 31 + fmt, nF, nA)
+    y_pin, st = run_pinned(env, L, host, b, gap)
+    # the device path on the same blob
+    y_dev = torch.empty(int(L.d_out_total), dtype=torch.float32, device=dev)
+    spax.spax_tiered_gemv(L, packed, b["x"], b["f"], b["a"], b["c"], y_dev, None, ws_bytes=0)
+    torch.cuda.synchronize()
+    _, wf, wa, _ = otiers.build_tiers(x16, otiers.MODE_TOPK, n_full=nF, n_approx=nA)
+    ref = ogemv.tiered_gemv(O, Ws, x16, wf, wa)
+    assert rel_l2(y_pin, ref) <= REL_L2
+    assert rel_l2(y_pin, y_dev.cpu().numpy()) <= 1e-6
+    led = orng.ledger(wf, wa, O.stride_F, O.stride_A, gap)
+    assert st.n_full == len(wf) and st.n_approx == len(wa)
+    assert st.selected_bytes == led["selected_bytes"]
+    assert st.moved_bytes == led["moved_bytes"]
+    assert st.n_ranges == led["n_ranges"]
+    assert st.list_bytes == 4 * (len(wf) + len(wa))
+
+
+def test_pinned_all_skip_and_all_full(env):
+    torch, spax, dev = env
+    d_in, d_out = 1000, [768]
+    L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 128, 5, 0, 0)
+    y, st = run_pinned(env, L, host, b, 0)
+    assert np.all(y == 0) and st.n_ranges == 0 and st.moved_bytes == 0
+    L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 128, 6, d_in, 0)
+    y, st = run_pinned(env, L, host, b, 0)
+    dense = Ws[0].astype(np.float64).T @ x16.astype(np.float64)
+    assert rel_l2(y, dense) <= REL_L2
+    assert st.n_ranges == 1 and st.moved_bytes == d_in * O.stride_F   # one range: every column
+
+
+def test_pinned_repeated_calls_and_wide_gap(env):
+    torch, spax, dev = env
+    d_in, d_out = 4096, [1024]
+    nF, nA = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
+    L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 128, 9, nF, nA)
+    y0, st0 = run_pinned(env, L, host, b, 0)
+    for _ in range(3):
+        y1, st1 = run_pinned(env, L, host, b, 0)
+        assert rel_l2(y1, y0) <= 1e-6 and st1.moved_bytes == st0.moved_bytes
+    y2, st2 = run_pinned(env, L, host, b, d_in)   # everything between the extremes merged
+    assert rel_l2(y2, y0) <= 1e-6
+    assert st2.n_ranges <= 2 and st2.moved_bytes >= st0.moved_bytes
+
+
+def test_pinned_rejects_device_blob(env):
+    torch, spax, dev = env
+    L, O, Ws, x16, packed, host, b = setup(env, 256, [256], 0, 128, 11, 32, 32)
+    ws = torch.empty(spax.spax_pinned_workspace_bytes(L), dtype=torch.uint8, device=dev)
+    y = torch.empty(int(L.d_out_total), dtype=torch.float32, device=dev)
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_tiered_gemv_pinned(L, packed, b["x"], b["f"], b["a"], b["c"], y, 0, ws)
+    assert "pinned" in str(e.value)
