@@ -135,16 +135,21 @@ def spax_pinned_workspace_bytes(layout: Layout) -> int:
     return int(lib.spax_pinned_workspace_bytes(C.byref(layout)))
 
 
+PINNED_MEMCPY, PINNED_GATHER = 0, 1
+
+
 def spax_tiered_gemv_pinned(layout: Layout, packed_host, x, full_idx, approx_idx, counts, y,
-                            gap: int, ws, ws_bytes: int | None = None, stream=None) -> MoveStats:
+                            gap: int, ws, ws_bytes: int | None = None, stream=None,
+                            transfer: int = PINNED_MEMCPY) -> MoveStats:
     """The blob in pinned host memory (e.g. a torch tensor with pin_memory=True); returns the
     byte account of the call."""
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     st = MoveStats()
     check(lib.spax_tiered_gemv_pinned(C.byref(layout), _ptr(packed_host), _ptr(x), _ptr(full_idx),
-                                      _ptr(approx_idx), _ptr(counts), _ptr(y), int(gap), _ptr(ws),
-                                      int(ws_bytes), C.byref(st), _stream(stream)),
+                                      _ptr(approx_idx), _ptr(counts), _ptr(y), int(gap),
+                                      int(transfer), _ptr(ws), int(ws_bytes), C.byref(st),
+                                      _stream(stream)),
           "spax_tiered_gemv_pinned")
     return st
 

@@ -100,8 +100,8 @@ def _load():
         "spax_decode_step_projections": (C.c_int, [C.POINTER(Step), P]),
         "spax_column_ranges": (C.c_int, [P, C.c_int32, C.c_int32, P, P, C.POINTER(C.c_int32)]),
         "spax_pinned_workspace_bytes": (C.c_size_t, [C.POINTER(Layout)]),
-        "spax_tiered_gemv_pinned": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, C.c_int32, P,
-                                              C.c_size_t, C.POINTER(MoveStats), P]),
+        "spax_tiered_gemv_pinned": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, C.c_int32,
+                                              C.c_int32, P, C.c_size_t, C.POINTER(MoveStats), P]),
         "spax_key_threshold": (C.c_int32, [C.c_double]),
         "spax_counts_from_fractions": (C.c_int, [C.c_int32, C.c_double, C.c_double,
                                                  C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),

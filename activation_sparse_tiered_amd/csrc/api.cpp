@@ -144,25 +144,29 @@ size_t spax_pinned_workspace_bytes(const spax_layout* L) {
 
 int spax_tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
                             const int32_t* full_idx, const int32_t* approx_idx,
-                            const int32_t* counts, float* y, int32_t gap, void* ws,
-                            size_t ws_bytes, spax_move_stats* stats, hipStream_t stream) {
+                            const int32_t* counts, float* y, int32_t gap, int32_t transfer,
+                            void* ws, size_t ws_bytes, spax_move_stats* stats,
+                            hipStream_t stream) {
   clear_error();
   GemvPlan plan;
   // the device-side arguments as for spax_tiered_gemv (packed_host stands in for packed)
   int st = check_gemv_args(L, packed_host, x, full_idx, approx_idx, counts, y, nullptr, 0, &plan);
   if (st) return st;
   if (gap < 0) return fail(SPAX_ERR_PARAM, "gap %d < 0", gap);
+  if (transfer != SPAX_PINNED_MEMCPY && transfer != SPAX_PINNED_GATHER)
+    return fail(SPAX_ERR_PARAM, "unknown transfer %d", transfer);
   if (!ws) return fail(SPAX_ERR_NULL, "ws is required");
   if (!aligned(ws, 256)) return fail(SPAX_ERR_ALIGN, "ws must be 256-byte aligned");
   if (ws_bytes < pinned_workspace_bytes(L))
     return fail(SPAX_ERR_WORKSPACE, "ws_bytes %zu < %zu", ws_bytes, pinned_workspace_bytes(L));
   hipPointerAttribute_t attr;
-  if (hipPointerGetAttributes(&attr, packed_host) != hipSuccess || attr.type != hipMemoryTypeHost) {
+  if (hipPointerGetAttributes(&attr, packed_host) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      !attr.devicePointer) {
     (void)hipGetLastError();
-    return fail(SPAX_ERR_PARAM, "packed_host is not pinned host memory");
+    return fail(SPAX_ERR_PARAM, "packed_host is not pinned host memory mapped for the device");
   }
-  return tiered_gemv_pinned(L, packed_host, x, full_idx, approx_idx, counts, y, gap, ws, stats,
-                            stream);
+  return tiered_gemv_pinned(L, packed_host, attr.devicePointer, x, full_idx, approx_idx, counts,
+                            y, gap, transfer, ws, stats, stream);
 }
 
 size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases) {

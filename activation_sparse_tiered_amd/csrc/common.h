@@ -88,11 +88,16 @@ inline size_t aligned_size(size_t b) { return (b + 255) / 256 * 256; }
 int32_t build_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* first,
                             int32_t* count);
 size_t pinned_workspace_bytes(const spax_layout* L);
-// Validated arguments; see spax_tiered_gemv_pinned.
-int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
-                       const int32_t* full_idx, const int32_t* approx_idx,
-                       const int32_t* counts, float* y, int32_t gap, void* ws,
+// Validated arguments; see spax_tiered_gemv_pinned.  host_dev: the device's address of the
+// pinned blob (for SPAX_PINNED_GATHER).
+int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void* host_dev,
+                       const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
+                       const int32_t* counts, float* y, int32_t gap, int32_t transfer, void* ws,
                        spax_move_stats* stats, hipStream_t s);
+// Copy kernel: staging slot t of region F (A) <- record colF[t] (colA[t]) of the mapped blob.
+int launch_gather_records(const spax_layout* L, const void* host_dev, void* staging,
+                          const int32_t* colF, int32_t nF_slots, const int32_t* colA,
+                          int32_t nA_slots, hipStream_t s);
 
 // y_zeroed: y already holds zeros (stream-ordered); otherwise a zero fill is enqueued first
 // whenever the plan splits K.

@@ -11,6 +11,7 @@
 // workgroup reduces" scheme was measured two orders of magnitude slower: a device-scope
 // fence writes back and invalidates the L2 of the caller's XCD.  The order in which chunks
 // land is not fixed, so y may differ in the last bits between runs.
+#include <algorithm>
 #include <cstdlib>
 
 #include "gemv_core.h"
@@ -30,6 +31,26 @@ __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
   const int chunk = (int)(blockIdx.x / (uint32_t)sh.n_tiles);
   gemv::gemv_item<FMT, kCompact>(sh, packed, x32, full_idx, approx_idx, counts, y, tile, chunk,
                                  red);
+}
+
+// Pinned-host gather: staging slot s of a region receives the record of column col[s] read
+// from the mapped host blob.  16-byte chunks, grid-stride; records are multiples of 128 bytes.
+__global__ __launch_bounds__(256) void gather_records_kernel(
+    const uint8_t* __restrict__ host, uint8_t* __restrict__ staging,
+    const int32_t* __restrict__ colF, int64_t chunksF, int64_t strideF,
+    const int32_t* __restrict__ colA, int64_t chunksA, int64_t strideA, int64_t offA) {
+  const int64_t n = chunksF + chunksA;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const bool a = c >= chunksF;
+    const int64_t b = (a ? c - chunksF : c) * 16;
+    const int64_t stride = a ? strideA : strideF;
+    const int64_t base = a ? offA : 0;
+    const int64_t slot = b / stride, in = b - slot * stride;
+    const int32_t col = (a ? colA : colF)[slot];
+    const uint4 v = *reinterpret_cast<const uint4*>(host + base + (int64_t)col * stride + in);
+    *reinterpret_cast<uint4*>(staging + base + b) = v;
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ p, int64_t n4) {
@@ -80,6 +101,19 @@ int launch_zero_f32(float* y, int64_t n, hipStream_t s) {
   const int threads = 256;
   hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n4 + threads - 1) / threads)), dim3(threads),
                      0, s, reinterpret_cast<float4*>(y), n4);
+  SPAX_HIP_CHECK(hipGetLastError());
+  return SPAX_OK;
+}
+
+int launch_gather_records(const spax_layout* L, const void* host_dev, void* staging,
+                          const int32_t* colF, int32_t nF_slots, const int32_t* colA,
+                          int32_t nA_slots, hipStream_t s) {
+  const int64_t cF = (int64_t)nF_slots * L->stride_F / 16, cA = (int64_t)nA_slots * L->stride_A / 16;
+  if (cF + cA == 0) return SPAX_OK;
+  const int64_t blocks = std::min<int64_t>((cF + cA + 255) / 256, 4096);
+  hipLaunchKernelGGL(gather_records_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(host_dev), static_cast<uint8_t*>(staging), colF,
+                     cF, L->stride_F, colA, cA, L->stride_A, L->off_A);
   SPAX_HIP_CHECK(hipGetLastError());
   return SPAX_OK;
 }

@@ -64,9 +64,9 @@ int32_t build_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t*
   });
 }
 
-int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
-                       const int32_t* full_idx, const int32_t* approx_idx,
-                       const int32_t* counts, float* y, int32_t gap, void* ws,
+int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void* host_dev,
+                       const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
+                       const int32_t* counts, float* y, int32_t gap, int32_t transfer, void* ws,
                        spax_move_stats* stats, hipStream_t s) {
   const int d = L->d_in;
   int dev = 0;
@@ -74,7 +74,7 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint
   if (dev < 0 || dev >= 64) return fail(SPAX_ERR_UNSUPPORTED, "device index %d", dev);
   Scratch& sc = g_scratch[dev];
   std::lock_guard<std::mutex> lock(sc.mu);
-  const size_t need = 16 + 16 * (size_t)d;  // counts, two lists in, two lists out
+  const size_t need = 16 + 24 * (size_t)d;  // counts, two lists in, two lists out, 2 tables
   if (sc.pending) {
     SPAX_HIP_CHECK(hipEventSynchronize(sc.done));
     sc.pending = false;
@@ -94,6 +94,9 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint
   int32_t* h_apx = h_full + d;
   uint32_t* h_outF = reinterpret_cast<uint32_t*>(h_apx + d);
   uint32_t* h_outA = h_outF + d;
+  int32_t* h_colF = reinterpret_cast<int32_t*>(h_outA + d);  // staging slot -> column
+  int32_t* h_colA = h_colF + d;
+  const bool gather = transfer == SPAX_PINNED_GATHER;
 
   // ---- the mask, back on the host
   SPAX_HIP_CHECK(hipMemcpyAsync(h_counts, counts, 12, hipMemcpyDeviceToHost, s));
@@ -109,32 +112,48 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint
   int64_t moved = 0;
   int n_ranges = 0;
   int rc = SPAX_OK;
-  const auto region = [&](const int32_t* idx, int n, uint32_t* out, int64_t off, int64_t stride) {
+  const auto region = [&](const int32_t* idx, int n, uint32_t* out, int32_t* col, int64_t off,
+                          int64_t stride) {
     int32_t slot = 0;
     const int r = for_ranges(idx, n, gap, [&](int32_t f, int32_t c, int32_t e0, int32_t ne) {
       if (rc) return;
       for (int32_t k = 0; k < ne; ++k)
         out[e0 + k] = (uint32_t)(slot + (idx[e0 + k] - f)) | ((uint32_t)idx[e0 + k] << 16);
-      const hipError_t e = hipMemcpyAsync(staging + off + (int64_t)slot * stride,
-                                          host + off + (int64_t)f * stride, (size_t)c * stride,
-                                          hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) rc = hip_fail(e, "hipMemcpyAsync of a record range");
+      if (gather) {
+        for (int32_t k = 0; k < c; ++k) col[slot + k] = f + k;
+      } else {
+        const hipError_t e = hipMemcpyAsync(staging + off + (int64_t)slot * stride,
+                                            host + off + (int64_t)f * stride, (size_t)c * stride,
+                                            hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) rc = hip_fail(e, "hipMemcpyAsync of a record range");
+      }
       moved += (int64_t)c * stride;
       slot += c;
     });
     if (r < 0 && !rc) rc = fail(SPAX_ERR_PARAM, "column list read back is not ascending");
     if (r > 0) n_ranges += r;
+    return slot;
   };
-  region(h_full, nF, h_outF, 0, L->stride_F);
+  const int32_t slotsF = region(h_full, nF, h_outF, h_colF, 0, L->stride_F);
   if (rc) return rc;
-  region(h_apx, nA, h_outA, L->off_A, L->stride_A);
+  const int32_t slotsA = region(h_apx, nA, h_outA, h_colA, L->off_A, L->stride_A);
   if (rc) return rc;
   uint32_t* d_listF = reinterpret_cast<uint32_t*>(staging + aligned_size((size_t)L->total_bytes));
   uint32_t* d_listA = d_listF + d;
+  int32_t* d_colF = reinterpret_cast<int32_t*>(d_listA + d);
+  int32_t* d_colA = d_colF + d;
   if (nF) SPAX_HIP_CHECK(hipMemcpyAsync(d_listF, h_outF, 4 * (size_t)nF, hipMemcpyHostToDevice, s));
   if (nA) SPAX_HIP_CHECK(hipMemcpyAsync(d_listA, h_outA, 4 * (size_t)nA, hipMemcpyHostToDevice, s));
+  if (gather) {
+    if (slotsF) SPAX_HIP_CHECK(hipMemcpyAsync(d_colF, h_colF, 4 * (size_t)slotsF, hipMemcpyHostToDevice, s));
+    if (slotsA) SPAX_HIP_CHECK(hipMemcpyAsync(d_colA, h_colA, 4 * (size_t)slotsA, hipMemcpyHostToDevice, s));
+  }
   SPAX_HIP_CHECK(hipEventRecord(sc.done, s));
   sc.pending = true;
+  if (gather) {
+    rc = launch_gather_records(L, host_dev, staging, d_colF, slotsF, d_colA, slotsA, s);
+    if (rc) return rc;
+  }
 
   // ---- the GEMV over the staged records (counts are still the device's)
   rc = launch_tiered_gemv(L, gemv_plan(L), staging, x, reinterpret_cast<const int32_t*>(d_listF),
@@ -153,7 +172,7 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint
 }
 
 size_t pinned_workspace_bytes(const spax_layout* L) {
-  return aligned_size((size_t)L->total_bytes) + 8 * (size_t)L->d_in;
+  return aligned_size((size_t)L->total_bytes) + 16 * (size_t)L->d_in;
 }
 
 }  // namespace spax

@@ -221,9 +221,18 @@ typedef struct spax_move_stats {
   int32_t reserved0;
 } spax_move_stats;
 
+/* spax_tiered_gemv_pinned: how the ranges cross PCIe */
+enum {
+  /* one hipMemcpyAsync per range (host-driven DMA) */
+  SPAX_PINNED_MEMCPY = 0,
+  /* one copy kernel for all ranges: the device reads the mapped pinned blob (zero-copy) and
+   * writes the compacted staging area; the range list goes over as one slot -> column table */
+  SPAX_PINNED_GATHER = 1
+};
+
 /* Device workspace for spax_tiered_gemv_pinned: a compacted staging copy of the blob's
- * records (total_bytes, for the case that every column is selected) and two compacted lists
- * (4 * d_in bytes each); 0 if *L is not initialised. */
+ * records (total_bytes, for the case that every column is selected), two compacted lists and
+ * two slot -> column tables (4 * d_in bytes each); 0 if *L is not initialised. */
 size_t spax_pinned_workspace_bytes(const spax_layout* L);
 
 /*
@@ -232,23 +241,26 @@ size_t spax_pinned_workspace_bytes(const spax_layout* L);
  *   x, full_idx, approx_idx, counts, y : device, as for spax_tiered_gemv (the lists as
  *                 written by spax_build_tiers: ascending).
  *   gap   : range merging, as for spax_column_ranges.
+ *   transfer : SPAX_PINNED_MEMCPY or SPAX_PINNED_GATHER (same bytes moved, same result).
  *   ws    : device, >= spax_pinned_workspace_bytes(L) bytes, 256-byte aligned.
  *   stats : may be NULL.
  * Reads counts and lists back to the host (this synchronizes `stream`), merges the selected
- * columns of each region into ranges, copies each range host -> device with hipMemcpyAsync
- * into a compacted staging area of ws (selected column t of a region lands in slot t plus the
- * merged gap columns before it), copies the compacted lists (staging slot | channel << 16),
+ * columns of each region into ranges, copies the ranges host -> device (see `transfer`) into
+ * a compacted staging area of ws (a range's columns land in consecutive slots, ranges in
+ * order), copies the compacted lists (staging slot | channel << 16),
  * then runs the tiered GEMV over the staged records.  y equals spax_tiered_gemv's on a device
  * copy of the blob up to the order of fp32 additions.  Returns with the copies and the GEMV
  * enqueued on `stream`.  Library-owned pinned buffers hold the lists; a later call waits until
  * the previous call's list copy has completed before reusing them.
- * Errors: as spax_tiered_gemv, plus SPAX_ERR_PARAM (gap < 0, packed_host not pinned host
- * memory, lists read back not ascending) and SPAX_ERR_WORKSPACE.
+ * Errors: as spax_tiered_gemv, plus SPAX_ERR_PARAM (gap < 0, unknown transfer, packed_host
+ * not pinned host memory mapped for the device, lists read back not ascending) and
+ * SPAX_ERR_WORKSPACE.
  */
 int spax_tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
                             const int32_t* full_idx, const int32_t* approx_idx,
-                            const int32_t* counts, float* y, int32_t gap, void* ws,
-                            size_t ws_bytes, spax_move_stats* stats, hipStream_t stream);
+                            const int32_t* counts, float* y, int32_t gap, int32_t transfer,
+                            void* ws, size_t ws_bytes, spax_move_stats* stats,
+                            hipStream_t stream);
 
 /* ---------------------------------------------------------------- decode step */
 

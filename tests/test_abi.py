@@ -252,14 +252,15 @@ def test_column_ranges_errors():
 def test_pinned_gemv_validation():
     L = spax.spax_layout_init(64, [512], 0, 128, 64)
     need = spax.spax_pinned_workspace_bytes(L)
-    assert need >= int(L.total_bytes) + 8 * 64
+    assert need >= int(L.total_bytes) + 16 * 64
     args = dict(x=FAKE, full_idx=FAKE, approx_idx=FAKE, counts=FAKE, y=FAKE)
 
-    def call(packed=FAKE, gap=0, ws=FAKE, ws_bytes=need):
+    def call(packed=FAKE, gap=0, ws=FAKE, ws_bytes=need, transfer=0):
         return spax.spax_tiered_gemv_pinned(L, packed, args["x"], args["full_idx"],
                                             args["approx_idx"], args["counts"], args["y"], gap,
-                                            ws, ws_bytes=ws_bytes, stream=0)
+                                            ws, ws_bytes=ws_bytes, stream=0, transfer=transfer)
     for kw, status in ((dict(gap=-1), _lib.SPAX_ERR_PARAM), (dict(ws=0), _lib.SPAX_ERR_NULL),
+                       (dict(transfer=2), _lib.SPAX_ERR_PARAM),
                        (dict(ws_bytes=need - 1), _lib.SPAX_ERR_WORKSPACE),
                        (dict(ws=FAKE + 64), _lib.SPAX_ERR_ALIGN),
                        (dict(packed=FAKE + 64), _lib.SPAX_ERR_ALIGN),

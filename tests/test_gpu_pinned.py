@@ -58,23 +58,25 @@ def setup(env, d_in, d_out, fmt, G, seed, n_full, n_approx, x16=None):
     return L, O, Ws, x16, packed, host, b
 
 
-def run_pinned(env, L, host, b, gap):
+def run_pinned(env, L, host, b, gap, transfer=0):
     torch, spax, dev = env
     y = torch.full((int(L.d_out_total),), float("nan"), dtype=torch.float32, device=dev)
     ws = torch.empty(spax.spax_pinned_workspace_bytes(L), dtype=torch.uint8, device=dev)
-    st = spax.spax_tiered_gemv_pinned(L, host, b["x"], b["f"], b["a"], b["c"], y, gap, ws)
+    st = spax.spax_tiered_gemv_pinned(L, host, b["x"], b["f"], b["a"], b["c"], y, gap, ws,
+                                      transfer=transfer)
     torch.cuda.synchronize()
     return y.cpu().numpy(), st
 
 
+@pytest.mark.parametrize("transfer", [0, 1])
 @pytest.mark.parametrize("fmt,G", [(0, 128), (1, 128), (0, 64)])
 @pytest.mark.parametrize("gap", [0, 3])
-def test_pinned_matches_oracle_and_device_path(env, fmt, G, gap):
+def test_pinned_matches_oracle_and_device_path(env, fmt, G, gap, transfer):
     torch, spax, dev = env
     d_in, d_out = 2048, [1024, 512, 512]
     nF, nA = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
     L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, fmt, G, 31 + fmt, nF, nA)
-    y_pin, st = run_pinned(env, L, host, b, gap)
+    y_pin, st = run_pinned(env, L, host, b, gap, transfer)
     # the device path on the same blob
     y_dev = torch.empty(int(L.d_out_total), dtype=torch.float32, device=dev)
     spax.spax_tiered_gemv(L, packed, b["x"], b["f"], b["a"], b["c"], y_dev, None, ws_bytes=0)
@@ -91,29 +93,31 @@ def test_pinned_matches_oracle_and_device_path(env, fmt, G, gap):
     assert st.list_bytes == 4 * (len(wf) + len(wa))
 
 
-def test_pinned_all_skip_and_all_full(env):
+@pytest.mark.parametrize("transfer", [0, 1])
+def test_pinned_all_skip_and_all_full(env, transfer):
     torch, spax, dev = env
     d_in, d_out = 1000, [768]
     L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 128, 5, 0, 0)
-    y, st = run_pinned(env, L, host, b, 0)
+    y, st = run_pinned(env, L, host, b, 0, transfer)
     assert np.all(y == 0) and st.n_ranges == 0 and st.moved_bytes == 0
     L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 128, 6, d_in, 0)
-    y, st = run_pinned(env, L, host, b, 0)
+    y, st = run_pinned(env, L, host, b, 0, transfer)
     dense = Ws[0].astype(np.float64).T @ x16.astype(np.float64)
     assert rel_l2(y, dense) <= REL_L2
     assert st.n_ranges == 1 and st.moved_bytes == d_in * O.stride_F   # one range: every column
 
 
-def test_pinned_repeated_calls_and_wide_gap(env):
+@pytest.mark.parametrize("transfer", [0, 1])
+def test_pinned_repeated_calls_and_wide_gap(env, transfer):
     torch, spax, dev = env
     d_in, d_out = 4096, [1024]
     nF, nA = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
     L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 128, 9, nF, nA)
-    y0, st0 = run_pinned(env, L, host, b, 0)
+    y0, st0 = run_pinned(env, L, host, b, 0, transfer)
     for _ in range(3):
-        y1, st1 = run_pinned(env, L, host, b, 0)
+        y1, st1 = run_pinned(env, L, host, b, 0, transfer)
         assert rel_l2(y1, y0) <= 1e-6 and st1.moved_bytes == st0.moved_bytes
-    y2, st2 = run_pinned(env, L, host, b, d_in)   # everything between the extremes merged
+    y2, st2 = run_pinned(env, L, host, b, d_in, transfer)   # everything merged
     assert rel_l2(y2, y0) <= 1e-6
     assert st2.n_ranges <= 2 and st2.moved_bytes >= st0.moved_bytes
 
