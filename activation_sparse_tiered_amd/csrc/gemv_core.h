@@ -11,8 +11,8 @@
 //   FULL fp16 : one 16-byte load per column (8 halves), fp32 FMA with fp16 operands;
 //   FULL int4 : 4 bytes of codes (8 nibbles) + the (s, z) word of the lane's group;
 //   APPROX 2b : 2 bytes of codes (8 two-bit codes) + the (s, z) word of the lane's group.
-// A group spans >= 64 rows, so the zero-point term x_j * z is the same for a lane's 8 rows
-// and is summed once per column into zsum: x_j (s q + z) = (x_j s) q + x_j z.
+// A group spans >= 64 rows, so the zero-point term is the same for a lane's 8 rows and is
+// summed once per column into zsum (see fma_int4x8 for the form the codes take).
 #pragma once
 
 #include "common.h"
@@ -57,35 +57,61 @@ __device__ __forceinline__ void fma_fp16x8(float (&acc)[8], float xv, const uint
   acc[7] = fmaf(xv, half_hi(v.w), acc[7]);
 }
 
-// 8 int4 codes (row 2k in the low nibble of byte k/2) scaled by a.
-__device__ __forceinline__ void fma_int4x8(float (&acc)[8], float a, uint32_t c) {
-  const uint32_t lo = c & 0x0F0F0F0Fu;          // rows 0,2,4,6 in bytes 0..3
-  const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;   // rows 1,3,5,7
-  acc[0] = fmaf(a, (float)(lo & 0xFFu), acc[0]);
-  acc[1] = fmaf(a, (float)(hi & 0xFFu), acc[1]);
-  acc[2] = fmaf(a, (float)((lo >> 8) & 0xFFu), acc[2]);
-  acc[3] = fmaf(a, (float)((hi >> 8) & 0xFFu), acc[3]);
-  acc[4] = fmaf(a, (float)((lo >> 16) & 0xFFu), acc[4]);
-  acc[5] = fmaf(a, (float)((hi >> 16) & 0xFFu), acc[5]);
-  acc[6] = fmaf(a, (float)(lo >> 24), acc[6]);
-  acc[7] = fmaf(a, (float)(hi >> 24), acc[7]);
+// Codes enter the multiply-adds as fp16 operands of v_fma_mix_f32 (an fp32 FMA that reads one
+// half of a packed register), with no integer-to-float conversion: a code q placed in the top
+// mantissa bits under the exponent of 1.0 reads as h = 1 + q / 2^b (b = 4 for int4, 2 for
+// two-bit codes).  Two rows share a register, one per half, so each pair of rows costs one
+// shift and one and-or.  The caller scales by 2^b and removes the constant part:
+// x (s q + z) = (2^b x s) h + x (z - 2^b s).
+constexpr uint32_t kOne16x2 = 0x3C003C00u;  // fp16 1.0 in both halves
+
+// (x & m) | k in one instruction.  Written out because the compiler splits it into two
+// (the three-operand form takes no literal constants, so m and k are passed in registers).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t k) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(k));
+  return r;
 }
 
-// 8 two-bit codes (row 4k+i in bits [2i+1:2i] of byte k; only bits 0..15 of c are read)
-// scaled by a.
-__device__ __forceinline__ void fma_int2x8(float (&acc)[8], float a, uint32_t c) {
-  const uint32_t t0 = c & 0x0303u;          // rows 0 (byte 0) and 4 (byte 1)
-  const uint32_t t1 = (c >> 2) & 0x0303u;   // rows 1, 5
-  const uint32_t t2 = (c >> 4) & 0x0303u;   // rows 2, 6
-  const uint32_t t3 = (c >> 6) & 0x0303u;   // rows 3, 7
-  acc[0] = fmaf(a, (float)(t0 & 0xFFu), acc[0]);
-  acc[4] = fmaf(a, (float)(t0 >> 8), acc[4]);
-  acc[1] = fmaf(a, (float)(t1 & 0xFFu), acc[1]);
-  acc[5] = fmaf(a, (float)(t1 >> 8), acc[5]);
-  acc[2] = fmaf(a, (float)(t2 & 0xFFu), acc[2]);
-  acc[6] = fmaf(a, (float)(t2 >> 8), acc[6]);
-  acc[3] = fmaf(a, (float)(t3 & 0xFFu), acc[3]);
-  acc[7] = fmaf(a, (float)(t3 >> 8), acc[7]);
+// 8 int4 codes (row n in bits [4n+3:4n]) times a = 16 x s: acc[r] += a (1 + q_r / 16).
+__device__ __forceinline__ void fma_int4x8(float (&acc)[8], float a, uint32_t c) {
+  const uint32_t m = 0x03C003C0u;  // mantissa bits 6..9 of both halves
+  const uint32_t h0 = and_or(c << 6, m, kOne16x2);  // rows 0, 4
+  const uint32_t h1 = and_or(c << 2, m, kOne16x2);  // rows 1, 5
+  const uint32_t h2 = and_or(c >> 2, m, kOne16x2);  // rows 2, 6
+  const uint32_t h3 = and_or(c >> 6, m, kOne16x2);  // rows 3, 7
+  acc[0] = fmaf(a, half_lo(h0), acc[0]);
+  acc[4] = fmaf(a, half_hi(h0), acc[4]);
+  acc[1] = fmaf(a, half_lo(h1), acc[1]);
+  acc[5] = fmaf(a, half_hi(h1), acc[5]);
+  acc[2] = fmaf(a, half_lo(h2), acc[2]);
+  acc[6] = fmaf(a, half_hi(h2), acc[6]);
+  acc[3] = fmaf(a, half_lo(h3), acc[3]);
+  acc[7] = fmaf(a, half_hi(h3), acc[7]);
+}
+
+// Byte selector that moves bytes k0 and k0 + 1 of a dword to bytes 1 and 3 (zeros elsewhere).
+__device__ __forceinline__ uint32_t spread_sel(uint32_t k0) {
+  return 0x000C000Cu | (k0 << 8) | ((k0 + 1u) << 24);
+}
+
+// 8 two-bit codes (row 4k+i in bits [2i+1:2i] of byte k0+k of w, k0 given through sel) times
+// a = 4 x s: acc[r] += a (1 + q_r / 4).
+__device__ __forceinline__ void fma_int2x8(float (&acc)[8], float a, uint32_t w, uint32_t sel) {
+  const uint32_t p = __builtin_amdgcn_perm(0u, w, sel);  // rows 0..3 at bits 8.., 4..7 at 24..
+  const uint32_t m = 0x03000300u;  // mantissa bits 8..9 of both halves
+  const uint32_t h0 = and_or(p, m, kOne16x2);        // rows 0, 4
+  const uint32_t h1 = and_or(p >> 2, m, kOne16x2);   // rows 1, 5
+  const uint32_t h2 = and_or(p >> 4, m, kOne16x2);   // rows 2, 6
+  const uint32_t h3 = and_or(p >> 6, m, kOne16x2);   // rows 3, 7
+  acc[0] = fmaf(a, half_lo(h0), acc[0]);
+  acc[4] = fmaf(a, half_hi(h0), acc[4]);
+  acc[1] = fmaf(a, half_lo(h1), acc[1]);
+  acc[5] = fmaf(a, half_hi(h1), acc[5]);
+  acc[2] = fmaf(a, half_lo(h2), acc[2]);
+  acc[6] = fmaf(a, half_hi(h2), acc[6]);
+  acc[3] = fmaf(a, half_lo(h3), acc[3]);
+  acc[7] = fmaf(a, half_hi(h3), acc[7]);
 }
 
 // Weight codes are read once per token: optionally as non-temporal loads.
@@ -181,7 +207,7 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
   // A lane's 2 bytes of two-bit codes are read as the aligned dword that holds them (a
   // 16-bit load would be widened right after it is issued, which makes it wait).
   const uint32_t loffA4 = ((uint32_t)row / 4u) & ~3u;
-  const uint32_t shA = (((uint32_t)row / 4u) & 2u) * 8u;
+  const uint32_t selA = spread_sel(((uint32_t)row / 4u) & 2u);
   const uint32_t szoffA = (uint32_t)(sh.T / 4) + (uint32_t)(row / sh.approx_group) * 4u;
   const uint32_t loffF = FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u;
   const uint32_t szoffF = (uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u;
@@ -227,14 +253,16 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
       if (FMT == SPAX_FMT_FP16) {
         fma_fp16x8(acc, xf[u], vf[u]);
       } else {
-        fma_int4x8(acc, xf[u] * half_lo(sf[u]), cf[u]);
-        zsum = fmaf(xf[u], half_hi(sf[u]), zsum);
+        const float sc = half_lo(sf[u]);
+        fma_int4x8(acc, xf[u] * (16.0f * sc), cf[u]);
+        zsum = fmaf(xf[u], fmaf(-16.0f, sc, half_hi(sf[u])), zsum);
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      fma_int2x8(acc, xa[u] * half_lo(sa[u]), ca[u] >> shA);
-      zsum = fmaf(xa[u], half_hi(sa[u]), zsum);
+      const float sc = half_lo(sa[u]);
+      fma_int2x8(acc, xa[u] * (4.0f * sc), ca[u], selA);
+      zsum = fmaf(xa[u], fmaf(-4.0f, sc, half_hi(sa[u])), zsum);
     }
     fi += max(nf, 0);
     ai += max(na, 0);
