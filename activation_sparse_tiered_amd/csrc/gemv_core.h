@@ -248,21 +248,30 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
         sa[u] = *reinterpret_cast<const uint32_t*>(col + szoffA);
       }
     }
+    // A tier with no column in this round skips its multiplies (a wave-uniform branch around
+    // whole blocks).  The explicit wait for every load makes the branches visible as complete
+    // to the compiler's wait tracking, which otherwise assumes loads of a skipped block are
+    // still in flight in the next round and waits for each of them there.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (nf > 0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (FMT == SPAX_FMT_FP16) {
-        fma_fp16x8(acc, xf[u], vf[u]);
-      } else {
-        const float sc = half_lo(sf[u]);
-        fma_int4x8(acc, xf[u] * (16.0f * sc), cf[u]);
-        zsum = fmaf(xf[u], fmaf(-16.0f, sc, half_hi(sf[u])), zsum);
+      for (int u = 0; u < kUnroll; ++u) {
+        if (FMT == SPAX_FMT_FP16) {
+          fma_fp16x8(acc, xf[u], vf[u]);
+        } else {
+          const float sc = half_lo(sf[u]);
+          fma_int4x8(acc, xf[u] * (16.0f * sc), cf[u]);
+          zsum = fmaf(xf[u], fmaf(-16.0f, sc, half_hi(sf[u])), zsum);
+        }
       }
     }
+    if (na > 0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float sc = half_lo(sa[u]);
-      fma_int2x8(acc, xa[u] * (4.0f * sc), ca[u], selA);
-      zsum = fmaf(xa[u], fmaf(-4.0f, sc, half_hi(sa[u])), zsum);
+      for (int u = 0; u < kUnroll; ++u) {
+        const float sc = half_lo(sa[u]);
+        fma_int2x8(acc, xa[u] * (4.0f * sc), ca[u], selA);
+        zsum = fmaf(xa[u], fmaf(-4.0f, sc, half_hi(sa[u])), zsum);
+      }
     }
     fi += max(nf, 0);
     ai += max(na, 0);
