@@ -6,9 +6,9 @@
 //
 // Default: one fused kernel per group, at most one 1024-thread workgroup per compute unit.
 // Every workgroup loads the activation vector into LDS and finds the two tier boundaries
-// from a per-key histogram (mask_core.h, select_exact), decides the tiers of its own range of
-// input channels, lists those columns in LDS (channel | fp16 x_j << 16 per entry) and streams
-// them for its 512-row tile (gemv_core.h).  One extra workgroup writes the tier bytes, the
+// from a per-key histogram (mask_core.h, select_begin / select_finish), decides the tiers of
+// its own range of input channels, lists those columns in LDS (channel | fp16 x_j << 16 per
+// entry) and streams them for its 512-row tile (gemv_core.h).  One extra workgroup writes the tier bytes, the
 // ascending lists and the counts with the rank-producing mask code, so the outputs equal
 // those of spax_build_tiers.  Repeating the boundary search in every workgroup costs no time
 // (it runs in parallel on separate compute units) and removes the second launch and the
@@ -31,6 +31,17 @@ namespace {
 
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / 64;
+// FULL fp16 columns per wave whose loads are issued before the mask completes (0: none).
+// Not done for int4 columns: a quarter of the bytes per load did not repay the extra work
+// on the mask's path (measured slower).
+#ifndef SPAX_EARLY
+#define SPAX_EARLY 4
+#endif
+template <int FMT>
+struct Early {
+  static constexpr bool use = FMT == SPAX_FMT_FP16 && SPAX_EARLY > 0;
+  static constexpr int n = SPAX_EARLY > 0 ? SPAX_EARLY : 1;
+};
 
 struct FusedArgs {
   TierArgs ta;
@@ -92,11 +103,15 @@ __device__ __forceinline__ void ties_between(const uint32_t* xs32, int begin, in
 // One group: mask and GEMV.  Workgroup gridDim.x - 1 only writes the outputs of the mask
 // (build_plan + emit, as the stand-alone mask kernel).  Every other workgroup owns one
 // 512-row tile and one contiguous range of input channels, split over its 16 waves:
-//   1. the exact boundaries from a per-key histogram (select_exact: one pass over the keys);
+//   1. the exact boundaries from a per-key histogram (select_begin / select_finish: one pass
+//      over the keys); as soon as the coarse bin of the FULL boundary is known, the loads of
+//      the wave's first few columns above that bin (FULL whatever the exact boundary) are
+//      issued, so they are in flight while the boundaries are completed (fp16 columns);
 //   2. each wave decides the tiers of its channels (ties at a boundary key by channel order,
 //      counting the equal keys before its first channel only when it holds such a tie) and
 //      lists its FULL and APPROX columns in LDS;
-//   3. each wave streams its columns; the tile is reduced across waves and added to y.
+//   3. each wave multiplies its early columns and streams the others; the tile is reduced
+//      across waves and added to y.
 template <int FMT, int MAXD>
 __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t dyn[];
@@ -137,10 +152,50 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
   const uint32_t jmax = (uint32_t)d - 1u;
 
-  // ---- 1. boundaries
+  // ---- 1. boundaries, with the first FULL columns already on their way
   mask::Select sel[2];
-  int E[2];
-  mask::select_exact<kFusedThreads, MAXD>(u.kh, k, xs32, a.x, a.ta, sel, E);
+  int E[2], R[2];
+  const bool search = mask::select_begin<kFusedThreads, MAXD>(u.kh, k, xs32, a.x, a.ta, R, sel, E);
+  // Keys >= kc are FULL wherever the exact boundary falls inside its coarse bin (THRESHOLD:
+  // the boundary itself).  The loads of this wave's first kEarly such columns (channel order)
+  // are issued now and stay in flight through the rest of the mask work.
+  int kc = 0x8000;
+  constexpr bool kUseEarly = Early<FMT>::use;
+  constexpr int kEarly = Early<FMT>::n;
+  if (!kUseEarly) {
+  } else if (!search) {
+    kc = sel[0].kb;
+  } else if (R[0] > 0) {
+    int cb, above;
+    mask::coarse_find<kFusedThreads>(u.kh, R[0], lane, cb, above);
+    kc = 32 * (cb + 1);
+  }
+  uint32_t pe[kEarly];
+#pragma unroll
+  for (int q = 0; q < kEarly; ++q) pe[q] = 0u;
+  int np = 0;
+  for (int j0 = ws; kUseEarly && j0 < we && np < kEarly; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t raw = j < we ? (uint32_t)xs16[j] : 0u;
+    uint64_t b = __ballot(j < we && (int)(raw & 0x7FFFu) >= kc);
+    const uint32_t e = (uint32_t)j | (raw << 16);
+    int taken = 0;
+#pragma unroll
+    for (int q = 0; q < kEarly; ++q) {
+      if (q >= np && b != 0) {
+        pe[q] = (uint32_t)__builtin_amdgcn_readlane((int)e, (int)__builtin_ctzll(b));
+        b &= b - 1;
+        ++taken;
+      }
+    }
+    np += taken;
+  }
+#pragma unroll
+  for (int q = 1; q < kEarly; ++q)
+    if (q >= np) pe[q] = pe[q - 1];  // unused slots repeat a used column (or column 0)
+  gemv::EarlyColumns<FMT, kEarly> early;
+  if (kUseEarly) early.issue(sh, a.packed, row, pe, np, jmax);
+  if (search) mask::select_finish<kFusedThreads>(u.kh, R, sel, E);
   const mask::Select s0 = sel[0], s1 = sel[1];
 
   // ---- 2. this wave's tiers and column lists
@@ -179,7 +234,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     ties0 = (c & 0xFFFF) + p0;
     ties1 = (c >> 16) + p1;
   }
-  int nF = 0, nA = 0;
+  int nF = 0, nA = 0, ne = 0;
   for (int j0 = ws; j0 < we; j0 += 64) {
     const int j = j0 + lane;
     const bool v = j < we;
@@ -188,9 +243,14 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     const bool t0 = key == s0.kb, t1 = key == s1.kb;
     const uint64_t b0 = __ballot(t0), b1 = __ballot(t1);
     const int r0 = ties0 + (int)mask::lanes_below(b0), r1 = ties1 + (int)mask::lanes_below(b1);
-    const bool full = key > s0.kb || (t0 && (!need0 || r0 < s0.m));
+    // the early columns are the wave's first np channels with key >= kc
+    const bool cand = key >= kc;
+    const uint64_t bc = __ballot(cand);
+    const bool is_early = cand && ne + (int)mask::lanes_below(bc) < np;
+    ne += mask::popc(bc);
+    const bool full = !is_early && (key > s0.kb || (t0 && (!need0 || r0 < s0.m)));
     const bool kept = key > s1.kb || (t1 && (!need1 || r1 < s1.m));
-    const bool apx = kept && !full;
+    const bool apx = kept && !full && !is_early;
     ties0 += mask::popc(b0);
     ties1 += mask::popc(b1);
     const uint32_t e = (uint32_t)j | (raw << 16);
@@ -207,6 +267,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
 #pragma unroll
   for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
   float zsum = 0.0f;
+  if (kUseEarly) early.multiply(acc, zsum);
   gemv::stream_columns<FMT>(sh, a.packed, row, 0, nF, gemv::LdsList{lF, 0, jmax}, 0, nA,
                             gemv::LdsList{lA, 0, jmax}, acc, zsum);
   __syncthreads();  // every wave is done with the mask scratch that `red` overlays

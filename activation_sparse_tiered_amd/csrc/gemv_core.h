@@ -189,6 +189,48 @@ struct LdsList {
   }
 };
 
+// Up to P FULL columns whose loads are issued ahead of the rest of the work and multiplied
+// later (the fused decode kernel issues them while its mask is still being completed, so
+// their memory latency overlaps that work).  Entries as in LdsList.  All P loads are issued
+// (a conditional load would make the compiler copy its result right away, which waits for
+// it): slots past n load the entry the caller put there (a repeat of a used column, which
+// costs no extra HBM traffic, or column 0) and are multiplied by a zero activation.
+template <int FMT, int P>
+struct EarlyColumns {
+  float xv[P];
+  uint4 v[P];
+  uint32_t c[P], sz[P];
+  __device__ __forceinline__ void issue(const Shape& sh, const uint8_t* __restrict__ packed,
+                                        int row, const uint32_t (&e)[P], int n, uint32_t jmax) {
+    const uint32_t loffF = FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u;
+    const uint32_t szoffF = (uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u;
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const uint32_t j = min(e[u] & 0xFFFFu, jmax);
+      xv[u] = u < n ? half_hi(e[u]) : 0.0f;
+      const uint8_t* col = packed + (int64_t)j * sh.stride_F;
+      if (FMT == SPAX_FMT_FP16) {
+        v[u] = load_stream(reinterpret_cast<const uint4*>(col + loffF));
+      } else {
+        c[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffF));
+        sz[u] = *reinterpret_cast<const uint32_t*>(col + szoffF);
+      }
+    }
+  }
+  __device__ __forceinline__ void multiply(float (&acc)[8], float& zsum) const {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      if (FMT == SPAX_FMT_FP16) {
+        fma_fp16x8(acc, xv[u], v[u]);
+      } else {
+        const float sc = half_lo(sz[u]);
+        fma_int4x8(acc, xv[u] * (16.0f * sc), c[u]);
+        zsum = fmaf(xv[u], fmaf(-16.0f, sc, half_hi(sz[u])), zsum);
+      }
+    }
+  }
+};
+
 // FULL columns [fb, fe) of `srcF` and APPROX (two-bit) columns [ab, ae) of `srcA` into
 // acc / zsum.  Each round issues the loads of up to kUnroll FULL and kUnroll APPROX columns
 // back to back (the counts are wave-uniform, so the guards are scalar branches) and only then

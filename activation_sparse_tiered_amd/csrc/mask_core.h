@@ -202,7 +202,8 @@ __device__ __forceinline__ void plan_stage1(Shared<NT>& sh, Keys& k, uint32_t* x
       for (int e = 0; e < 2; ++e) {
         const bool valid = k.valid(s, lane, e);
         const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
-        if (valid) atomicAdd(&sh.hist_rep[(lane & (S::kCopies - 1)) * S::kStride + (key >> 7)], 1);
+        // unconditional (zero past the range): see select_begin
+        atomicAdd(&sh.hist_rep[(lane & (S::kCopies - 1)) * S::kStride + (key >> 7)], valid ? 1 : 0);
         nat += valid && key < a.k_tau;
       }
     }
@@ -277,8 +278,8 @@ __device__ __forceinline__ Plan plan_stage2(Shared<NT>& sh, const Keys& k, const
         const bool valid = k.valid(s, lane, e);
         const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
         const int hi = valid ? key >> 7 : -2;
-        if (hi == b0) atomicAdd(&sh.wave_hist[0][wave][key & 127], 1);
-        if (hi == b1) atomicAdd(&sh.wave_hist[1][wave][key & 127], 1);
+        atomicAdd(&sh.wave_hist[0][wave][key & 127], hi == b0 ? 1 : 0);  // see select_begin
+        atomicAdd(&sh.wave_hist[1][wave][key & 127], hi == b1 ? 1 : 0);
         above += (b0 >= 0 && hi > b0 ? 1 : 0) + (b1 >= 0 && hi > b1 ? 0x10000 : 0);
       }
     }
@@ -370,13 +371,15 @@ struct KeyHist {
   int E[2];
 };
 
-// Loads x into LDS (xs32: roundup(d, 2) halves) and returns both boundaries and, for each,
-// the number of channels whose key equals it (E; 0 for THRESHOLD, whose boundaries keep all
-// their ties).  Sets k like build_plan.  Contains the barriers it needs and ends with one.
+// Exact boundaries from a per-key histogram, in two parts (a caller may do other work in
+// between).  select_begin loads x into LDS (xs32: roundup(d, 2) halves), sets k like
+// build_plan, builds the per-key histogram and its coarse sums, and gives every wave the two
+// target ranks R (FULL, kept; counted from the largest key).  For THRESHOLD the boundaries
+// are the given keys: sel and E are set and false is returned.  Ends with a barrier.
 template <int NT, int MAXD>
-__device__ __forceinline__ void select_exact(KeyHist<NT>& h, Keys& k, uint32_t* xs32,
+__device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* xs32,
                                              const uint16_t* __restrict__ x, const TierArgs& a,
-                                             Select (&sel)[2], int (&E)[2]) {
+                                             int (&R)[2], Select (&sel)[2], int (&E)[2]) {
   constexpr int W = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -410,7 +413,8 @@ __device__ __forceinline__ void select_exact(KeyHist<NT>& h, Keys& k, uint32_t* 
     sel[0] = Select{a.k_full, d};
     sel[1] = Select{a.k_skip, d};
     E[0] = E[1] = 0;
-    return;
+    R[0] = R[1] = 0;
+    return false;
   }
   int nat = 0;
   for (int s = 0; s < k.steps; ++s) {
@@ -419,7 +423,9 @@ __device__ __forceinline__ void select_exact(KeyHist<NT>& h, Keys& k, uint32_t* 
     for (int e = 0; e < 2; ++e) {
       const bool valid = k.valid(s, lane, e);
       const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
-      if (valid) atomicAdd(&h.fine[key >> 1], 1u << ((key & 1) << 4));
+      // Unconditional (a zero increment past the range): a conditional LDS atomic makes the
+      // compiler wait for every earlier LDS operation before it.
+      atomicAdd(&h.fine[key >> 1], valid ? 1u << ((key & 1) << 4) : 0u);
       nat += valid && key < a.k_tau;
     }
   }
@@ -427,64 +433,82 @@ __device__ __forceinline__ void select_exact(KeyHist<NT>& h, Keys& k, uint32_t* 
   if (lane == 0) h.wave_nat[wave] = nat;
   __syncthreads();
   for (int c = tid; c < 1024; c += NT) {
+    // The low halves of the 16 words hold the even keys' counts, the high halves the odd
+    // keys'; each sum is at most d <= 32768 < 65536, so plain 32-bit adds never carry from
+    // one half into the other.
     const uint4* f4 = reinterpret_cast<const uint4*>(h.fine) + 4 * c;
     uint32_t t = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 v = f4[q];
-      t += (v.x & 0xFFFFu) + (v.x >> 16) + (v.y & 0xFFFFu) + (v.y >> 16) + (v.z & 0xFFFFu) +
-           (v.z >> 16) + (v.w & 0xFFFFu) + (v.w >> 16);
+      t += v.x + v.y + v.z + v.w;
     }
-    h.coarse[c] = (int)t;
+    h.coarse[c] = (int)((t & 0xFFFFu) + (t >> 16));
+  }
+  if (a.mode == SPAX_MODE_TOPK) {
+    R[0] = a.n_full;
+    R[1] = a.n_full + a.n_approx;
+  } else {
+    const int natural = wave_sum(lane < W ? h.wave_nat[lane] : 0);
+    const int n_skip = min(max(natural, a.n_lo), a.n_hi);
+    const int kept = d - n_skip;
+    // num <= den <= 65535 and kept <= 32768: fits 32 bits
+    const int n_approx = (int)(((uint32_t)a.num * (uint32_t)kept + (uint32_t)(a.den / 2)) /
+                               (uint32_t)a.den);
+    R[0] = kept - n_approx;
+    R[1] = kept;
   }
   __syncthreads();
+  return true;
+}
+
+// The coarse bin cb (keys [32 cb, 32 cb + 32)) that holds the R-th largest key, R >= 1, and
+// the number of keys above it.  One wave, after select_begin; the result is wave-uniform.
+template <int NT>
+__device__ __forceinline__ void coarse_find(const KeyHist<NT>& h, int R, int lane, int& cb,
+                                            int& above) {
+  int local[16];
+  const int4* c4 = reinterpret_cast<const int4*>(h.coarse) + 4 * lane;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int4 v = c4[q];
+    local[4 * q] = v.x;
+    local[4 * q + 1] = v.y;
+    local[4 * q + 2] = v.z;
+    local[4 * q + 3] = v.w;
+  }
+  cb = 0;
+  above = 0;
+  suffix_find<16>(local, R, 0, lane, &cb, &above);
+  cb = min(max(cb, 0), 1023);  // R <= d: always found
+}
+
+// Second part: waves 0 and 1 each find one boundary inside its coarse bin; every wave gets
+// both (sel) and, for each, the number of channels whose key equals it (E).  Ends with a
+// barrier.
+template <int NT>
+__device__ __forceinline__ void select_finish(KeyHist<NT>& h, const int (&R)[2],
+                                              Select (&sel)[2], int (&E)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave < 2) {  // wave b finds boundary b
     const int b = wave;
-    int R[2];
-    if (a.mode == SPAX_MODE_TOPK) {
-      R[0] = a.n_full;
-      R[1] = a.n_full + a.n_approx;
-    } else {
-      const int natural = wave_sum(lane < W ? h.wave_nat[lane] : 0);
-      const int n_skip = min(max(natural, a.n_lo), a.n_hi);
-      const int kept = d - n_skip;
-      // num <= den <= 65535 and kept <= 32768: fits 32 bits
-      const int n_approx = (int)(((uint32_t)a.num * (uint32_t)kept + (uint32_t)(a.den / 2)) /
-                                 (uint32_t)a.den);
-      R[0] = kept - n_approx;
-      R[1] = kept;
+    Select sb{0x8000, 0};
+    int eb = 0;
+    if (R[b] > 0) {
+      int cb, above;
+      coarse_find<NT>(h, R[b], lane, cb, above);
+      const uint32_t dw = h.fine[16 * cb + ((lane & 31) >> 1)];
+      const int cnt[1] = {lane < 32 ? (int)((dw >> ((lane & 1) << 4)) & 0xFFFFu) : 0};
+      int v = 0, ab = 0;
+      suffix_find<1>(cnt, R[b], above, lane, &v, &ab);
+      v = min(max(v, 0), 31);
+      sb = Select{32 * cb + v, R[b] - ab};
+      eb = __builtin_amdgcn_readlane(cnt[0], v);
     }
-    int local[16];
-    {
-      const int4* c4 = reinterpret_cast<const int4*>(h.coarse) + 4 * lane;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int4 v = c4[q];
-        local[4 * q] = v.x;
-        local[4 * q + 1] = v.y;
-        local[4 * q + 2] = v.z;
-        local[4 * q + 3] = v.w;
-      }
-    }
-    {
-      Select sb{0x8000, 0};
-      int eb = 0;
-      if (R[b] > 0) {
-        int cb = 0, above = 0;
-        suffix_find<16>(local, R[b], 0, lane, &cb, &above);
-        cb = min(max(cb, 0), 1023);  // R <= d: always found
-        const uint32_t dw = h.fine[16 * cb + ((lane & 31) >> 1)];
-        const int cnt[1] = {lane < 32 ? (int)((dw >> ((lane & 1) << 4)) & 0xFFFFu) : 0};
-        int v = 0, ab = 0;
-        suffix_find<1>(cnt, R[b], above, lane, &v, &ab);
-        v = min(max(v, 0), 31);
-        sb = Select{32 * cb + v, R[b] - ab};
-        eb = __builtin_amdgcn_readlane(cnt[0], v);
-      }
-      if (lane == 0) {
-        h.sel[b] = sb;
-        h.E[b] = eb;
-      }
+    if (lane == 0) {
+      h.sel[b] = sb;
+      h.E[b] = eb;
     }
   }
   __syncthreads();
