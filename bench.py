@@ -1,7 +1,7 @@
 """Benchmark of the tiered activation-sparse decoding GEMV on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode7b] [--sparsity 0.5]
-                    [--no-cpu-baseline] [--no-batched]
+                    [--no-cpu-baseline] [--no-batched] [--control none|full|skip]
 
 Default workload (decode7b): one step is one token of a 32-layer 7B-shaped decoder: for each
 layer and each projection group (q|k|v, o, gate|up, down) one TopK-Guided tier mask (s +-
@@ -27,6 +27,9 @@ per launch, over its average launch duration (the timed step's event time over i
 ``cpu_baseline`` times the oracle (float64 NumPy) on a bounded sample of the same workload on
 the host cores.  ``batched`` is the same step in the batched launch form (all masks in one
 launch, all GEMVs in one), legal here only because the synthetic inputs are independent.
+``token_us`` gives the median and 90th percentile over the timed tokens, each timed on its
+own after the timed region.  ``--control full|skip`` replaces the tier rule by all-FULL or
+all-SKIP masks: controls for the hardware byte counters.
 """
 
 from __future__ import annotations
@@ -76,6 +79,9 @@ def parse():
                          "byte counters (use more than the 256 MB last-level cache)")
     ap.add_argument("--cpu-layers", type=int, default=None,
                     help="layers the oracle runs for the CPU baseline")
+    ap.add_argument("--control", default="none", choices=["none", "full", "skip"],
+                    help="decode workloads: replace the tier rule by all-FULL (reads the dense "
+                         "bytes) or all-SKIP (reads almost nothing), as byte-counter controls")
     ap.add_argument("--gap", type=int, default=0, help="host8b: range merging gap (columns)")
     ap.add_argument("--transfer", default="gather", choices=["memcpy", "gather"],
                     help="host8b: one hipMemcpyAsync per range, or one copy kernel")
@@ -105,6 +111,12 @@ def workload_spec(args):
                          "MLP pass per token")
     else:
         raise ValueError(args.workload)
+    if args.control != "none":
+        if args.workload == "mlp7b":
+            raise ValueError("--control applies to the decode workloads")
+        spec["tiers"] = ("topk", 1.0, 0.0) if args.control == "full" else ("topk", 0.0, 0.0)
+        spec["desc"] += f"; CONTROL: all channels {args.control.upper()} (TopK " + \
+            ("d/0/0)" if args.control == "full" else "0/0/d)")
     if args.layers is not None:
         spec["layers"] = args.layers
         if args.workload == "mlp7b":
@@ -225,8 +237,8 @@ def recorded_traffic(args):
     """HBM MB per fused launch from the committed FETCH_SIZE / WRITE_SIZE summary, scaled by
     its copy calibration; None unless this is the workload it was taken on and the kernel
     sources are unchanged since."""
-    if (args.workload, args.sparsity, args.delta, args.layers) != ("decode7b", 0.5, 0.01, None) \
-            or not os.path.exists(TRAFFIC_FILE):
+    if (args.workload, args.sparsity, args.delta, args.layers, args.control) != \
+            ("decode7b", 0.5, 0.01, None, "none") or not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
     with open(TRAFFIC_FILE) as fh:
@@ -343,6 +355,19 @@ def device_bench(args, spax, torch, dev):
     log(f"[bench] fused kernel: {avg_launch_ms * 1e3:.2f} us/launch, {avg_bytes / 1e6:.2f} MB/launch, "
         f"{achieved:.1f} GB/s; selected bytes/step {bytes_per_step / 1e9:.3f} GB")
 
+    # ---- per-token spread: the same steps again, each between its own pair of events
+    # (outside the timed region above)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for t in range(args.steps):
+        stack.step(args.warmup + t)
+        ev[t + 1].record()
+    torch.cuda.synchronize()
+    tok_us = np.array([ev[t].elapsed_time(ev[t + 1]) * 1e3 / per_tok for t in range(args.steps)])
+    token_us = {"median": round(float(np.median(tok_us)), 2),
+                "p90": round(float(np.percentile(tok_us, 90)), 2), "n": int(args.steps)}
+    log(f"[bench] per token: median {token_us['median']} us, p90 {token_us['p90']} us")
+
     # ---- the batched form of the same step (all masks in one launch, all GEMVs in one launch):
     # legal here only because the synthetic phase inputs are independent; reported beside the
     # layer-serial value, never as it
@@ -398,6 +423,7 @@ def device_bench(args, spax, torch, dev):
                      "avg_algorithmic_MB": round(avg_bytes / 1e6, 3)},
         "cpu_baseline": cpu,
         "batched": batched,
+        "token_us": token_us,
     }
 
 

@@ -1,0 +1,70 @@
+"""Host-side logic of bench.py (no GPU): argument handling, workload specs, the byte-counter
+controls and the rule that a recorded traffic figure is only reported for its own workload."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def args_for(*argv):
+    old = sys.argv
+    sys.argv = ["bench.py", *argv]
+    try:
+        return bench.parse()
+    finally:
+        sys.argv = old
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    assert out["n_gpus"] == 2 and "one GPU" in out["error"]
+
+
+@pytest.mark.parametrize("workload,fmt,layers", [("decode7b", 0, 32), ("decode7b-int4", 1, 32),
+                                                 ("mlp7b", 0, 5)])
+def test_workload_specs(workload, fmt, layers):
+    spec = bench.workload_spec(args_for("--workload", workload))
+    assert spec["fmt"] == fmt and spec["layers"] == layers
+    assert spec["cpu_layers"] <= spec["layers"]
+    assert workload in spec["desc"]
+
+
+def test_default_is_the_guided_decode_at_half_sparsity():
+    a = args_for()
+    spec = bench.workload_spec(a)
+    assert a.workload == "decode7b" and spec["tiers"] == ("guided", 0.5, 0.01)
+    assert spec["tokens_per_step"] == 1
+
+
+@pytest.mark.parametrize("control,tiers", [("full", ("topk", 1.0, 0.0)),
+                                           ("skip", ("topk", 0.0, 0.0))])
+def test_controls_replace_the_tier_rule(control, tiers):
+    spec = bench.workload_spec(args_for("--control", control))
+    assert spec["tiers"] == tiers and "CONTROL" in spec["desc"]
+
+
+def test_control_rejected_for_the_mlp_workload():
+    with pytest.raises(ValueError):
+        bench.workload_spec(args_for("--workload", "mlp7b", "--control", "full"))
+
+
+def test_recorded_traffic_only_for_its_own_workload():
+    assert bench.recorded_traffic(args_for("--sparsity", "0.3")) is None
+    assert bench.recorded_traffic(args_for("--control", "full")) is None
+    assert bench.recorded_traffic(args_for("--workload", "decode7b-int4")) is None
+    assert bench.recorded_traffic(args_for("--layers", "4")) is None
+
+
+def test_sources_hash_is_stable():
+    assert bench.sources_sha256() == bench.sources_sha256()
+    assert len(bench.sources_sha256()) == 64
