@@ -76,7 +76,11 @@ __device__ __forceinline__ int phase_of(const GemvDesc* __restrict__ gd, int n, 
 __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDesc* __restrict__ gd,
                                                                     int n_phases, int n_items) {
   __shared__ float red[gemv::kWaves][kTileRows];
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // Item i runs on XCD i % 8 (the grid is a multiple of 8 or holds one item per
+  // workgroup), so the XCD-aware order applies to the item index.  Only the speed depends on
+  // this: the order is a bijection whatever the grid.
+  for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+    const int item = gemv::xcd_order(i, n_items);
     const int p = phase_of(gd, n_phases, item);
     const GemvDesc& g = gd[p];
     const int local = item - g.item0;

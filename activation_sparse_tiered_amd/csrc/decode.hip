@@ -139,8 +139,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     return;
   }
 
-  const int tile = (int)(blockIdx.x % (uint32_t)sh.n_tiles);
-  const int chunk = (int)(blockIdx.x / (uint32_t)sh.n_tiles);
+  const int item = gemv::xcd_order((int)blockIdx.x, (int)gridDim.x - 1);
+  const int tile = (int)((uint32_t)item % (uint32_t)sh.n_tiles);
+  const int chunk = (int)((uint32_t)item / (uint32_t)sh.n_tiles);
   const int c0 = gemv::split_at(d, chunk, sh.n_chunks);
   const int c1 = gemv::split_at(d, chunk + 1, sh.n_chunks);
   const int S = a.wave_cap;  // channels per wave

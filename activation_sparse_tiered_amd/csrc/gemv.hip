@@ -27,8 +27,9 @@ __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
     const int32_t* __restrict__ full_idx, const int32_t* __restrict__ approx_idx,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
   __shared__ float red[kWaves][kTileRows];
-  const int tile = (int)(blockIdx.x % (uint32_t)sh.n_tiles);
-  const int chunk = (int)(blockIdx.x / (uint32_t)sh.n_tiles);
+  const int item = gemv::xcd_order((int)blockIdx.x, (int)gridDim.x);
+  const int tile = (int)((uint32_t)item % (uint32_t)sh.n_tiles);
+  const int chunk = (int)((uint32_t)item / (uint32_t)sh.n_tiles);
   gemv::gemv_item<FMT, kCompact>(sh, packed, x32, full_idx, approx_idx, counts, y, tile, chunk,
                                  red);
 }

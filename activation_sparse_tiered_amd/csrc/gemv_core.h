@@ -327,6 +327,17 @@ __device__ __forceinline__ int split_at(int n, int c, int parts) {
   return (int)((uint32_t)n * (uint32_t)c / (uint32_t)parts);
 }
 
+// Work-item order for the chip's 8 XCDs.  Workgroups are dispatched to the XCDs round-robin
+// (workgroup b runs on XCD b % 8), and each XCD has its own L2.  Item b is mapped to
+// (b % 8) * (n / 8) + b / 8, so each XCD takes one contiguous run of items: whole column
+// chunks with all their row tiles, and the lines that the tiles of one column share (its
+// (s, z) words) are fetched into one L2 instead of several.  A bijection on [0, n); items past
+// the last multiple of 8 keep their index.
+__device__ __forceinline__ int xcd_order(int b, int n) {
+  const int n8 = n >> 3;
+  return b < (n8 << 3) ? (b & 7) * n8 + (b >> 3) : b;
+}
+
 // Split [b, e) evenly over the workgroup's NW waves.
 template <int NW>
 __device__ __forceinline__ void wave_range(int b, int e, int wave, int& wb, int& we) {
