@@ -14,6 +14,8 @@ in HBM before the timed region.
 Other workloads (one JSON line each, never printed by the default run):
   decode7b-int4 : the same stack with int4 base columns (g128) and two-bit approximations,
                   TopK 25% FULL / 35% APPROX / 40% skipped.
+  linear512     : one 512x512 layer (TopK 20% / 30% / 50%, two-bit groups of 64 rows): the
+                  latency of one mask + GEMV call on a blob that stays in the cache.
   mlp7b         : gate|up 4096->2x11008 and down 11008->4096, per-channel LogNormal(0, 0.5)
                   scaled Laplace activations, TopK 30% / 30% / 40%; five weight copies cycled
                   (one MLP pass per token) so the 256 MB last-level cache does not hold them.
@@ -65,7 +67,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="decode7b",
-                    choices=["decode7b", "decode7b-int4", "mlp7b", "host8b"])
+                    choices=["decode7b", "decode7b-int4", "mlp7b", "linear512", "host8b"])
     ap.add_argument("--sparsity", type=float, default=0.5, help="decode7b TopK-Guided target s")
     ap.add_argument("--delta", type=float, default=0.01)
     ap.add_argument("--layers", type=int, default=None, help="override the workload's layers")
@@ -109,10 +111,16 @@ def workload_spec(args):
                     desc="mlp7b: gate|up 4096->2x11008 + down 11008->4096, fp16, TopK 30/30/40, "
                          "LogNormal(0,0.5)-scaled Laplace x, 2-bit G=128; 5 weight copies, one "
                          "MLP pass per token")
+    elif args.workload == "linear512":
+        spec = dict(shapes=[("linear", 512, [512])], fmt=0, G=64, tiers=("topk", 0.2, 0.3),
+                    channel_scaled=False, layers=1, tokens_per_step=1, cpu_layers=1,
+                    desc="linear512: one 512x512 fp16 layer, TopK 20/30/50, 2-bit G=64, batch "
+                         "1; the blob (0.6 MB) stays in the last-level cache, so this is a "
+                         "latency figure per call, not a bandwidth one")
     else:
         raise ValueError(args.workload)
     if args.control != "none":
-        if args.workload == "mlp7b":
+        if args.workload in ("mlp7b", "linear512"):
             raise ValueError("--control applies to the decode workloads")
         spec["tiers"] = ("topk", 1.0, 0.0) if args.control == "full" else ("topk", 0.0, 0.0)
         spec["desc"] += f"; CONTROL: all channels {args.control.upper()} (TopK " + \

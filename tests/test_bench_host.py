@@ -31,7 +31,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 
 @pytest.mark.parametrize("workload,fmt,layers", [("decode7b", 0, 32), ("decode7b-int4", 1, 32),
-                                                 ("mlp7b", 0, 5)])
+                                                 ("mlp7b", 0, 5), ("linear512", 0, 1)])
 def test_workload_specs(workload, fmt, layers):
     spec = bench.workload_spec(args_for("--workload", workload))
     assert spec["fmt"] == fmt and spec["layers"] == layers

@@ -168,6 +168,31 @@ def test_byte_ledger_and_ranges():
     assert ranges.compact_positions([(3, 2), (9, 1)]) == [(3, 0), (4, 1), (9, 2)]
 
 
+@pytest.mark.parametrize("gap", [0, 1, 3, 7])
+def test_ranges_characterised_by_their_gaps(gap):
+    """Gap merging pinned by what it must produce, not by how: the ranges are disjoint and
+    ascending, cover every selected channel and start and end on one, no range holds a run of
+    unselected channels longer than the gap, and the channels between two ranges are a run of
+    more than gap unselected channels."""
+    rng = np.random.default_rng(100 + gap)
+    for _ in range(200):
+        d = int(rng.integers(1, 60))
+        sel = sorted(rng.choice(d, size=int(rng.integers(0, d + 1)), replace=False).tolist())
+        rs = ranges.runs(sel, gap)
+        chosen = set(sel)
+        covered = [j for first, c in rs for j in range(first, first + c)]
+        assert covered == sorted(set(covered))                      # disjoint, ascending
+        assert chosen <= set(covered)
+        for first, c in rs:
+            assert first in chosen and first + c - 1 in chosen
+            run = 0
+            for j in range(first, first + c):
+                run = 0 if j in chosen else run + 1
+                assert run <= gap
+        for (f0, c0), (f1, _) in zip(rs, rs[1:]):
+            assert f1 - (f0 + c0) > gap
+
+
 def test_decode_step_matches_per_phase_calls():
     rng = np.random.default_rng(11)
     phases = []
