@@ -373,9 +373,10 @@ struct KeyHist {
 
 // Exact boundaries from a per-key histogram, in two parts (a caller may do other work in
 // between).  select_begin loads x into LDS (xs32: roundup(d, 2) halves), sets k like
-// build_plan, builds the per-key histogram and its coarse sums, and gives every wave the two
-// target ranks R (FULL, kept; counted from the largest key).  For THRESHOLD the boundaries
-// are the given keys: sel and E are set and false is returned.  Ends with a barrier.
+// build_plan, builds the per-key histogram and the coarse one (32 keys per bin), and gives
+// every wave the two target ranks R (FULL, kept; counted from the largest key).  For
+// THRESHOLD the boundaries are the given keys: sel and E are set and false is returned.
+// Both histograms are complete on return (its last barrier follows the last atomic).
 template <int NT, int MAXD>
 __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* xs32,
                                              const uint16_t* __restrict__ x, const TierArgs& a,
@@ -402,6 +403,8 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
       const uint4 z = make_uint4(0u, 0u, 0u, 0u);
       uint4* f4 = reinterpret_cast<uint4*>(h.fine);
       for (int i = tid; i < 16384 / 4; i += NT) f4[i] = z;
+      uint4* c4 = reinterpret_cast<uint4*>(h.coarse);
+      for (int i = tid; i < 1024 / 4; i += NT) c4[i] = z;
     }
 #pragma unroll
     for (int q = 0; q < PER; ++q)
@@ -424,27 +427,17 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
       const bool valid = k.valid(s, lane, e);
       const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
       // Unconditional (a zero increment past the range): a conditional LDS atomic makes the
-      // compiler wait for every earlier LDS operation before it.
+      // compiler wait for every earlier LDS operation before it.  The coarse count is kept
+      // by a second atomic rather than summed from the fine counters afterwards, which would
+      // cost one more pass and one more barrier before the boundary search can start.
       atomicAdd(&h.fine[key >> 1], valid ? 1u << ((key & 1) << 4) : 0u);
+      atomicAdd(&h.coarse[key >> 5], valid ? 1 : 0);
       nat += valid && key < a.k_tau;
     }
   }
   nat = wave_sum(nat);
   if (lane == 0) h.wave_nat[wave] = nat;
   __syncthreads();
-  for (int c = tid; c < 1024; c += NT) {
-    // The low halves of the 16 words hold the even keys' counts, the high halves the odd
-    // keys'; each sum is at most d <= 32768 < 65536, so plain 32-bit adds never carry from
-    // one half into the other.
-    const uint4* f4 = reinterpret_cast<const uint4*>(h.fine) + 4 * c;
-    uint32_t t = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = f4[q];
-      t += v.x + v.y + v.z + v.w;
-    }
-    h.coarse[c] = (int)((t & 0xFFFFu) + (t >> 16));
-  }
   if (a.mode == SPAX_MODE_TOPK) {
     R[0] = a.n_full;
     R[1] = a.n_full + a.n_approx;
@@ -458,7 +451,6 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
     R[0] = kept - n_approx;
     R[1] = kept;
   }
-  __syncthreads();
   return true;
 }
 
