@@ -67,10 +67,35 @@ __device__ __forceinline__ int phase_of(const GemvDesc* __restrict__ gd, int n, 
   int lo = 0, hi = n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (gd[mid].item0 <= item) lo = mid;
+    if (gemv::uniform(gd[mid].item0) <= item) lo = mid;
     else hi = mid - 1;
   }
   return lo;
+}
+
+// The descriptor in scalar registers (see gemv::uniform): loop bounds and addresses derived
+// from it are then uniform, and the loop's branches are scalar branches.
+__device__ __forceinline__ GemvDesc uniform_desc(const GemvDesc& g) {
+  using gemv::uniform;
+  GemvDesc u;
+  u.sh.stride_F = uniform(g.sh.stride_F);
+  u.sh.stride_A = uniform(g.sh.stride_A);
+  u.sh.off_A = uniform(g.sh.off_A);
+  u.sh.T = uniform(g.sh.T);
+  u.sh.n_tiles = uniform(g.sh.n_tiles);
+  u.sh.n_chunks = uniform(g.sh.n_chunks);
+  u.sh.approx_group = uniform(g.sh.approx_group);
+  u.sh.base_group = uniform(g.sh.base_group);
+  u.sh.d_in = uniform(g.sh.d_in);
+  u.packed = uniform(g.packed);
+  u.x32 = uniform(g.x32);
+  u.full_idx = uniform(g.full_idx);
+  u.approx_idx = uniform(g.approx_idx);
+  u.counts = uniform(g.counts);
+  u.y = uniform(g.y);
+  u.item0 = uniform(g.item0);
+  u.fmt = uniform(g.fmt);
+  return u;
 }
 
 __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDesc* __restrict__ gd,
@@ -82,7 +107,7 @@ __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDe
   for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
     const int item = gemv::xcd_order(i, n_items);
     const int p = phase_of(gd, n_phases, item);
-    const GemvDesc& g = gd[p];
+    const GemvDesc g = uniform_desc(gd[p]);
     const int local = item - g.item0;
     const int tile = (int)((uint32_t)local % (uint32_t)g.sh.n_tiles);
     const int chunk = (int)((uint32_t)local / (uint32_t)g.sh.n_tiles);

@@ -114,25 +114,49 @@ __device__ __forceinline__ void fma_int2x8(float (&acc)[8], float a, uint32_t w,
   acc[7] = fmaf(a, half_hi(h3), acc[7]);
 }
 
+// Every pointer here points to device (global) memory.  Loads through a pointer that reaches
+// the kernel inside a descriptor in memory are compiled as flat loads unless the address
+// space is stated; flat loads also count as LDS operations for the wait counters.
+template <class T>
+using global_ptr = const __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ T load_global(const void* p) {
+  return *(global_ptr<T>)p;  // a C-style cast: reinterpret_cast cannot change address space
+}
+
+// A wave-uniform value moved to a scalar register, so that the compiler treats what depends
+// on it (loop bounds, branches, addresses) as uniform: values loaded from memory after the
+// kernel has stored to memory are otherwise kept per lane.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ T* uniform(T* p) {
+  return reinterpret_cast<T*>(uniform((int64_t)reinterpret_cast<uintptr_t>(p)));
+}
+
 // Weight codes are read once per token: optionally as non-temporal loads.
 #ifndef SPAX_NT_LOADS
 #define SPAX_NT_LOADS 1
 #endif
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) {
 #if SPAX_NT_LOADS
-  return __builtin_nontemporal_load(p);
+  return __builtin_nontemporal_load((global_ptr<uint32_t>)p);
 #else
-  return *p;
+  return load_global<uint32_t>(p);
 #endif
 }
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
-#if SPAX_NT_LOADS
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+#if SPAX_NT_LOADS
+  const u32x4 v = __builtin_nontemporal_load((global_ptr<u32x4>)p);
 #else
-  return *p;
+  const u32x4 v = load_global<u32x4>(p);
 #endif
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // A block of up to 64 entries of a column list held in registers, one per lane: entry =
@@ -156,8 +180,8 @@ __device__ __forceinline__ RegBlock load_block(const int32_t* __restrict__ idx,
   const int lane = threadIdx.x & 63;
   const int i = base + lane;
   uint32_t j = 0;
-  if (i < end) j = min((uint32_t)idx[i], jmax);
-  const uint32_t xb = i < end ? (uint32_t)x16[j] : 0u;
+  if (i < end) j = min((uint32_t)load_global<int32_t>(idx + i), jmax);
+  const uint32_t xb = i < end ? (uint32_t)load_global<uint16_t>(x16 + j) : 0u;
   return RegBlock{j | (xb << 16), base};
 }
 
@@ -169,9 +193,9 @@ __device__ __forceinline__ RegBlock load_block_compact(const uint32_t* __restric
   const int lane = threadIdx.x & 63;
   const int i = base + lane;
   uint32_t v = 0;
-  if (i < end) v = ent[i];
+  if (i < end) v = load_global<uint32_t>(ent + i);
   const uint32_t slot = min(v & 0xFFFFu, jmax), j = min(v >> 16, jmax);
-  const uint32_t xb = i < end ? (uint32_t)x16[j] : 0u;
+  const uint32_t xb = i < end ? (uint32_t)load_global<uint16_t>(x16 + j) : 0u;
   return RegBlock{slot | (xb << 16), base};
 }
 
@@ -213,7 +237,7 @@ struct EarlyColumns {
         v[u] = load_stream(reinterpret_cast<const uint4*>(col + loffF));
       } else {
         c[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffF));
-        sz[u] = *reinterpret_cast<const uint32_t*>(col + szoffF);
+        sz[u] = load_global<uint32_t>(col + szoffF);
       }
     }
   }
@@ -276,7 +300,7 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
           vf[u] = load_stream(reinterpret_cast<const uint4*>(col + loffF));
         } else {
           cf[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffF));
-          sf[u] = *reinterpret_cast<const uint32_t*>(col + szoffF);
+          sf[u] = load_global<uint32_t>(col + szoffF);
         }
       }
     }
@@ -287,7 +311,7 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
         srcA.get(ai + u, j, xa[u]);
         const uint8_t* col = regionA + (int64_t)j * sh.stride_A;
         ca[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffA4));
-        sa[u] = *reinterpret_cast<const uint32_t*>(col + szoffA);
+        sa[u] = load_global<uint32_t>(col + szoffA);
       }
     }
     // A tier with no column in this round skips its multiplies (a wave-uniform branch around
@@ -388,8 +412,8 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
   // Lanes past the last row (ragged last tile) read the record's first rows instead, which
   // is always in bounds; their sums land in rows >= T and are never stored.
   const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
-  const int nF = min(max(counts[0], 0), sh.d_in);
-  const int nA = min(max(counts[1], 0), sh.d_in);
+  const int nF = uniform(min(max(load_global<int32_t>(counts), 0), sh.d_in));
+  const int nA = uniform(min(max(load_global<int32_t>(counts + 1), 0), sh.d_in));
   const uint32_t jmax = (uint32_t)sh.d_in - 1u;
   const int fb = split_at(nF, chunk, sh.n_chunks);
   const int fe = split_at(nF, chunk + 1, sh.n_chunks);
