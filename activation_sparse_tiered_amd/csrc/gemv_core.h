@@ -161,9 +161,10 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 
 // A block of up to 64 entries of a column list held in registers, one per lane: entry =
 // channel | (fp16 bits of x_j) << 16, for list positions [base, base + 64).  Loaded with one
-// vector load of the indices and one gather of the activations (two dependent round trips per
-// 64 columns instead of two per column); get() broadcasts one entry with readlane.  Indices
-// are clamped to [0, d_in), so malformed lists cannot address outside the blob.
+// vector load of the indices and one gather of the activations (load_blocks: two dependent
+// round trips per 64 columns instead of two per column); get() broadcasts one entry with
+// readlane.  Indices are clamped to [0, d_in), so malformed lists cannot address outside the
+// blob.
 struct RegBlock {
   uint32_t e;
   int base;
@@ -174,29 +175,31 @@ struct RegBlock {
   }
 };
 
-__device__ __forceinline__ RegBlock load_block(const int32_t* __restrict__ idx,
-                                               const uint16_t* __restrict__ x16, int base,
-                                               int end, uint32_t jmax) {
+// The FULL and the APPROX block of one step of 64 list positions, [fi, fend) and [ai, aend),
+// with their loads overlapped: both index loads, then both activation gathers (two dependent
+// round trips for the pair instead of four).  The loads are unconditional: a lane past its
+// tier's end reads the tier's last entry (or entry 0 of an empty list, whose buffer still
+// holds d_in entries) and keeps a zero entry.  kCompact: the lists hold staging slot |
+// channel << 16 (pinned-host path) and the returned entry holds the slot and x of the
+// channel.
+template <bool kCompact>
+__device__ __forceinline__ void load_blocks(const void* __restrict__ idxF,
+                                            const void* __restrict__ idxA,
+                                            const uint16_t* __restrict__ x16, int fi, int fend,
+                                            int ai, int aend, uint32_t jmax, RegBlock& bf,
+                                            RegBlock& ba) {
   const int lane = threadIdx.x & 63;
-  const int i = base + lane;
-  uint32_t j = 0;
-  if (i < end) j = min((uint32_t)load_global<int32_t>(idx + i), jmax);
-  const uint32_t xb = i < end ? (uint32_t)load_global<uint16_t>(x16 + j) : 0u;
-  return RegBlock{j | (xb << 16), base};
-}
-
-// The same for a compacted list (pinned-host path): entry = staging slot | channel << 16; the
-// returned entry holds the slot (the record to read) and x of the channel.
-__device__ __forceinline__ RegBlock load_block_compact(const uint32_t* __restrict__ ent,
-                                                       const uint16_t* __restrict__ x16,
-                                                       int base, int end, uint32_t jmax) {
-  const int lane = threadIdx.x & 63;
-  const int i = base + lane;
-  uint32_t v = 0;
-  if (i < end) v = load_global<uint32_t>(ent + i);
-  const uint32_t slot = min(v & 0xFFFFu, jmax), j = min(v >> 16, jmax);
-  const uint32_t xb = i < end ? (uint32_t)load_global<uint16_t>(x16 + j) : 0u;
-  return RegBlock{slot | (xb << 16), base};
+  const int iF = fi + lane, iA = ai + lane;
+  const uint32_t rF =
+      load_global<uint32_t>(reinterpret_cast<const uint32_t*>(idxF) + min(iF, max(fend - 1, 0)));
+  const uint32_t rA =
+      load_global<uint32_t>(reinterpret_cast<const uint32_t*>(idxA) + min(iA, max(aend - 1, 0)));
+  const uint32_t jF = min(kCompact ? rF >> 16 : rF, jmax), jA = min(kCompact ? rA >> 16 : rA, jmax);
+  const uint32_t sF = kCompact ? min(rF & 0xFFFFu, jmax) : jF;
+  const uint32_t sA = kCompact ? min(rA & 0xFFFFu, jmax) : jA;
+  const uint32_t xF = load_global<uint16_t>(x16 + jF), xA = load_global<uint16_t>(x16 + jA);
+  bf = RegBlock{iF < fend ? sF | (xF << 16) : 0u, fi};
+  ba = RegBlock{iA < aend ? sA | (xA << 16) : 0u, ai};
 }
 
 // Column lists in LDS (fused kernel): entry = channel | (fp16 bits of x_j) << 16, indexed
@@ -431,13 +434,7 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
   for (int fi = wfb, ai = wab; fi < wfe || ai < wae; fi += 64, ai += 64) {
     const int fend = min(fi + 64, wfe), aend = min(ai + 64, wae);
     RegBlock bf, ba;
-    if (kCompact) {
-      bf = load_block_compact(reinterpret_cast<const uint32_t*>(full_idx), x16, fi, fend, jmax);
-      ba = load_block_compact(reinterpret_cast<const uint32_t*>(approx_idx), x16, ai, aend, jmax);
-    } else {
-      bf = load_block(full_idx, x16, fi, fend, jmax);
-      ba = load_block(approx_idx, x16, ai, aend, jmax);
-    }
+    load_blocks<kCompact>(full_idx, approx_idx, x16, fi, fend, ai, aend, jmax, bf, ba);
     stream_columns<FMT>(sh, packed, row, fi, max(fi, fend), bf, ai, max(ai, aend), ba, acc, zsum);
   }
   finish_tile<kWaves>(red, acc, zsum, wave, lane, row0, T, sh.n_chunks, y);
