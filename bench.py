@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--gap", type=int, default=0, help="host8b: range merging gap (columns)")
     ap.add_argument("--transfer", default="gather", choices=["memcpy", "gather"],
                     help="host8b: one hipMemcpyAsync per range, or one copy kernel")
+    ap.add_argument("--placement", default="channel", choices=["channel", "frequency"],
+                    help="host8b: records in channel order, or ordered by calibrated "
+                         "selection frequency (jointly selected columns placed together)")
     return ap.parse_args()
 
 
@@ -435,6 +438,25 @@ def device_bench(args, spax, torch, dev):
     }
 
 
+def calibrated_order(spax, torch, dev, L, params, d_in, layer, group, tokens=16):
+    """Channel order for the packed records: descending selected bytes per channel over
+    `tokens` calibration activations (FULL counts stride_F bytes, APPROX stride_A), ties by
+    channel index.  Returns a device index tensor: position p holds channel order[p]."""
+    score = np.zeros(d_in, dtype=np.int64)
+    tier = torch.empty(d_in, dtype=torch.uint8, device=dev)
+    f = torch.empty(d_in, dtype=torch.int32, device=dev)
+    a = torch.empty(d_in, dtype=torch.int32, device=dev)
+    c = torch.zeros(3, dtype=torch.int32, device=dev)
+    for t in range(tokens):
+        xc = torch.from_numpy(synth.activations(SEED, d_in, 1000 + t, 100 + layer, group,
+                                                channel_scaled=True)).to(dev)
+        spax.spax_build_tiers(xc, d_in, params, tier, f, a, c)
+        tv = tier.cpu().numpy()
+        score += np.where(tv == 2, int(L.stride_F), np.where(tv == 1, int(L.stride_A), 0))
+    order = np.lexsort((np.arange(d_in), -score))
+    return torch.from_numpy(order).to(dev)
+
+
 def host_bench(args, spax, torch, dev):
     """Llama-3-8B shapes, blobs in pinned host memory: per phase a device mask, then
     spax_tiered_gemv_pinned (ranges over PCIe).  Compared with the measured single-copy pinned
@@ -448,15 +470,25 @@ def host_bench(args, spax, torch, dev):
             L = spax.spax_layout_init(d_in, d_out, 0, 128, 128)
             dblob = torch.empty(int(L.total_bytes), dtype=torch.uint8, device=dev)
             Ws = [synth.weights_device(SEED, d_in, r, dev, 100 + l, k, m) for m, r in enumerate(d_out)]
+            nf, na = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
+            params = spax.topk_params(nf, na)
+            x = torch.from_numpy(synth.activations(SEED, d_in, 0, 100 + l, k,
+                                                   channel_scaled=True)).to(dev)
+            if args.placement == "frequency":
+                # Offline placement: records in descending order of how many bytes each
+                # channel made selected over calibration tokens (distinct from the timed
+                # ones).  Permuting the weight columns and the activations alike leaves y
+                # unchanged; a model does it once by permuting the rows of the layer that
+                # produces x.
+                perm = calibrated_order(spax, torch, dev, L, params, d_in, l, k)
+                Ws = [w[perm] for w in Ws]
+                x = x[perm].contiguous()
             spax.spax_pack_columns(L, Ws, dblob)
             del Ws
             host = torch.empty(int(L.total_bytes), dtype=torch.uint8, pin_memory=True)
             host.copy_(dblob)
             del dblob
-            nf, na = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
-            x = torch.from_numpy(synth.activations(SEED, d_in, 0, 100 + l, k,
-                                                   channel_scaled=True)).to(dev)
-            phases.append(dict(L=L, host=host, x=x, p=spax.topk_params(nf, na), d=d_in,
+            phases.append(dict(L=L, host=host, x=x, p=params, d=d_in,
                                f=torch.empty(d_in, dtype=torch.int32, device=dev),
                                a=torch.empty(d_in, dtype=torch.int32, device=dev),
                                c=torch.zeros(3, dtype=torch.int32, device=dev),
@@ -516,7 +548,8 @@ def host_bench(args, spax, torch, dev):
         "data": "synthetic",
         "config": {"workload": f"host8b: Llama-3-8B shapes (q|k|v 4096->4096+1024+1024, o, "
                                f"gate|up 4096->2x14336, down 14336->4096), fp16 blobs in pinned "
-                               f"host memory, TopK 20/30/50, range gap {args.gap}, transfer {args.transfer}; {n_layers} "
+                               f"host memory, TopK 20/30/50, range gap {args.gap}, transfer {args.transfer}, "
+                               f"placement {args.placement}; {n_layers} "
                                f"distinct layers timed (wall clock), scaled x{scale:g} to 32",
                    "selected_GB_per_token": round(r["sel"] * scale / 1e9, 4),
                    "moved_GB_per_token": round(r["moved"] * scale / 1e9, 4),

@@ -41,6 +41,7 @@ def test_workload_specs(workload, fmt, layers):
 
 def test_default_is_the_guided_decode_at_half_sparsity():
     a = args_for()
+    assert a.placement == "channel" and a.transfer == "gather" and a.gap == 0
     spec = bench.workload_spec(a)
     assert a.workload == "decode7b" and spec["tiers"] == ("guided", 0.5, 0.01)
     assert spec["tokens_per_step"] == 1
