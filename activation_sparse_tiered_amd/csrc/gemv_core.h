@@ -90,6 +90,17 @@ __device__ __forceinline__ void fma_int4x8(float (&acc)[8], float a, uint32_t c)
   acc[7] = fmaf(a, half_hi(h3), acc[7]);
 }
 
+// A column's group terms for codes read as h = 1 + q / 2^B: returns the multiplier
+// a = 2^B x s and adds x z - a to zsum, with s and z the fp16 halves of the group's (s, z)
+// word read by v_fma_mix_f32 (no separate conversions).  The zero addend keeps the first
+// product a fused multiply-add, which can read an fp16 operand.
+template <int B>
+__device__ __forceinline__ float group_terms(float x, uint32_t sz, float& zsum) {
+  const float a = fmaf(x * (float)(1 << B), half_lo(sz), 0.0f);
+  zsum = fmaf(x, half_hi(sz), zsum) - a;
+  return a;
+}
+
 // Byte selector that moves bytes k0 and k0 + 1 of a dword to bytes 1 and 3 (zeros elsewhere).
 __device__ __forceinline__ uint32_t spread_sel(uint32_t k0) {
   return 0x000C000Cu | (k0 << 8) | ((k0 + 1u) << 24);
@@ -250,9 +261,7 @@ struct EarlyColumns {
       if (FMT == SPAX_FMT_FP16) {
         fma_fp16x8(acc, xv[u], v[u]);
       } else {
-        const float sc = half_lo(sz[u]);
-        fma_int4x8(acc, xv[u] * (16.0f * sc), c[u]);
-        zsum = fmaf(xv[u], fmaf(-16.0f, sc, half_hi(sz[u])), zsum);
+        fma_int4x8(acc, group_terms<4>(xv[u], sz[u], zsum), c[u]);
       }
     }
   }
@@ -328,18 +337,14 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
         if (FMT == SPAX_FMT_FP16) {
           fma_fp16x8(acc, xf[u], vf[u]);
         } else {
-          const float sc = half_lo(sf[u]);
-          fma_int4x8(acc, xf[u] * (16.0f * sc), cf[u]);
-          zsum = fmaf(xf[u], fmaf(-16.0f, sc, half_hi(sf[u])), zsum);
+          fma_int4x8(acc, group_terms<4>(xf[u], sf[u], zsum), cf[u]);
         }
       }
     }
     if (na > 0) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const float sc = half_lo(sa[u]);
-        fma_int2x8(acc, xa[u] * (4.0f * sc), ca[u], selA);
-        zsum = fmaf(xa[u], fmaf(-4.0f, sc, half_hi(sa[u])), zsum);
+        fma_int2x8(acc, group_terms<2>(xa[u], sa[u], zsum), ca[u], selA);
       }
     }
     fi += max(nf, 0);
