@@ -164,12 +164,16 @@ def make_phase(layout: Layout, packed, x, params: TierParams, tier, full_idx, ap
     ph.params = params
     ph.tier, ph.full_idx, ph.approx_idx = _ptr(tier), _ptr(full_idx), _ptr(approx_idx)
     ph.counts, ph.y = _ptr(counts), _ptr(y)
-    ph._keep = (layout,)  # keep the layout alive as long as the phase
+    # The struct holds raw addresses: keep the layout and every buffer alive with it, so that
+    # a caller dropping its own reference cannot free (and the allocator reuse) a buffer the
+    # phase still points to.
+    ph._keep = (layout, packed, x, tier, full_idx, approx_idx, counts, y)
     return ph
 
 
 def phase_array(phases):
     arr = (Phase * len(phases))(*phases)
+    arr._keep = [getattr(p, "_keep", None) for p in phases]  # the elements are copies
     return arr
 
 

@@ -268,3 +268,26 @@ def test_pinned_gemv_validation():
         with pytest.raises(spax.SpaxError) as e:
             call(**kw)
         assert e.value.status == status, kw
+
+
+def test_phase_array_keeps_its_buffers_alive():
+    """A phase holds raw addresses; the binding keeps the buffers it points to alive, so a
+    caller that drops its own references cannot have them freed and reused underneath."""
+    import gc
+    import weakref
+
+    import torch
+    L = spax.spax_layout_init(64, [64], 0, 128, 64)
+    bufs = [torch.zeros(n, dtype=dt) for n, dt in [(int(L.total_bytes), torch.uint8),
+                                                    (64, torch.float16), (64, torch.uint8),
+                                                    (64, torch.int32), (64, torch.int32),
+                                                    (3, torch.int32), (64, torch.float32)]]
+    refs = [weakref.ref(b) for b in bufs]
+    arr = spax.phase_array([spax.make_phase(L, bufs[0], bufs[1], spax.topk_params(8, 8),
+                                            *bufs[2:])])
+    del bufs
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del arr
+    gc.collect()
+    assert all(r() is None for r in refs)
