@@ -1,7 +1,8 @@
 """GPU parity at the full sizes the benchmark runs: one layer of the 7B-shaped decoder (q|k|v
 4096 -> 3 x 4096, o 4096 -> 4096, gate|up 4096 -> 2 x 11008, down 11008 -> 4096) through
 spax_decode_step_projections in the launch forms the benchmark times (fused layer-serial and
-batched), fp16 and int4 bases, TopK-Guided masks.
+batched), fp16 and int4 bases, TopK-Guided masks; and the pinned-host path at the
+Llama-3-8B down projection (14336 -> 4096) in both transfer modes.
 
 Masks, lists and counts are compared with the oracle bit for bit over every channel.  The
 oracle GEMV over whole matrices of this size is slow, so y is checked on sampled rows: whole
@@ -95,3 +96,39 @@ def test_decode_layer_7b_full_size(env, fmt, flags):
             err = rel_l2(y[off + rows], ref)
             assert err <= REL_L2, (k, m, err)
             off += r
+
+
+@pytest.mark.parametrize("transfer", [0, 1])
+def test_pinned_down_projection_8b_full_size(env, transfer):
+    """The pinned-host path at the Llama-3-8B down projection (14336 -> 4096): y on sampled
+    row groups against the oracle, the byte account against the oracle's range ledger."""
+    from oracle import ranges as orng
+    torch, spax, dev = env
+    d_in, d_out = 14336, [4096]
+    L = spax.spax_layout_init(d_in, d_out, 0, GROUP, GROUP)
+    O = opack.Layout(d_in, d_out, 0, GROUP, GROUP)
+    Ws = [synth.weights(SEED, d_in, d_out[0], 7)]
+    packed = torch.empty(int(L.total_bytes), dtype=torch.uint8, device=dev)
+    spax.spax_pack_columns(L, [torch.from_numpy(Ws[0]).to(dev)], packed)
+    host = torch.empty(int(L.total_bytes), dtype=torch.uint8, pin_memory=True)
+    host.copy_(packed)
+    del packed
+    x16 = synth.activations(SEED, d_in, 7, channel_scaled=True)
+    nF, nA = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
+    x = torch.from_numpy(x16).to(dev)
+    f = torch.empty(d_in, dtype=torch.int32, device=dev)
+    a = torch.empty(d_in, dtype=torch.int32, device=dev)
+    c = torch.zeros(3, dtype=torch.int32, device=dev)
+    spax.spax_build_tiers(x, d_in, spax.topk_params(nF, nA), None, f, a, c)
+    y = torch.full((d_out[0],), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(spax.spax_pinned_workspace_bytes(L), dtype=torch.uint8, device=dev)
+    st = spax.spax_tiered_gemv_pinned(L, host, x, f, a, c, y, 0, ws, transfer=transfer)
+    torch.cuda.synchronize()
+    _, wf, wa, _ = otiers.build_tiers(x16, otiers.MODE_TOPK, n_full=nF, n_approx=nA)
+    rows = np.concatenate([np.arange(g * GROUP, (g + 1) * GROUP) for g in sampled_groups(4096)])
+    ref = ogemv.tiered_gemv(opack.Layout(d_in, [len(rows)], 0, GROUP, GROUP),
+                            [np.ascontiguousarray(Ws[0][:, rows])], x16, wf, wa)
+    assert rel_l2(y.cpu().numpy()[rows], ref) <= REL_L2
+    led = orng.ledger(wf, wa, O.stride_F, O.stride_A, 0)
+    assert st.selected_bytes == led["selected_bytes"] and st.moved_bytes == led["moved_bytes"]
+    assert st.n_ranges == led["n_ranges"]
