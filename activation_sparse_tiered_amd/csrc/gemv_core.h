@@ -153,22 +153,29 @@ __device__ __forceinline__ T* uniform(T* p) {
 #ifndef SPAX_NT_LOADS
 #define SPAX_NT_LOADS 1
 #endif
-__device__ __forceinline__ uint32_t load_stream(const uint32_t* p) {
-#if SPAX_NT_LOADS
-  return __builtin_nontemporal_load((global_ptr<uint32_t>)p);
-#else
-  return load_global<uint32_t>(p);
-#endif
-}
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-#if SPAX_NT_LOADS
-  const u32x4 v = __builtin_nontemporal_load((global_ptr<u32x4>)p);
-#else
-  const u32x4 v = load_global<u32x4>(p);
-#endif
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
+
+// Loads from one column record through a buffer descriptor built on the record's (uniform)
+// base: the record base stays in scalar registers and the lane's byte offset, the same for
+// every column, is the only vector operand, so no 64-bit address is added per column and
+// load.  The descriptor's size is the record's, so a load past it reads zero.
+struct Record {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ Record(const uint8_t* base, int64_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
+                                            0x00020000)) {}
+  // cache policy 2: non-temporal (weight codes are read once per token)
+  __device__ __forceinline__ uint32_t stream32(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, SPAX_NT_LOADS ? 2 : 0);
+  }
+  __device__ __forceinline__ uint32_t word(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ __forceinline__ uint4 stream128(uint32_t off) const {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SPAX_NT_LOADS ? 2 : 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+};
 
 // A block of up to 64 entries of a column list held in registers, one per lane: entry =
 // channel | (fp16 bits of x_j) << 16, for list positions [base, base + 64).  Loaded with one
@@ -246,12 +253,12 @@ struct EarlyColumns {
     for (int u = 0; u < P; ++u) {
       const uint32_t j = min(e[u] & 0xFFFFu, jmax);
       xv[u] = u < n ? half_hi(e[u]) : 0.0f;
-      const uint8_t* col = packed + (int64_t)j * sh.stride_F;
+      const Record rec(packed + (int64_t)j * sh.stride_F, sh.stride_F);
       if (FMT == SPAX_FMT_FP16) {
-        v[u] = load_stream(reinterpret_cast<const uint4*>(col + loffF));
+        v[u] = rec.stream128(loffF);
       } else {
-        c[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffF));
-        sz[u] = load_global<uint32_t>(col + szoffF);
+        c[u] = rec.stream32(loffF);
+        sz[u] = rec.word(szoffF);
       }
     }
   }
@@ -307,12 +314,12 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
       if (u < nf) {
         int j;
         srcF.get(fi + u, j, xf[u]);
-        const uint8_t* col = packed + (int64_t)j * sh.stride_F;
+        const Record rec(packed + (int64_t)j * sh.stride_F, sh.stride_F);
         if (FMT == SPAX_FMT_FP16) {
-          vf[u] = load_stream(reinterpret_cast<const uint4*>(col + loffF));
+          vf[u] = rec.stream128(loffF);
         } else {
-          cf[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffF));
-          sf[u] = load_global<uint32_t>(col + szoffF);
+          cf[u] = rec.stream32(loffF);
+          sf[u] = rec.word(szoffF);
         }
       }
     }
@@ -321,9 +328,9 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
       if (u < na) {
         int j;
         srcA.get(ai + u, j, xa[u]);
-        const uint8_t* col = regionA + (int64_t)j * sh.stride_A;
-        ca[u] = load_stream(reinterpret_cast<const uint32_t*>(col + loffA4));
-        sa[u] = load_global<uint32_t>(col + szoffA);
+        const Record rec(regionA + (int64_t)j * sh.stride_A, sh.stride_A);
+        ca[u] = rec.stream32(loffA4);
+        sa[u] = rec.word(szoffA);
       }
     }
     // A tier with no column in this round skips its multiplies (a wave-uniform branch around
