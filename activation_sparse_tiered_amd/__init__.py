@@ -21,6 +21,7 @@ __all__ = [
     "spax_tiered_gemv", "spax_step_workspace_bytes", "spax_decode_step_projections",
     "spax_key_threshold", "spax_counts_from_fractions", "spax_guided_bounds", "spax_version",
     "spax_column_ranges", "spax_pinned_workspace_bytes", "spax_tiered_gemv_pinned", "MoveStats",
+    "spax_read_probe",
     "topk_params", "threshold_params", "guided_params", "make_phase", "Layout", "TierParams",
     "Phase", "Step", "SpaxError", "LIB_PATH",
 ]
@@ -202,6 +203,26 @@ def spax_decode_step_projections(phases, ws, ws_bytes: int | None = None, flags:
         st.events = C.cast(ev, C.POINTER(C.c_void_p))
     check(lib.spax_decode_step_projections(C.byref(st), _stream(stream)),
           "spax_decode_step_projections")
+
+
+# ------------------------------------------------------------------ diagnostics
+
+def spax_read_probe(buf, out, nbytes: int | None = None, offset: int = 0, stream=None) -> int:
+    """Reads ``nbytes`` bytes of the device tensor ``buf`` from byte ``offset`` (default: all
+    of it); every wave stores the XOR of the 32-bit words it read in its own word of the
+    device tensor ``out`` (int32/uint32).  Returns how many leading words of ``out`` were
+    written: their XOR is the XOR of all words read."""
+    total = buf.numel() * buf.element_size()
+    if nbytes is None:
+        nbytes = total - offset
+    if offset < 0 or nbytes < 0 or offset + nbytes > total:
+        raise ValueError("read range outside the buffer")
+    n = C.c_int32()
+    words = out.numel() * out.element_size() // 4
+    check(lib.spax_read_probe(C.c_void_p(_ptr(buf) + int(offset)), int(nbytes), _ptr(out),
+                              int(min(words, 2**31 - 1)), C.byref(n), _stream(stream)),
+          "spax_read_probe")
+    return int(n.value)
 
 
 # ------------------------------------------------------------------ host helpers

@@ -1,6 +1,6 @@
 """ctypes view of libspax.so (the C ABI declared in include/spax.h).
 
-Loads the in-tree library built by ``activation_sparse_tiered_amd.build``.  There is no
+Loads the in-tree library built by ``activation_sparse_tiered_amd/build.py``.  There is no
 fallback: if the library is missing, importing this module raises.
 """
 
@@ -78,7 +78,8 @@ def _hip_runtimes():
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run activation_sparse_tiered_amd.build.build()")
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python activation_sparse_tiered_amd/build.py")
     # torch owns the device memory and the streams we are handed, so libspax must bind to the
     # HIP runtime torch has loaded.  Loading torch first makes libspax's libamdhip64.so.7
     # dependency resolve to that already-loaded copy (same soname); a second runtime in the
@@ -102,6 +103,7 @@ def _load():
         "spax_pinned_workspace_bytes": (C.c_size_t, [C.POINTER(Layout)]),
         "spax_tiered_gemv_pinned": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, C.c_int32,
                                               C.c_int32, P, C.c_size_t, C.POINTER(MoveStats), P]),
+        "spax_read_probe": (C.c_int, [P, C.c_size_t, P, C.c_int32, C.POINTER(C.c_int32), P]),
         "spax_key_threshold": (C.c_int32, [C.c_double]),
         "spax_counts_from_fractions": (C.c_int, [C.c_int32, C.c_double, C.c_double,
                                                  C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),

@@ -1,6 +1,6 @@
 """Build libspax.so in-tree with hipcc for gfx950.
 
-    python -m activation_sparse_tiered_amd.build        # or build() from Python
+    python activation_sparse_tiered_amd/build.py       # or __graft_entry__.build()
 
 Every source under csrc/ is compiled as HIP for gfx950 and linked into
 activation_sparse_tiered_amd/libspax.so.  Objects go to _build/ at the repository root.
@@ -29,7 +29,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["host.cpp", "api.cpp", "pack.hip", "tiers.hip", "gemv.hip", "decode.hip", "batch.hip", "pinned.cpp"]
+SOURCES = ["host.cpp", "api.cpp", "pack.hip", "tiers.hip", "gemv.hip", "decode.hip", "batch.hip",
+           "pinned.cpp", "probe.hip"]
 
 
 def hipcc() -> str:

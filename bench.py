@@ -31,7 +31,11 @@ the host cores.  ``batched`` is the same step in the batched launch form (all ma
 launch, all GEMVs in one), legal here only because the synthetic inputs are independent.
 ``token_us`` gives the median and 90th percentile over the timed tokens, each timed on its
 own after the timed region.  ``--control full|skip`` replaces the tier rule by all-FULL or
-all-SKIP masks: controls for the hardware byte counters.
+all-SKIP masks: controls for the hardware byte counters.  ``read_probe`` gives what a plain
+streaming read (spax_read_probe) gets: its rate on one large read (also reported in
+``roofline`` as a measured second denominator) and the time of the step's launch pattern
+when every launch only reads its selected byte count (a floor for the layer-serial form).
+For linear512 and mlp7b ``cpu_baseline`` also holds a one-thread run of the oracle.
 """
 
 from __future__ import annotations
@@ -75,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip timing the batched step form")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the plain streaming-read ceiling and floor")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="before the timed steps, run one elementwise kernel (bitwise_not) that "
                          "reads and writes this many MiB: known traffic for scaling hardware "
@@ -262,20 +268,38 @@ def recorded_traffic(args):
     return float(vals["traffic_MB_per_launch"])
 
 
-def cpu_baseline(stack, layers):
-    """The oracle on `layers` layers of token 0, timed on the host, scaled to one token.
-    Each phase's weights are drawn (on the device, as for the GPU run) and copied to the
-    host right before it is timed, so only one phase is held in host memory at a time."""
+def cpu_baseline(stack, layers, threads=None, min_seconds=2.0):
+    """The oracle on `layers` layers of token 0, timed on the host, scaled to one token;
+    the whole sample is repeated until it has taken at least `min_seconds` (small workloads)
+    and the mean is reported.  Each phase's weights are drawn (on the device, as for the GPU
+    run) and copied to the host right before it is timed, so only one phase is held in host
+    memory at a time.  `threads`: BLAS threads (default: every core this process may run on)."""
     from oracle import gemv as ogemv
     from oracle import pack as opack
     from oracle import tiers as otiers
     spec = stack.spec
-    cores = len(os.sched_getaffinity(0))
+    cores = threads or len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
         limiter = None
+    dt = 0.0
+    reps = 0
+    while reps == 0 or dt < min_seconds:
+        dt += _oracle_pass(stack, spec, layers, ogemv, opack, otiers)
+        reps += 1
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    per_token_us = dt / reps / layers * stack.layers * 1e6 / spec["tokens_per_step"]
+    return {"value": round(per_token_us, 1), "unit": "us/token", "cores": cores, "kind": "oracle",
+            "sample": f"{layers} of {stack.layers} layers ({len(stack.shapes)} projection groups "
+                      f"each) of one token, {reps} time(s): float64 NumPy tier mask + tiered "
+                      f"GEMV, scaled to one token; {dt:.1f} s measured; BLAS threads = {cores}"}
+
+
+def _oracle_pass(stack, spec, layers, ogemv, opack, otiers):
+    """Seconds the oracle takes for `layers` layers of token 0 (weights drawn untimed)."""
     dt = 0.0
     for l in range(layers):
         for k, (name, d_in, d_out) in enumerate(stack.shapes):
@@ -296,13 +320,60 @@ def cpu_baseline(stack, layers):
             ogemv.tiered_gemv(O, Ws, x, f, a)
             dt += time.perf_counter() - t0
             del Ws
-    if limiter is not None and hasattr(limiter, "unregister"):
-        limiter.unregister()
-    per_token_us = dt / layers * stack.layers * 1e6 / spec["tokens_per_step"]
-    return {"value": round(per_token_us, 1), "unit": "us/token", "cores": cores, "kind": "oracle",
-            "sample": f"{layers} of {stack.layers} layers ({len(stack.shapes)} projection groups "
-                      f"each) of one token: float64 NumPy tier mask + tiered GEMV, scaled to one "
-                      f"token; {dt:.1f} s measured; BLAS threads = cores"}
+    return dt
+
+
+def read_probe(spax, torch, dev, launch_bytes, reps=8):
+    """What a launch that only reads gets, with spax_read_probe (16-byte non-temporal loads
+    over the whole GPU, nothing else): (1) the ceiling, its rate on one 2 GiB read; (2) the
+    floor of the timed step's launch pattern, i.e. the same number of launches back to back
+    on one stream, each reading as many bytes as that launch of the step selects (from
+    consecutive places of the 2 GiB buffer, so the last-level cache does not hold them)."""
+    big = 2 << 30
+    buf = torch.empty(big, dtype=torch.uint8, device=dev)
+    out = torch.zeros(8192, dtype=torch.int32, device=dev)
+    f = spax.lib.spax_read_probe
+    stream = torch.cuda.current_stream().cuda_stream
+    base, outp = buf.data_ptr(), out.data_ptr()
+
+    def run(ranges):
+        # raw ctypes calls on precomputed pointers keep the host ahead of the GPU
+        bad = 0
+        for o, n in ranges:
+            bad |= f(base + o, n, outp, 8192, None, stream)
+        if bad:
+            raise RuntimeError(f"spax_read_probe failed: {spax.lib.spax_last_error()}")
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(ranges):
+        run(ranges)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            run(ranges)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us per pass
+
+    ceil_us = timed([(0, big)])
+    ranges, off = [], 0
+    for b in launch_bytes:
+        n = int(b) // 16 * 16
+        if off + n > big:
+            off = 0
+        ranges.append((off, n))
+        off += (n + 4095) // 4096 * 4096
+    floor_us = timed(ranges)
+    total = sum(n for _, n in ranges)
+    del buf, out
+    return {"ceiling_GBps": round(big / (ceil_us * 1e-6) / 1e9, 1),
+            "floor_us_per_step": round(floor_us, 2),
+            "floor_GBps": round(total / (floor_us * 1e-6) / 1e9, 1),
+            "launches_per_step": len(ranges),
+            "what": "spax_read_probe (a plain streaming read, 16-byte non-temporal loads): "
+                    "ceiling = one 2 GiB read; floor = the timed step's launches back to back, "
+                    "each reading that launch's selected byte count"}
 
 
 def device_bench(args, spax, torch, dev):
@@ -338,20 +409,25 @@ def device_bench(args, spax, torch, dev):
     n_ph = len(stack.layouts)
     tok_bytes = {}
     per_phase = {}
+    launch_bytes = None  # per launch, first timed token
     for t in range(args.warmup, args.warmup + args.steps):
         key = t % stack.tokens
         if key in tok_bytes:
             continue
         ms, counts = stack.timed_kernels(t)
         tb = 0
+        lb = []
         for i, (m, c) in enumerate(zip(ms, counts)):
             b = stack.algorithmic_bytes(i, c)
             tb += b
+            lb.append(b)
             pb = per_phase.setdefault(stack.shapes[i % len(stack.shapes)][0], [0, 0.0, 0])
             pb[0] += b
             pb[1] += m
             pb[2] += 1
         tok_bytes[key] = tb
+        if launch_bytes is None:
+            launch_bytes = lb
     timed_bytes = [tok_bytes[t % stack.tokens] for t in range(args.warmup, args.warmup + args.steps)]
     bytes_per_step = float(np.mean(timed_bytes))
     # The timed step is one fused launch per phase (plus one small clearing launch), back to
@@ -404,9 +480,19 @@ def device_bench(args, spax, torch, dev):
                            "independent"}
         log(f"[bench] batched step: {bt_ms * 1e3:.1f} us, {bgbs:.1f} GB/s")
 
+    probe = None
+    if not args.no_read_probe:
+        probe = read_probe(spax, torch, dev, launch_bytes)
+        probe["floor_us_per_token"] = round(probe["floor_us_per_step"] / per_tok, 2)
+        log(f"[bench] read probe {probe}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(stack, spec["cpu_layers"])
+        if args.workload in ("linear512", "mlp7b"):
+            one = cpu_baseline(stack, spec["cpu_layers"], threads=1)
+            cpu["one_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1,
+                                 "sample": one["sample"]}
         log(f"[bench] cpu baseline {cpu}")
 
     return {
@@ -431,10 +517,14 @@ def device_bench(args, spax, torch, dev):
                      "traffic_unit": "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "fused_phase_kernel<%s>" % ("fp16" if spec["fmt"] == 0 else "int4"),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-                     "avg_algorithmic_MB": round(avg_bytes / 1e6, 3)},
+                     "avg_algorithmic_MB": round(avg_bytes / 1e6, 3),
+                     "measured_read_GBps": probe["ceiling_GBps"] if probe else None,
+                     "frac_of_measured_read": (round(achieved / probe["ceiling_GBps"], 4)
+                                               if probe else None)},
         "cpu_baseline": cpu,
         "batched": batched,
         "token_us": token_us,
+        "read_probe": probe,
     }
 
 

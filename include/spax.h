@@ -329,6 +329,23 @@ size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases);
  */
 int spax_decode_step_projections(const spax_step* step, hipStream_t stream);
 
+/* ---------------------------------------------------------------- diagnostics */
+
+/* A plain streaming read, to measure what a launch that only reads gets from the memory
+ * system (not a step of the method; the benchmark uses it for a read ceiling and for a
+ * read floor at the byte counts of a decode step's launches).  The `bytes` bytes at p
+ * (device memory) are read once with 16-byte non-temporal loads by 512-thread workgroups
+ * (reads of 1 GiB or more: one contiguous chunk per workgroup, one workgroup per compute
+ * unit; smaller reads: grid-stride over four workgroups per unit), and every wave stores
+ * the XOR of the 32-bit words it read in its own word of `out` (device memory, out_words
+ * uint32, at least 8; fewer words than waves means fewer workgroups).  The XOR of the first
+ * *n_written words (host; nullable) is the XOR of all words read.  bytes = 0 launches
+ * nothing and sets *n_written = 0.  Asynchronous on `stream`.  Errors: SPAX_ERR_NULL (p or
+ * out NULL), SPAX_ERR_ALIGN (p or bytes not a multiple of 16, out not 4-byte aligned),
+ * SPAX_ERR_PARAM (out_words < 8), SPAX_ERR_HIP. */
+int spax_read_probe(const void* p, size_t bytes, uint32_t* out, int32_t out_words,
+                    int32_t* n_written, hipStream_t stream);
+
 /* ---------------------------------------------------------------- host helpers */
 
 /* K(tau): smallest fp16 magnitude key k in [0, 0x7C00] with half(k) >= tau (compared in

@@ -137,6 +137,38 @@ def test_build_tiers_validation():
 
 
 @needs_no_gpu
+def test_read_probe_validation():
+    lib = _lib.lib
+    n = C.c_int32(-1)
+    assert lib.spax_read_probe(FAKE, 0, FAKE, 8, C.byref(n), 0) == _lib.SPAX_OK  # no launch
+    assert n.value == 0
+    assert lib.spax_read_probe(0, 16, FAKE, 8, None, 0) == _lib.SPAX_ERR_NULL
+    assert lib.spax_read_probe(FAKE, 16, 0, 8, None, 0) == _lib.SPAX_ERR_NULL
+    assert lib.spax_read_probe(FAKE + 8, 16, FAKE, 8, None, 0) == _lib.SPAX_ERR_ALIGN
+    assert lib.spax_read_probe(FAKE, 24, FAKE, 8, None, 0) == _lib.SPAX_ERR_ALIGN
+    assert lib.spax_read_probe(FAKE, 16, FAKE + 2, 8, None, 0) == _lib.SPAX_ERR_ALIGN
+    assert "4-byte" in lib.spax_last_error().decode()
+    assert lib.spax_read_probe(FAKE, 16, FAKE, 7, None, 0) == _lib.SPAX_ERR_PARAM
+
+
+def test_builder_loads_without_the_package():
+    """build() must work where the library is missing or older than the header, so the
+    builder module is loaded by path and does not import the package (which loads the
+    library)."""
+    import subprocess
+    import sys
+    code = ("import importlib.util, sys; "
+            f"s = importlib.util.spec_from_file_location('b', {os.path.join(ROOT, 'activation_sparse_tiered_amd', 'build.py')!r}); "
+            "m = importlib.util.module_from_spec(s); s.loader.exec_module(m); "
+            "assert 'activation_sparse_tiered_amd' not in sys.modules; "
+            "assert 'probe.hip' in m.SOURCES; print('ok')")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+    src = open(os.path.join(ROOT, "__graft_entry__.py")).read()
+    assert "spec_from_file_location" in src
+
+
+@needs_no_gpu
 def test_gemv_and_pack_validation():
     lib = _lib.lib
     L = spax.spax_layout_init(64, [512], 0, 128, 64)
