@@ -76,6 +76,46 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+#ifndef SPAX_SHARE_LISTS
+#define SPAX_SHARE_LISTS 1
+#endif
+
+// The next up to kUnroll entries of tier t (0 FULL, 1 APPROX) for this wave from the column
+// lists of its workgroup: from its own list while that has entries left, else from the next
+// wave's list (in wave order) that has.  q = KeyHist::lists_q; lane v reads wave v's counter
+// and published length, so one look costs one LDS round trip.  A list not yet published
+// looks used up (its owner streams it).  A claim is one LDS atomic on the list's counter, so
+// every entry goes to exactly one wave; a claim that comes too late leaves that counter at
+// or past the length, so the list drops out of the next look, and the loop ends after at
+// most kFusedWaves such misses.  Returns the count (0: no work left) and sets `base`, the
+// entry's index from the start of the lists (wave v's FULL list at 2 v S, its APPROX list at
+// 2 v S + S).  Wave-uniform.
+__device__ __forceinline__ int claim_entries(int (*q)[kFusedWaves], int t, int wave, int S,
+                                             int lane, int& base) {
+#pragma unroll 1
+  for (int miss = 0; miss <= kFusedWaves; ++miss) {
+    const int v_l = lane & (kFusedWaves - 1);
+    const int c = __hip_atomic_load(&q[2 + t][v_l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int seen = __hip_atomic_load(&q[t][v_l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t m = (uint32_t)__ballot(lane < kFusedWaves && seen < c);  // wave v: bit v
+    if (m == 0u) return 0;
+    const uint32_t rot = ((m >> wave) | (m << (kFusedWaves - wave))) & 0xFFFFu;  // own wave first
+    const int v = (wave + (int)__builtin_ctz(rot)) & (kFusedWaves - 1);
+    const int cv = __builtin_amdgcn_readlane(c, v);
+    int st = 0;
+    if (lane == 0)
+      st = __hip_atomic_fetch_add(&q[t][v], gemv::kUnroll, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+    st = __builtin_amdgcn_readfirstlane(st);
+    if (st < cv) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // the entries before the count
+      base = v * 2 * S + t * S + st;
+      return min(gemv::kUnroll, cv - st);
+    }
+  }
+  return 0;
+}
+
 // Channels j in [begin, end) whose key is kb0 / kb1 (begin a multiple of 8; eight keys per
 // lane and LDS read).  One wave; the result is wave-uniform.
 __device__ __forceinline__ void ties_between(const uint32_t* xs32, int begin, int end, int kb0,
@@ -269,8 +309,44 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
   float zsum = 0.0f;
   if (kUseEarly) early.multiply(acc, zsum);
-  gemv::stream_columns<FMT>(sh, a.packed, row, 0, nF, gemv::LdsList{lF, 0, jmax}, 0, nA,
-                            gemv::LdsList{lA, 0, jmax}, acc, zsum);
+  if (SPAX_SHARE_LISTS) {
+    // The waves' lists are shared out: a wave streams its own list and then helps the
+    // others, so the workgroup ends with its average wave rather than its longest list.
+    // Publishing: the entries are written before the count (release), a claim reads the
+    // count before the entries (acquire).
+    // The wave keeps its first round for itself: its counters start past those entries, set
+    // before the lengths are published, so no claim is needed to start.
+    int nf = min(nF, gemv::kUnroll), na = min(nA, gemv::kUnroll);
+    int bF = wave * 2 * S, bA = wave * 2 * S + S;
+    if (lane == 0) {
+      __hip_atomic_store(&u.kh.lists_q[0][wave], nf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(&u.kh.lists_q[1][wave], na, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) {
+      __hip_atomic_store(&u.kh.lists_q[2][wave], nF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(&u.kh.lists_q[3][wave], nA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    const uint32_t* lists = reinterpret_cast<const uint32_t*>(dyn + a.xs_bytes);
+    const gemv::TileOffsets<FMT> g(sh, row);
+    while (nf > 0 || na > 0) {
+      gemv::RoundLoads<FMT> r;
+      gemv::issue_round<FMT>(sh, a.packed, g, gemv::LdsBlock(lists + bF, nf, jmax), 0, nf,
+                             gemv::LdsBlock(lists + bA, na, jmax), 0, na, r);
+      // the next claims overlap this round's loads
+      int nbF = bF, nbA = bA;
+      const int nf2 = claim_entries(u.kh.lists_q, 0, wave, S, lane, nbF);
+      const int na2 = claim_entries(u.kh.lists_q, 1, wave, S, lane, nbA);
+      gemv::finish_round<FMT>(r, g, nf, na, acc, zsum);
+      nf = nf2;
+      na = na2;
+      bF = nbF;
+      bA = nbA;
+    }
+  } else {
+    gemv::stream_columns<FMT>(sh, a.packed, row, 0, nF, gemv::LdsList{lF, 0, jmax}, 0, nA,
+                              gemv::LdsList{lA, 0, jmax}, acc, zsum);
+  }
   __syncthreads();  // every wave is done with the mask scratch that `red` overlays
   gemv::finish_tile<kFusedWaves>(u.red, acc, zsum, wave, lane, row0, T, sh.n_chunks, a.y);
   clear_next(a);

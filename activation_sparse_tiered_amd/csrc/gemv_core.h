@@ -234,6 +234,23 @@ struct LdsList {
   }
 };
 
+// Up to 64 consecutive LDS list entries (as in LdsList) held one per lane: one LDS read for
+// the wave instead of one read and wait per column; get() broadcasts entry i with readlane.
+// Lanes past n read entry n - 1 (entry 0 when n <= 0), so p must hold at least one entry.
+struct LdsBlock {
+  uint32_t e;
+  uint32_t jmax;
+  __device__ __forceinline__ LdsBlock(const uint32_t* p, int n, uint32_t jmax_) : jmax(jmax_) {
+    const int lane = threadIdx.x & 63;
+    e = p[min(lane, max(n - 1, 0))];
+  }
+  __device__ __forceinline__ void get(int i, int& j, float& xv) const {
+    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)e, i);
+    j = (int)min(v & 0xFFFFu, jmax);
+    xv = half_hi(v);
+  }
+};
+
 // Up to P FULL columns whose loads are issued ahead of the rest of the work and multiplied
 // later (the fused decode kernel issues them while its mask is still being completed, so
 // their memory latency overlaps that work).  Entries as in LdsList.  All P loads are issued
@@ -274,6 +291,100 @@ struct EarlyColumns {
   }
 };
 
+// A lane's byte offsets inside a column record for its rows of the tile.
+template <int FMT>
+struct TileOffsets {
+  uint32_t loffA4;  // two-bit codes: the aligned dword that holds the lane's 2 bytes (a 16-bit
+                    // load would be widened right after it is issued, which makes it wait)
+  uint32_t selA;    // byte selector for those 2 bytes
+  uint32_t szoffA;  // (s, z) word of the lane's two-bit group
+  uint32_t loffF;   // FULL codes (fp16 rows or int4 codes)
+  uint32_t szoffF;  // (s, z) word of the lane's int4 group
+  __device__ __forceinline__ TileOffsets(const Shape& sh, int row)
+      : loffA4(((uint32_t)row / 4u) & ~3u),
+        selA(spread_sel(((uint32_t)row / 4u) & 2u)),
+        szoffA((uint32_t)(sh.T / 4) + (uint32_t)(row / sh.approx_group) * 4u),
+        loffF(FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u),
+        szoffF((uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u) {}
+};
+
+// The registers of one round: up to kUnroll FULL and kUnroll APPROX columns.
+template <int FMT>
+struct RoundLoads {
+  float xf[kUnroll], xa[kUnroll];
+  uint4 vf[kUnroll];
+  uint32_t cf[kUnroll], sf[kUnroll], ca[kUnroll], sa[kUnroll];
+};
+
+// Issues the loads of FULL columns [fi, fi + nf) of srcF and APPROX columns [ai, ai + na) of
+// srcA (counts wave-uniform, at most kUnroll, may be <= 0).  Slots past a count keep zero
+// data and a zero activation.
+template <int FMT, class SrcF, class SrcA>
+__device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __restrict__ packed,
+                                            const TileOffsets<FMT>& g, const SrcF& srcF, int fi,
+                                            int nf, const SrcA& srcA, int ai, int na,
+                                            RoundLoads<FMT>& r) {
+  const uint8_t* regionA = packed + sh.off_A;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    r.xf[u] = 0.0f;
+    r.xa[u] = 0.0f;
+    r.vf[u] = make_uint4(0u, 0u, 0u, 0u);
+    r.cf[u] = r.sf[u] = r.ca[u] = r.sa[u] = 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if (u < nf) {
+      int j;
+      srcF.get(fi + u, j, r.xf[u]);
+      const Record rec(packed + (int64_t)j * sh.stride_F, sh.stride_F);
+      if (FMT == SPAX_FMT_FP16) {
+        r.vf[u] = rec.stream128(g.loffF);
+      } else {
+        r.cf[u] = rec.stream32(g.loffF);
+        r.sf[u] = rec.word(g.szoffF);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if (u < na) {
+      int j;
+      srcA.get(ai + u, j, r.xa[u]);
+      const Record rec(regionA + (int64_t)j * sh.stride_A, sh.stride_A);
+      r.ca[u] = rec.stream32(g.loffA4);
+      r.sa[u] = rec.word(g.szoffA);
+    }
+  }
+}
+
+// Waits for every load of the round and multiplies.  A tier with no column in the round
+// skips its multiplies (a wave-uniform branch around whole blocks).  The explicit wait for
+// every load makes the branches visible as complete to the compiler's wait tracking, which
+// otherwise assumes loads of a skipped block are still in flight in the next round and waits
+// for each of them there.
+template <int FMT>
+__device__ __forceinline__ void finish_round(const RoundLoads<FMT>& r, const TileOffsets<FMT>& g,
+                                             int nf, int na, float (&acc)[8], float& zsum) {
+  __builtin_amdgcn_s_waitcnt(0);
+  if (nf > 0) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (FMT == SPAX_FMT_FP16) {
+        fma_fp16x8(acc, r.xf[u], r.vf[u]);
+      } else {
+        fma_int4x8(acc, group_terms<4>(r.xf[u], r.sf[u], zsum), r.cf[u]);
+      }
+    }
+  }
+  if (na > 0) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      fma_int2x8(acc, group_terms<2>(r.xa[u], r.sa[u], zsum), r.ca[u], g.selA);
+    }
+  }
+}
+
 // FULL columns [fb, fe) of `srcF` and APPROX (two-bit) columns [ab, ae) of `srcA` into
 // acc / zsum.  Each round issues the loads of up to kUnroll FULL and kUnroll APPROX columns
 // back to back (the counts are wave-uniform, so the guards are scalar branches) and only then
@@ -288,72 +399,13 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
                                                int row, int fb, int fe, const SrcF& srcF, int ab,
                                                int ae, const SrcA& srcA, float (&acc)[8],
                                                float& zsum) {
-  const uint8_t* regionA = packed + sh.off_A;
-  // A lane's 2 bytes of two-bit codes are read as the aligned dword that holds them (a
-  // 16-bit load would be widened right after it is issued, which makes it wait).
-  const uint32_t loffA4 = ((uint32_t)row / 4u) & ~3u;
-  const uint32_t selA = spread_sel(((uint32_t)row / 4u) & 2u);
-  const uint32_t szoffA = (uint32_t)(sh.T / 4) + (uint32_t)(row / sh.approx_group) * 4u;
-  const uint32_t loffF = FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u;
-  const uint32_t szoffF = (uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u;
+  const TileOffsets<FMT> g(sh, row);
   int fi = fb, ai = ab;
   while (fi < fe || ai < ae) {
     const int nf = min(fe - fi, kUnroll), na = min(ae - ai, kUnroll);  // may be <= 0
-    float xf[kUnroll], xa[kUnroll];
-    uint4 vf[kUnroll];
-    uint32_t cf[kUnroll], sf[kUnroll], ca[kUnroll], sa[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      xf[u] = 0.0f;
-      xa[u] = 0.0f;
-      vf[u] = make_uint4(0u, 0u, 0u, 0u);
-      cf[u] = sf[u] = ca[u] = sa[u] = 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (u < nf) {
-        int j;
-        srcF.get(fi + u, j, xf[u]);
-        const Record rec(packed + (int64_t)j * sh.stride_F, sh.stride_F);
-        if (FMT == SPAX_FMT_FP16) {
-          vf[u] = rec.stream128(loffF);
-        } else {
-          cf[u] = rec.stream32(loffF);
-          sf[u] = rec.word(szoffF);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (u < na) {
-        int j;
-        srcA.get(ai + u, j, xa[u]);
-        const Record rec(regionA + (int64_t)j * sh.stride_A, sh.stride_A);
-        ca[u] = rec.stream32(loffA4);
-        sa[u] = rec.word(szoffA);
-      }
-    }
-    // A tier with no column in this round skips its multiplies (a wave-uniform branch around
-    // whole blocks).  The explicit wait for every load makes the branches visible as complete
-    // to the compiler's wait tracking, which otherwise assumes loads of a skipped block are
-    // still in flight in the next round and waits for each of them there.
-    __builtin_amdgcn_s_waitcnt(0);
-    if (nf > 0) {
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (FMT == SPAX_FMT_FP16) {
-          fma_fp16x8(acc, xf[u], vf[u]);
-        } else {
-          fma_int4x8(acc, group_terms<4>(xf[u], sf[u], zsum), cf[u]);
-        }
-      }
-    }
-    if (na > 0) {
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        fma_int2x8(acc, group_terms<2>(xa[u], sa[u], zsum), ca[u], selA);
-      }
-    }
+    RoundLoads<FMT> r;
+    issue_round<FMT>(sh, packed, g, srcF, fi, nf, srcA, ai, na, r);
+    finish_round<FMT>(r, g, nf, na, acc, zsum);
     fi += max(nf, 0);
     ai += max(na, 0);
   }

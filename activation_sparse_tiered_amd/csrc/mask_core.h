@@ -367,6 +367,10 @@ struct KeyHist {
   alignas(16) int coarse[1024];      // channels with key in [32c, 32c + 32)
   int wave_nat[W];
   int wave_ties[W];  // per mask-pass wave range: channels at boundary key 0 | key 1 << 16
+  // For a caller that shares out column lists among its waves after the search: per wave,
+  // the next unclaimed FULL / APPROX entry ([0], [1]) and the published list lengths ([2],
+  // [3]); zeroed by select_begin before its first barrier.
+  int lists_q[4][W];
   Select sel[2];
   int E[2];
 };
@@ -406,6 +410,7 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
       uint4* c4 = reinterpret_cast<uint4*>(h.coarse);
       for (int i = tid; i < 1024 / 4; i += NT) c4[i] = z;
     }
+    if (tid < 4 * W) (&h.lists_q[0][0])[tid] = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q)
       if (tid + q * NT < ndw) xs32[tid + q * NT] = v[q];
