@@ -6,7 +6,9 @@ one launch, all GEMVs in one launch) wherever the phases are independent.
 * the two-kernel fallback (d_in > 16384) mixed into the same step;
 * a single column chunk (tiny d_in: plain stores instead of atomics);
 * consecutive phases writing the same y buffer (the early clearing must not fire);
-* TOPK, THRESHOLD and TOPK_GUIDED masks in one step.
+* TOPK, THRESHOLD and TOPK_GUIDED masks in one step;
+* selections concentrated in one wave's channel range per workgroup (the fused kernel's
+  waves then stream columns from each other's lists).
 Masks, lists and counts bit-exact against the oracle; y within relative L2 1e-3.
 """
 
@@ -247,3 +249,27 @@ def test_step_batched_rejects_shared_outputs(env):
     with pytest.raises(spax.SpaxError) as e:
         run_step(env, specs, 405, share_y={1}, flags=2)
     assert "overlap" in str(e.value)
+
+
+def _concentrated_x(d, period, width, seed):
+    """Large activations only on channels j with j % period < width (one wave's range in each
+    column chunk of a 12288-row fused phase); tiny ones elsewhere."""
+    rng = np.random.default_rng(seed)
+    j = np.arange(d)
+    hot = (j % period) < width
+    mag = np.where(hot, 4.0 + rng.exponential(1.0, d), 0.01 * rng.exponential(1.0, d))
+    sign = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    return (sign * mag).astype(np.float16)
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2])
+def test_step_concentrated_selection(env, flags):
+    """Every selected column of a workgroup in one wave's channel range: the fused kernel's
+    waves then take most of their columns from another wave's list."""
+    d = 4096
+    xs = {0: _concentrated_x(d, 410, 26, 11), 1: _concentrated_x(d, 410, 26, 12),
+          2: _concentrated_x(d, 410, 26, 13)}
+    specs = [(d, [4096, 4096, 4096], 0, 128, ("topk", 200 / d, 60 / d)),
+             (d, [4096, 4096, 4096], 1, 128, ("topk", 200 / d, 60 / d)),
+             (d, [4096, 4096, 4096], 0, 128, ("threshold", 1.0, 4.5))]
+    check(run_step(env, specs, 808, flags=flags, xs=xs))
