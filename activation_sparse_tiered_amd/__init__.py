@@ -107,10 +107,14 @@ def spax_gemv_workspace_bytes(layout: Layout) -> int:
     return int(lib.spax_gemv_workspace_bytes(C.byref(layout)))
 
 
-def spax_tiered_gemv(layout: Layout, packed, x, full_idx, approx_idx, counts, y, ws,
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def spax_tiered_gemv(layout: Layout, packed, x, full_idx, approx_idx, counts, y, ws=None,
                      ws_bytes: int | None = None, stream=None) -> None:
     if ws_bytes is None:
-        ws_bytes = ws.numel() * ws.element_size()
+        ws_bytes = _nbytes(ws)
     check(lib.spax_tiered_gemv(C.byref(layout), _ptr(packed), _ptr(x), _ptr(full_idx),
                                _ptr(approx_idx), _ptr(counts), _ptr(y), _ptr(ws), int(ws_bytes),
                                _stream(stream)),
@@ -145,7 +149,7 @@ def spax_tiered_gemv_pinned(layout: Layout, packed_host, x, full_idx, approx_idx
     """The blob in pinned host memory (e.g. a torch tensor with pin_memory=True); returns the
     byte account of the call."""
     if ws_bytes is None:
-        ws_bytes = ws.numel() * ws.element_size()
+        ws_bytes = _nbytes(ws)
     st = MoveStats()
     check(lib.spax_tiered_gemv_pinned(C.byref(layout), _ptr(packed_host), _ptr(x), _ptr(full_idx),
                                       _ptr(approx_idx), _ptr(counts), _ptr(y), int(gap),
@@ -189,7 +193,7 @@ def spax_decode_step_projections(phases, ws, ws_bytes: int | None = None, flags:
     events[2i] -> events[2i+1] then brackets phase i's GEMV launch on the stream."""
     arr = phases if isinstance(phases, C.Array) else phase_array(phases)
     if ws_bytes is None:
-        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+        ws_bytes = _nbytes(ws)
     st = Step()
     st.n_phases = len(arr)
     st.flags = int(flags)
