@@ -323,3 +323,19 @@ def test_phase_array_keeps_its_buffers_alive():
     del arr
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_header_compiles_as_c():
+    """include/spax.h is usable from plain C: the C user of the ABI (tests/c) compiles as C11
+    with every warning an error."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    src = os.path.join(ROOT, "tests", "c", "spax_abi_demo.c")
+    r = subprocess.run(["gcc", "-fsyntax-only", "-std=c11", "-Wall", "-Wextra", "-Werror",
+                        "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+                        f"-I{os.path.join(ROOT, 'include')}", src],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr

@@ -1,5 +1,6 @@
-"""The usage shown in README.md, run as written (torch tensors in, the library does the work)
-and checked against the oracle: masks and lists bit-exact, y within rel-L2 1e-3."""
+"""The library as a user calls it: the usage shown in README.md, run as written (torch
+tensors in, the library does the work) and checked against the oracle (masks and lists
+bit-exact, y within rel-L2 1e-3); and a plain-C program that uses the C ABI directly."""
 
 import math
 
@@ -49,3 +50,20 @@ def test_readme_usage():
     got = y.cpu().numpy().astype(np.float64)
     assert np.linalg.norm(got - ref) <= 1e-3 * np.linalg.norm(ref)
     assert math.isfinite(float(np.abs(got).max()))
+
+
+def test_c_abi_demo():
+    """A plain-C program (tests/c/spax_abi_demo.c, no Python, no torch) packs, masks and
+    multiplies through the C ABI and checks the dense product exactly, the TopK counts and
+    lists, and the validation of a NULL pointer."""
+    import os
+    import subprocess
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import __graft_entry__ as ge
+    exe = ge.C_DEMO_BIN if os.path.exists(ge.C_DEMO_BIN) else ge.build_c_demo()
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "spax C ABI demo: ok" in r.stdout
