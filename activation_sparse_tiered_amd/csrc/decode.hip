@@ -116,28 +116,39 @@ __device__ __forceinline__ int claim_entries(int (*q)[kFusedWaves], int t, int w
   return 0;
 }
 
-// Channels j in [begin, end) whose key is kb0 / kb1 (begin a multiple of 8; eight keys per
-// lane and LDS read).  One wave; the result is wave-uniform.
-__device__ __forceinline__ void ties_between(const uint32_t* xs32, int begin, int end, int kb0,
-                                             int kb1, int lane, int& t0, int& t1) {
-  int c0 = 0, c1 = 0;
+// How many of the two fp16 halves of an LDS word of x have key (bits & 0x7FFF) kb, where
+// kb2 = kb in both halves; only the first nv (0, 1 or 2) halves count.  XOR with kb2 leaves
+// a half zero exactly where the key equals kb (a key never has its top bit set).
+__device__ __forceinline__ int equal_halves(uint32_t wd, uint32_t kb2, int nv) {
+  const uint32_t t = (wd & 0x7FFF7FFFu) ^ kb2;
+  return (nv > 0 && (t & 0xFFFFu) == 0u ? 1 : 0) + (nv > 1 && t < 0x10000u ? 1 : 0);
+}
+
+// Channels j in [begin, end) whose key is kb (begin even; eight keys per lane and LDS read).
+// One wave; the result is wave-uniform.
+__device__ __forceinline__ int ties_between(const uint32_t* xs32, int begin, int end, int kb,
+                                            int lane) {
+  const uint32_t kb2 = (uint32_t)kb * 0x10001u;
+  int c = 0;
   const uint4* x4 = reinterpret_cast<const uint4*>(xs32);
   for (int base = begin; base < end; base += 512) {
     const int j = base + 8 * lane;
     if (j < end) {
       const uint4 v = x4[j >> 3];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = (int)(((e & 1) ? w[e >> 1] >> 16 : w[e >> 1]) & 0x7FFFu);
-        const bool in = j + e < end;
-        c0 += in && key == kb0;
-        c1 += in && key == kb1;
-      }
+      c += equal_halves(v.x, kb2, end - j) + equal_halves(v.y, kb2, end - j - 2) +
+           equal_halves(v.z, kb2, end - j - 4) + equal_halves(v.w, kb2, end - j - 6);
     }
   }
-  t0 = mask::wave_sum(c0);
-  t1 = mask::wave_sum(c1);
+  return mask::wave_sum(c);
+}
+
+// Channels of this wave's mask-pass range (select_begin's k) whose key is kb.
+__device__ __forceinline__ int ties_in_range(const mask::Keys& k, int kb, int lane) {
+  const uint32_t kb2 = (uint32_t)kb * 0x10001u;
+  int c = 0;
+  for (int s = 0; s < k.steps; ++s)
+    c += equal_halves(k.word(s, lane), kb2, k.n - k.off(s, lane, 0));
+  return c;
 }
 
 // One group: mask and GEMV.  Workgroup gridDim.x - 1 only writes the outputs of the mask
@@ -242,16 +253,11 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   // ---- 2. this wave's tiers and column lists
   bool need0 = s0.m < E[0], need1 = s1.m < E[1];  // the boundary keeps some of its ties only
   if (need0 || need1) {
-    // equal keys per mask-pass wave range (C channels each), for the tie bases below
+    // equal keys per mask-pass wave range (C channels each), for the tie bases below; only
+    // for the boundaries that split their ties (uniform branches)
     int c = 0;
-    for (int s = 0; s < k.steps; ++s) {
-      const uint32_t wd = k.word(s, lane);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int key = k.valid(s, lane, e) ? (int)((e ? wd >> 16 : wd) & 0x7FFFu) : -1;
-        c += (key == s0.kb ? 1 : 0) + (key == s1.kb ? 0x10000 : 0);
-      }
-    }
+    if (need0) c += ties_in_range(k, s0.kb, lane);
+    if (need1) c += ties_in_range(k, s1.kb, lane) << 16;
     c = mask::wave_sum(c);
     if (lane == 0) u.kh.wave_ties[wave] = c;
     __syncthreads();  // uniform: need0 / need1 are the same on every wave
@@ -270,10 +276,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     // equal keys before ws: whole mask-pass ranges, then the rest of the one holding ws
     const int gw = ws / k.C;
     const int c = mask::wave_sum(lane < gw ? u.kh.wave_ties[lane] : 0);
-    int p0 = 0, p1 = 0;
-    ties_between(xs32, gw * k.C, ws, s0.kb, s1.kb, lane, p0, p1);
-    ties0 = (c & 0xFFFF) + p0;
-    ties1 = (c >> 16) + p1;
+    ties0 = (c & 0xFFFF) + (need0 ? ties_between(xs32, gw * k.C, ws, s0.kb, lane) : 0);
+    ties1 = (c >> 16) + (need1 ? ties_between(xs32, gw * k.C, ws, s1.kb, lane) : 0);
   }
   int nF = 0, nA = 0, ne = 0;
   for (int j0 = ws; j0 < we; j0 += 64) {
