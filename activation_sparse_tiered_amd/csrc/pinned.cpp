@@ -142,12 +142,15 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
   uint32_t* d_listA = d_listF + d;
   int32_t* d_colF = reinterpret_cast<int32_t*>(d_listA + d);
   int32_t* d_colA = d_colF + d;
-  if (nF) SPAX_HIP_CHECK(hipMemcpyAsync(d_listF, h_outF, 4 * (size_t)nF, hipMemcpyHostToDevice, s));
-  if (nA) SPAX_HIP_CHECK(hipMemcpyAsync(d_listA, h_outA, 4 * (size_t)nA, hipMemcpyHostToDevice, s));
-  if (gather) {
-    if (slotsF) SPAX_HIP_CHECK(hipMemcpyAsync(d_colF, h_colF, 4 * (size_t)slotsF, hipMemcpyHostToDevice, s));
-    if (slotsA) SPAX_HIP_CHECK(hipMemcpyAsync(d_colA, h_colA, 4 * (size_t)slotsA, hipMemcpyHostToDevice, s));
-  }
+  // The host tables and their device copies have the same layout (four arrays of d entries:
+  // FULL list, APPROX list, FULL slot columns, APPROX slot columns), so one upload of the span
+  // that holds the used entries replaces four (each upload costs more to enqueue than to move).
+  size_t words = 0;
+  if (nF) words = (size_t)nF;
+  if (nA) words = (size_t)d + (size_t)nA;
+  if (gather && slotsF) words = 2 * (size_t)d + (size_t)slotsF;
+  if (gather && slotsA) words = 3 * (size_t)d + (size_t)slotsA;
+  if (words) SPAX_HIP_CHECK(hipMemcpyAsync(d_listF, h_outF, 4 * words, hipMemcpyHostToDevice, s));
   SPAX_HIP_CHECK(hipEventRecord(sc.done, s));
   sc.pending = true;
   if (gather) {
@@ -162,7 +165,7 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
   if (stats) {
     stats->selected_bytes = (int64_t)nF * L->stride_F + (int64_t)nA * L->stride_A;
     stats->moved_bytes = moved;
-    stats->list_bytes = 4 * (int64_t)(nF + nA);
+    stats->list_bytes = 4 * (int64_t)words;
     stats->n_ranges = n_ranges;
     stats->n_full = nF;
     stats->n_approx = nA;

@@ -215,7 +215,10 @@ int spax_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* firs
 typedef struct spax_move_stats {
   int64_t selected_bytes;  /* n_full * stride_F + n_approx * stride_A                   */
   int64_t moved_bytes;     /* record bytes copied host -> device (selected + merged gaps) */
-  int64_t list_bytes;      /* compacted list bytes copied host -> device                 */
+  int64_t list_bytes;      /* list bytes copied host -> device: one upload of the span of
+                              the host tables (FULL and APPROX compacted entries, then for
+                              the gather transfer the FULL and APPROX slot -> column tables;
+                              d_in entries each) that holds every used entry              */
   int32_t n_ranges;        /* record copies enqueued (FULL ranges + APPROX ranges)       */
   int32_t n_full, n_approx;
   int32_t reserved0;

@@ -86,11 +86,30 @@ def test_pinned_matches_oracle_and_device_path(env, fmt, G, gap, transfer):
     assert rel_l2(y_pin, ref) <= REL_L2
     assert rel_l2(y_pin, y_dev.cpu().numpy()) <= 1e-6
     led = orng.ledger(wf, wa, O.stride_F, O.stride_A, gap)
+    led["n_full"], led["n_approx"] = len(wf), len(wa)
     assert st.n_full == len(wf) and st.n_approx == len(wa)
     assert st.selected_bytes == led["selected_bytes"]
     assert st.moved_bytes == led["moved_bytes"]
     assert st.n_ranges == led["n_ranges"]
-    assert st.list_bytes == 4 * (len(wf) + len(wa))
+    assert st.list_bytes == expected_upload(d_in, led, transfer)
+
+
+def expected_upload(d, led, transfer):
+    """Bytes of the one list upload: the four host tables (FULL entries, APPROX entries, FULL
+    slot columns, APPROX slot columns; d entries each) up to the last one in use."""
+    nf = sum(c for _, c in led["ranges_full"])   # staging slots: columns moved, gaps included
+    na = sum(c for _, c in led["ranges_approx"])
+    lf, la = led["n_full"], led["n_approx"]
+    words = 0
+    if lf:
+        words = lf
+    if la:
+        words = d + la
+    if transfer == 1 and nf:
+        words = 2 * d + nf
+    if transfer == 1 and na:
+        words = 3 * d + na
+    return 4 * words
 
 
 @pytest.mark.parametrize("transfer", [0, 1])
