@@ -236,17 +236,29 @@ class Stack:
         return ms, counts
 
 
+# The sources the fused decode kernel is compiled from: its recorded byte counters stay valid
+# while these are unchanged (comments aside).
+KERNEL_SOURCES = [os.path.join(ROOT, "activation_sparse_tiered_amd", "csrc", f)
+                  for f in ("decode.hip", "gemv_core.h", "mask_core.h", "common.h")] + \
+                 [os.path.join(ROOT, "include", "spax.h")]
+
+
+def _strip_c_comments(text: str) -> str:
+    """C/C++ source without its comments (block and line), string literals kept."""
+    import re
+    pat = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"', re.S)
+    return pat.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+
+
 def sources_sha256():
-    """sha256 over the kernel sources and the C header (name, then bytes; sorted by path)."""
-    import glob
+    """sha256 over the fused kernel's sources without their comments (name, then text; in
+    the order of KERNEL_SOURCES)."""
     import hashlib
-    files = sorted(glob.glob(os.path.join(ROOT, "activation_sparse_tiered_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "spax.h"))
     h = hashlib.sha256()
-    for f in files:
+    for f in KERNEL_SOURCES:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_strip_c_comments(fh.read()).encode())
     return h.hexdigest()
 
 

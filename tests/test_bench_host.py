@@ -69,3 +69,14 @@ def test_recorded_traffic_only_for_its_own_workload():
 def test_sources_hash_is_stable():
     assert bench.sources_sha256() == bench.sources_sha256()
     assert len(bench.sources_sha256()) == 64
+    assert all(os.path.exists(f) for f in bench.KERNEL_SOURCES)
+
+
+def test_comment_edits_leave_the_sources_hash_alone():
+    a = 'int f(int x) { return x + 1; }  // add one\n/* note */ const char* s = "/* kept */";'
+    b = 'int f(int x) { return x + 1; }  // plus one\n/* other note */ const char* s = "/* kept */";'
+    c = 'int f(int x) { return x + 2; }  // add one\n/* note */ const char* s = "/* kept */";'
+    strip = bench._strip_c_comments
+    assert strip(a) == strip(b)
+    assert strip(a) != strip(c)
+    assert '"/* kept */"' in strip(a)
