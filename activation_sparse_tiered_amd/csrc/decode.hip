@@ -20,6 +20,7 @@
 // y of a group is accumulated with fp32 atomics and must start at zero: the mask kernel (or,
 // fused, the previous launch, spread over its workgroups) clears it; otherwise a small
 // kernel does.
+#include <atomic>
 #include <climits>
 #include <cstdlib>
 
@@ -361,18 +362,19 @@ struct FusedLds {
   size_t bytes;
 };
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; calls from several host threads
+// may fill an entry at once, with the same value).
 int cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // Fused grid: the 512-row tiles times as many column chunks as fill one workgroup per

@@ -5,6 +5,8 @@
 // checked.  Two launch shapes, picked by size (measured on MI355X): a large read goes best
 // as one contiguous chunk per workgroup, one workgroup per compute unit; a read of tens of
 // MB, as one launch among many, ends soonest grid-stride over four workgroups per unit.
+#include <atomic>
+
 #include "common.h"
 
 namespace spax {
@@ -49,15 +51,15 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* 
 }
 
 int probe_cus() {
-  static int cache[kProbeMaxDevices] = {0};
+  static std::atomic<int> cache[kProbeMaxDevices];  // filled once per device, same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  int cus = dev < kProbeMaxDevices ? cache[dev] : 0;
+  int cus = dev < kProbeMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
   if (cus <= 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
       cus = 256;
-    if (dev < kProbeMaxDevices) cache[dev] = cus;
+    if (dev < kProbeMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
   }
   return cus;
 }
