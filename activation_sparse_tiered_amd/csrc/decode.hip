@@ -77,10 +77,6 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-#ifndef SPAX_SHARE_LISTS
-#define SPAX_SHARE_LISTS 1
-#endif
-
 // The next up to kUnroll entries of tier t (0 FULL, 1 APPROX) for this wave from the column
 // lists of its workgroup: from its own list while that has entries left, else from the next
 // wave's list (in wave order) that has.  q = KeyHist::lists_q; lane v reads wave v's counter
@@ -314,43 +310,37 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
   float zsum = 0.0f;
   if (kUseEarly) early.multiply(acc, zsum);
-  if (SPAX_SHARE_LISTS) {
-    // The waves' lists are shared out: a wave streams its own list and then helps the
-    // others, so the workgroup ends with its average wave rather than its longest list.
-    // Publishing: the entries are written before the count (release), a claim reads the
-    // count before the entries (acquire).
-    // The wave keeps its first round for itself: its counters start past those entries, set
-    // before the lengths are published, so no claim is needed to start.
-    int nf = min(nF, gemv::kUnroll), na = min(nA, gemv::kUnroll);
-    int bF = wave * 2 * S, bA = wave * 2 * S + S;
-    if (lane == 0) {
-      __hip_atomic_store(&u.kh.lists_q[0][wave], nf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_store(&u.kh.lists_q[1][wave], na, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (lane == 0) {
-      __hip_atomic_store(&u.kh.lists_q[2][wave], nF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_store(&u.kh.lists_q[3][wave], nA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    const uint32_t* lists = reinterpret_cast<const uint32_t*>(dyn + a.xs_bytes);
-    const gemv::TileOffsets<FMT> g(sh, row);
-    while (nf > 0 || na > 0) {
-      gemv::RoundLoads<FMT> r;
-      gemv::issue_round<FMT>(sh, a.packed, g, gemv::LdsBlock(lists + bF, nf, jmax), 0, nf,
-                             gemv::LdsBlock(lists + bA, na, jmax), 0, na, r);
-      // the next claims overlap this round's loads
-      int nbF = bF, nbA = bA;
-      const int nf2 = claim_entries(u.kh.lists_q, 0, wave, S, lane, nbF);
-      const int na2 = claim_entries(u.kh.lists_q, 1, wave, S, lane, nbA);
-      gemv::finish_round<FMT>(r, g, nf, na, acc, zsum);
-      nf = nf2;
-      na = na2;
-      bF = nbF;
-      bA = nbA;
-    }
-  } else {
-    gemv::stream_columns<FMT>(sh, a.packed, row, 0, nF, gemv::LdsList{lF, 0, jmax}, 0, nA,
-                              gemv::LdsList{lA, 0, jmax}, acc, zsum);
+  // The waves' lists are shared out: a wave streams its own list and then helps the others,
+  // so the workgroup ends with its average wave rather than its longest list.  A wave keeps
+  // its first round for itself: its counters start past those entries and are set before
+  // the lengths are published, so no claim is needed to start.  The entries are written
+  // before the lengths (release); a claim reads a length before the entries (acquire).
+  int nf = min(nF, gemv::kUnroll), na = min(nA, gemv::kUnroll);
+  int bF = wave * 2 * S, bA = wave * 2 * S + S;
+  if (lane == 0) {
+    __hip_atomic_store(&u.kh.lists_q[0][wave], nf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&u.kh.lists_q[1][wave], na, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane == 0) {
+    __hip_atomic_store(&u.kh.lists_q[2][wave], nF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&u.kh.lists_q[3][wave], nA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  const uint32_t* lists = reinterpret_cast<const uint32_t*>(dyn + a.xs_bytes);
+  const gemv::TileOffsets<FMT> g(sh, row);
+  while (nf > 0 || na > 0) {
+    gemv::RoundLoads<FMT> r;
+    gemv::issue_round<FMT>(sh, a.packed, g, gemv::LdsBlock(lists + bF, nf, jmax), 0, nf,
+                           gemv::LdsBlock(lists + bA, na, jmax), 0, na, r);
+    // the next claims overlap this round's loads
+    int nbF = bF, nbA = bA;
+    const int nf2 = claim_entries(u.kh.lists_q, 0, wave, S, lane, nbF);
+    const int na2 = claim_entries(u.kh.lists_q, 1, wave, S, lane, nbA);
+    gemv::finish_round<FMT>(r, g, nf, na, acc, zsum);
+    nf = nf2;
+    na = na2;
+    bF = nbF;
+    bA = nbA;
   }
   __syncthreads();  // every wave is done with the mask scratch that `red` overlays
   gemv::finish_tile<kFusedWaves>(u.red, acc, zsum, wave, lane, row0, T, sh.n_chunks, a.y);

@@ -220,23 +220,11 @@ __device__ __forceinline__ void load_blocks(const void* __restrict__ idxF,
   ba = RegBlock{iA < aend ? sA | (xA << 16) : 0u, ai};
 }
 
-// Column lists in LDS (fused kernel): entry = channel | (fp16 bits of x_j) << 16, indexed
-// from the workgroup's first rank `base`.  The channel is clamped to [0, d_in) like the
-// global lists, so a corrupted entry can never address outside the blob.
-struct LdsList {
-  const uint32_t* e;
-  int base;
-  uint32_t jmax;
-  __device__ __forceinline__ void get(int i, int& j, float& xv) const {
-    const uint32_t v = __builtin_amdgcn_readfirstlane(e[i - base]);
-    j = (int)min(v & 0xFFFFu, jmax);
-    xv = half_hi(v);
-  }
-};
-
-// Up to 64 consecutive LDS list entries (as in LdsList) held one per lane: one LDS read for
-// the wave instead of one read and wait per column; get() broadcasts entry i with readlane.
-// Lanes past n read entry n - 1 (entry 0 when n <= 0), so p must hold at least one entry.
+// Column lists in LDS (fused kernel): entry = channel | (fp16 bits of x_j) << 16.  Up to 64
+// consecutive entries are held one per lane: one LDS read for the wave instead of one read
+// and wait per column; get() broadcasts entry i with readlane.  Lanes past n read entry n - 1
+// (entry 0 when n <= 0), so p must hold at least one entry.  The channel is clamped to
+// [0, d_in) like the global lists, so a corrupted entry can never address outside the blob.
 struct LdsBlock {
   uint32_t e;
   uint32_t jmax;
@@ -253,7 +241,7 @@ struct LdsBlock {
 
 // Up to P FULL columns whose loads are issued ahead of the rest of the work and multiplied
 // later (the fused decode kernel issues them while its mask is still being completed, so
-// their memory latency overlaps that work).  Entries as in LdsList.  All P loads are issued
+// their memory latency overlaps that work).  Entries as in LdsBlock.  All P loads are issued
 // (a conditional load would make the compiler copy its result right away, which waits for
 // it): slots past n load the entry the caller put there (a repeat of a used column, which
 // costs no extra HBM traffic, or column 0) and are multiplied by a zero activation.
