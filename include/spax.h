@@ -287,7 +287,8 @@ typedef struct spax_phase {
 enum {
   /* one fused mask+GEMV launch per phase whose d_in <= 16384 (and whose lists fit in LDS):
    * one 1024-thread workgroup per compute unit, each finding the boundaries itself; other
-   * phases take the two launches of SPAX_STEP_SEPARATE.  Same outputs either way. */
+   * phases take the two launches of SPAX_STEP_SEPARATE.  Same outputs either way.  Kernel
+   * launches only (no copy, no memset), so the step can be captured into a HIP graph. */
   SPAX_STEP_DEFAULT = 0,
   /* one stand-alone mask launch (spax_build_tiers' kernel, which also clears y) and one
    * GEMV launch (spax_tiered_gemv's kernel) per phase */

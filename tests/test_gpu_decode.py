@@ -8,7 +8,8 @@ one launch, all GEMVs in one launch) wherever the phases are independent.
 * consecutive phases writing the same y buffer (the early clearing must not fire);
 * TOPK, THRESHOLD and TOPK_GUIDED masks in one step;
 * selections concentrated in one wave's channel range per workgroup (the fused kernel's
-  waves then stream columns from each other's lists).
+  waves then stream columns from each other's lists);
+* the default step captured into a HIP graph and replayed.
 Masks, lists and counts bit-exact against the oracle; y within relative L2 1e-3.
 """
 
@@ -273,3 +274,49 @@ def test_step_concentrated_selection(env, flags):
              (d, [4096, 4096, 4096], 1, 128, ("topk", 200 / d, 60 / d)),
              (d, [4096, 4096, 4096], 0, 128, ("threshold", 1.0, 4.5))]
     check(run_step(env, specs, 808, flags=flags, xs=xs))
+
+
+def test_step_graph_capture_replays(env):
+    """The default step (fused launches, plus the clearing launch of the first y) captured into
+    a HIP graph through torch and replayed several times, with eager work between the replays:
+    every replay gives the eager step's masks, lists and counts bit for bit and its y within
+    the atomics' reordering (the graph holds no memset and no host copy)."""
+    torch, spax, dev = env
+    specs = [(4096, [1024, 512, 512], 0, 128, ("guided", 0.5, 0.01)),
+             (2048, [2048], 1, 128, ("topk", 0.25, 0.35)),
+             (3000, [1024], 0, 64, ("threshold", 0.6, 1.4))]
+    keep = run_step(env, specs, 909, flags=0)
+    check(keep)
+    want = [dict((k, b[k].clone()) for k in ("tier", "f", "a", "c", "y")) for *_, b in keep]
+    phases = [spax.make_phase(L, packed, b["x"], _params(spax, oa), b["tier"], b["f"], b["a"],
+                              b["c"], b["y"]) for (L, O, Ws, x16, oa, packed, b) in keep]
+    arr = spax.phase_array(phases)
+    ws = torch.zeros(max(1, spax.spax_step_workspace_bytes(arr)), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        spax.spax_decode_step_projections(arr, ws, flags=0)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        spax.spax_decode_step_projections(arr, ws, flags=0)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for *_, b in keep:  # clobber every output, eagerly, between replays
+            b["tier"].fill_(0xAB)
+            b["f"].fill_(-7)
+            b["a"].fill_(-7)
+            b["c"].fill_(-7)
+            b["y"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, ((*_, b), w) in enumerate(zip(keep, want)):
+            c = w["c"].cpu().numpy()
+            assert torch.equal(b["c"], w["c"]), (rep, i)
+            assert torch.equal(b["tier"], w["tier"]), (rep, i)
+            assert torch.equal(b["f"][:c[0]], w["f"][:c[0]]), (rep, i)
+            assert torch.equal(b["a"][:c[1]], w["a"][:c[1]]), (rep, i)
+            err = rel_l2(b["y"].cpu().numpy(), w["y"].cpu().numpy())
+            assert err <= 1e-6, (rep, i, err)
