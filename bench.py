@@ -36,6 +36,8 @@ streaming read (spax_read_probe) gets: its rate on one large read (also reported
 ``roofline`` as a measured second denominator) and the time of the step's launch pattern
 when every launch only reads its selected byte count (a floor for the layer-serial form).
 For linear512 and mlp7b ``cpu_baseline`` also holds a one-thread run of the oracle.
+``dense_baseline`` (fp16 workloads) times the same step without tiers through torch's fp16
+matrix-vector product on the same weights, as context for the speedup over dense decoding.
 """
 
 from __future__ import annotations
@@ -81,6 +83,8 @@ def parse():
                     help="skip timing the batched step form")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the plain streaming-read ceiling and floor")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense fp16 baseline (torch matmul on the same weights)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="before the timed steps, run one elementwise kernel (bitwise_not) that "
                          "reads and writes this many MiB: known traffic for scaling hardware "
@@ -388,6 +392,43 @@ def read_probe(spax, torch, dev, launch_bytes, reps=8):
                     "each reading that launch's selected byte count"}
 
 
+def dense_baseline(stack, reps=10):
+    """The same step without tiers, as context for the speedup over dense decoding: per phase
+    one torch fp16 matrix-vector product (the vendor BLAS) of the phase's dense weights with
+    the activation vector, W [sum d_out, d_in] (the matrices of a phase stacked, row-major:
+    of the layouts and calls tried, torch.mv on this one was the fastest) times x [d_in]; the
+    dense weights of every layer resident in HBM, phases in order on one stream."""
+    torch, dev, spec = stack.torch, stack.dev, stack.spec
+    Ws, xs = [], []
+    for l in range(stack.layers):
+        for k, (name, d_in, d_out) in enumerate(stack.shapes):
+            Ws.append(torch.cat([synth.weights_device(SEED, d_in, r, dev, l, k, m)
+                                 for m, r in enumerate(d_out)], dim=1).t().contiguous())
+            xs.append(stack.x[0][l * len(stack.shapes) + k])
+    dense_bytes = sum(w.numel() * 2 for w in Ws)
+
+    def step():
+        for w, x in zip(Ws, xs):
+            torch.mv(w, x)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps / spec["tokens_per_step"]
+    del Ws
+    return {"value": round(us, 2), "unit": "us/token",
+            "GBps": round(dense_bytes / spec["tokens_per_step"] / (us * 1e-6) / 1e9, 1),
+            "dense_GB_per_token": round(dense_bytes / spec["tokens_per_step"] / 1e9, 4),
+            "kind": "torch.mv in fp16 per phase (W [sum d_out, d_in] row-major times x), "
+                    "dense weights in HBM, same shapes and weights, phases in order"}
+
+
 def device_bench(args, spax, torch, dev):
     spec = workload_spec(args)
     per_tok = spec["tokens_per_step"]
@@ -492,6 +533,14 @@ def device_bench(args, spax, torch, dev):
                            "independent"}
         log(f"[bench] batched step: {bt_ms * 1e3:.1f} us, {bgbs:.1f} GB/s")
 
+    dense = None
+    if not args.no_dense and spec["fmt"] == 0 and args.control == "none":
+        dense = dense_baseline(stack)
+        dense["speedup_layer_serial"] = round(dense["value"] / (step_ms * 1e3 / per_tok), 3)
+        if batched is not None:
+            dense["speedup_batched"] = round(dense["value"] / batched["value"], 3)
+        log(f"[bench] dense baseline {dense}")
+
     probe = None
     if not args.no_read_probe:
         probe = read_probe(spax, torch, dev, launch_bytes)
@@ -537,6 +586,7 @@ def device_bench(args, spax, torch, dev):
         "batched": batched,
         "token_us": token_us,
         "read_probe": probe,
+        "dense_baseline": dense,
     }
 
 
