@@ -8,8 +8,9 @@
 // Every workgroup loads the activation vector into LDS and finds the two tier boundaries
 // from a per-key histogram (mask_core.h, select_begin / select_finish), decides the tiers of
 // its own range of input channels, lists those columns in LDS (channel | fp16 x_j << 16 per
-// entry) and streams them for its 512-row tile (gemv_core.h).  One extra workgroup writes the tier bytes, the
-// ascending lists and the counts with the rank-producing mask code, so the outputs equal
+// entry, one list per wave and tier, shared out among the waves) and streams them for its
+// 512-row tile (gemv_core.h).  One extra workgroup writes the tier bytes, the ascending
+// lists and the counts with the rank-producing mask code, so the outputs equal
 // those of spax_build_tiers.  Repeating the boundary search in every workgroup costs no time
 // (it runs in parallel on separate compute units) and removes the second launch and the
 // counts -> indices -> activations chain of dependent global loads.  With
@@ -158,7 +159,8 @@ __device__ __forceinline__ int ties_in_range(const mask::Keys& k, int kb, int la
 //   2. each wave decides the tiers of its channels (ties at a boundary key by channel order,
 //      counting the equal keys before its first channel only when it holds such a tie) and
 //      lists its FULL and APPROX columns in LDS;
-//   3. each wave multiplies its early columns and streams the others; the tile is reduced
+//   3. each wave multiplies its early columns, streams its own list and then takes columns
+//      from the other waves' lists until all are done (claim_entries); the tile is reduced
 //      across waves and added to y.
 template <int FMT, int MAXD>
 __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a) {
