@@ -248,10 +248,13 @@ KERNEL_SOURCES = [os.path.join(ROOT, "activation_sparse_tiered_amd", "csrc", f)
 
 
 def _strip_c_comments(text: str) -> str:
-    """C/C++ source without its comments (block and line), string literals kept."""
+    """C/C++ source without its comments (block and line; string literals kept), every run of
+    white space reduced to one space, so that rewording or rewrapping a comment leaves it
+    unchanged."""
     import re
     pat = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"', re.S)
-    return pat.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    code = pat.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return " ".join(code.split())
 
 
 def sources_sha256():

@@ -77,6 +77,7 @@ def test_comment_edits_leave_the_sources_hash_alone():
     b = 'int f(int x) { return x + 1; }  // plus one\n/* other note */ const char* s = "/* kept */";'
     c = 'int f(int x) { return x + 2; }  // add one\n/* note */ const char* s = "/* kept */";'
     strip = bench._strip_c_comments
-    assert strip(a) == strip(b)
+    d = 'int f(int x) {\n  return x + 1;\n}\n// add\n// one\nconst char* s = "/* kept */";'
+    assert strip(a) == strip(b) == strip(d)
     assert strip(a) != strip(c)
     assert '"/* kept */"' in strip(a)
