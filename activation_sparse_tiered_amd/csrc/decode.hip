@@ -140,15 +140,6 @@ __device__ __forceinline__ int ties_between(const uint32_t* xs32, int begin, int
   return mask::wave_sum(c);
 }
 
-// Channels of this wave's mask-pass range (select_begin's k) whose key is kb.
-__device__ __forceinline__ int ties_in_range(const mask::Keys& k, int kb, int lane) {
-  const uint32_t kb2 = (uint32_t)kb * 0x10001u;
-  int c = 0;
-  for (int s = 0; s < k.steps; ++s)
-    c += equal_halves(k.word(s, lane), kb2, k.n - k.off(s, lane, 0));
-  return c;
-}
-
 // One group: mask and GEMV.  Workgroup gridDim.x - 1 only writes the outputs of the mask
 // (build_plan + emit, as the stand-alone mask kernel).  Every other workgroup owns one
 // 512-row tile and one contiguous range of input channels, split over its 16 waves:
@@ -252,15 +243,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   // ---- 2. this wave's tiers and column lists
   bool need0 = s0.m < E[0], need1 = s1.m < E[1];  // the boundary keeps some of its ties only
   if (need0 || need1) {
-    // equal keys per mask-pass wave range (C channels each), for the tie bases below; only
-    // for the boundaries that split their ties (uniform branches)
-    int c = 0;
-    if (need0) c += ties_in_range(k, s0.kb, lane);
-    if (need1) c += ties_in_range(k, s1.kb, lane) << 16;
-    c = mask::wave_sum(c);
-    if (lane == 0) u.kh.wave_ties[wave] = c;
-    __syncthreads();  // uniform: need0 / need1 are the same on every wave
-    bool here0 = false, here1 = false;
+    bool here0 = false, here1 = false;  // this wave holds a channel at that boundary key
     for (int j0 = ws; j0 < we; j0 += 64) {
       const int j = j0 + lane;
       const int key = j < we ? (int)(xs16[j] & 0x7FFFu) : -1;
@@ -270,14 +253,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     need0 = need0 && here0;
     need1 = need1 && here1;
   }
-  int ties0 = 0, ties1 = 0;
-  if (need0 || need1) {
-    // equal keys before ws: whole mask-pass ranges, then the rest of the one holding ws
-    const int gw = ws / k.C;
-    const int c = mask::wave_sum(lane < gw ? u.kh.wave_ties[lane] : 0);
-    ties0 = (c & 0xFFFF) + (need0 ? ties_between(xs32, gw * k.C, ws, s0.kb, lane) : 0);
-    ties1 = (c >> 16) + (need1 ? ties_between(xs32, gw * k.C, ws, s1.kb, lane) : 0);
-  }
+  // Channels before ws at a split boundary key: counted by the few waves that hold such a
+  // channel, each over x[0, ws) in LDS, so the others go on with no barrier.
+  int ties0 = need0 ? ties_between(xs32, 0, ws, s0.kb, lane) : 0;
+  int ties1 = need1 ? ties_between(xs32, 0, ws, s1.kb, lane) : 0;
   int nF = 0, nA = 0, ne = 0;
   for (int j0 = ws; j0 < we; j0 += 64) {
     const int j = j0 + lane;

@@ -366,7 +366,6 @@ struct KeyHist {
   alignas(16) uint32_t fine[16384];  // count of key 2i in bits 0..15, of key 2i + 1 in 16..31
   alignas(16) int coarse[1024];      // channels with key in [32c, 32c + 32)
   int wave_nat[W];
-  int wave_ties[W];  // per mask-pass wave range: channels at boundary key 0 | key 1 << 16
   // For a caller that shares out column lists among its waves after the search: per wave,
   // the next unclaimed FULL / APPROX entry ([0], [1]) and the published list lengths ([2],
   // [3]); zeroed by select_begin before its first barrier.
