@@ -145,16 +145,17 @@ PINNED_MEMCPY, PINNED_GATHER = 0, 1
 
 def spax_tiered_gemv_pinned(layout: Layout, packed_host, x, full_idx, approx_idx, counts, y,
                             gap: int, ws, ws_bytes: int | None = None, stream=None,
-                            transfer: int = PINNED_MEMCPY) -> MoveStats:
+                            transfer: int = PINNED_MEMCPY, stats: bool = True):
     """The blob in pinned host memory (e.g. a torch tensor with pin_memory=True); returns the
-    byte account of the call."""
+    byte account of the call (MoveStats), or None with stats=False (the gather transfer then
+    does not wait for the device)."""
     if ws_bytes is None:
         ws_bytes = _nbytes(ws)
-    st = MoveStats()
+    st = MoveStats() if stats else None
     check(lib.spax_tiered_gemv_pinned(C.byref(layout), _ptr(packed_host), _ptr(x), _ptr(full_idx),
                                       _ptr(approx_idx), _ptr(counts), _ptr(y), int(gap),
-                                      int(transfer), _ptr(ws), int(ws_bytes), C.byref(st),
-                                      _stream(stream)),
+                                      int(transfer), _ptr(ws), int(ws_bytes),
+                                      C.byref(st) if st is not None else None, _stream(stream)),
           "spax_tiered_gemv_pinned")
     return st
 

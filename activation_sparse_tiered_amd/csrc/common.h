@@ -94,11 +94,14 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
                        const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
                        const int32_t* counts, float* y, int32_t gap, int32_t transfer, void* ws,
                        spax_move_stats* stats, hipStream_t s);
-// Copy kernel: staging slot t of region F (A) <- record colF[t] (colA[t]) of the mapped blob.
-int launch_gather_records(const spax_layout* L, const void* host_dev, void* staging,
-                          const int32_t* colF, int32_t nF_slots, const int32_t* colA,
-                          int32_t nA_slots, hipStream_t s);
-
+// Pinned-host gather transfer with the ranges merged on the device: merge_ranges_kernel (two
+// workgroups) writes the compacted lists, the slot tables and totals[6] = {slots F, slots A,
+// ranges F, ranges A, entries F, entries A}; then one gather launch sized for the largest
+// possible move reads the slot counts from totals.
+int launch_merge_and_gather(const spax_layout* L, const void* host_dev, void* staging,
+                            const int32_t* full_idx, const int32_t* approx_idx,
+                            const int32_t* counts, int32_t gap, uint32_t* listF, uint32_t* listA,
+                            int32_t* colF, int32_t* colA, int32_t* totals, hipStream_t s);
 // y_zeroed: y already holds zeros (stream-ordered); otherwise a zero fill is enqueued first
 // whenever the plan splits K.
 // compact: the lists hold slot | channel << 16 entries into a compacted staging copy of the

@@ -34,12 +34,91 @@ __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
                                  red);
 }
 
+// Range merging on the device (pinned-host path, gather transfer): workgroup r merges region
+// r's list (0 FULL, 1 APPROX) into runs of channels whose gaps are at most `gap` unselected
+// channels, and writes what the host merge would: the compacted entries (staging slot |
+// channel << 16), the slot -> channel table and the totals.  Entry i contributes the columns
+// from its channel up to (not including) the next entry of its run, or just its own column
+// when it ends the run; its slot is the exclusive prefix sum of those contributions, so the
+// columns of a run land in consecutive slots and runs follow each other.  Each thread takes
+// a contiguous share of the entries; one block-wide scan gives the prefixes.  Lists that
+// are not strictly ascending start a new run at every descent and stay memory-safe (slots
+// and table writes are kept below d), with an unspecified y.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeWaves = kMergeThreads / 64;
+
+__device__ __forceinline__ int merge_wave_scan(int x) {  // inclusive, DPP
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void merge_ranges_kernel(
+    const int32_t* __restrict__ full_idx, const int32_t* __restrict__ approx_idx,
+    const int32_t* __restrict__ counts, int32_t d, int32_t gap, uint32_t* __restrict__ listF,
+    uint32_t* __restrict__ listA, int32_t* __restrict__ colF, int32_t* __restrict__ colA,
+    int32_t* __restrict__ totals) {
+  __shared__ int wsum[2][kMergeWaves];
+  const int r = blockIdx.x;
+  const int32_t* idx = r ? approx_idx : full_idx;
+  uint32_t* out = r ? listA : listF;
+  int32_t* col = r ? colA : colF;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = min(max(counts[r], 0), d);
+  const int per = (n + kMergeThreads - 1) / kMergeThreads;
+  const int b = min(tid * per, n), e = min(b + per, n);
+  auto chan = [&](int i) { return min(max(idx[i], 0), d - 1); };
+  // does entry i + 1 continue entry i's run?
+  auto joins = [&](int i) {
+    if (i + 1 >= n) return false;
+    const int a = chan(i), c = chan(i + 1);
+    return c > a && c - a - 1 <= gap;
+  };
+  int cols = 0, runs = 0;
+  for (int i = b; i < e; ++i) {
+    cols += joins(i) ? chan(i + 1) - chan(i) : 1;
+    runs += (i == 0 || !joins(i - 1)) ? 1 : 0;
+  }
+  const int sc = merge_wave_scan(cols), sr = merge_wave_scan(runs);
+  if (lane == 63) {
+    wsum[0][wave] = sc;
+    wsum[1][wave] = sr;
+  }
+  __syncthreads();
+  int base = 0, tot_cols = 0, tot_runs = 0;
+  for (int w = 0; w < kMergeWaves; ++w) {
+    base += w < wave ? wsum[0][w] : 0;
+    tot_cols += wsum[0][w];
+    tot_runs += wsum[1][w];
+  }
+  int slot = base + sc - cols;  // exclusive prefix of this thread's first entry
+  for (int i = b; i < e; ++i) {
+    const int c = chan(i);
+    const int len = joins(i) ? chan(i + 1) - c : 1;
+    out[i] = (uint32_t)min(slot, d - 1) | ((uint32_t)c << 16);
+    for (int t = 0; t < len && slot + t < d; ++t) col[slot + t] = c + t;
+    slot += len;
+  }
+  if (tid == 0) {
+    totals[r] = min(tot_cols, d);  // staging slots used
+    totals[2 + r] = tot_runs;      // ranges
+    totals[4 + r] = n;             // entries
+  }
+}
+
 // Pinned-host gather: staging slot s of a region receives the record of column col[s] read
-// from the mapped host blob.  16-byte chunks, grid-stride; records are multiples of 128 bytes.
+// from the mapped host blob.  16-byte chunks, grid-stride; records are multiples of 128 bytes;
+// the slot counts are read on the device (totals[0], totals[1] from merge_ranges_kernel).
 __global__ __launch_bounds__(256) void gather_records_kernel(
     const uint8_t* __restrict__ host, uint8_t* __restrict__ staging,
-    const int32_t* __restrict__ colF, int64_t chunksF, int64_t strideF,
-    const int32_t* __restrict__ colA, int64_t chunksA, int64_t strideA, int64_t offA) {
+    const int32_t* __restrict__ colF, int64_t strideF, const int32_t* __restrict__ colA,
+    int64_t strideA, int64_t offA, const int32_t* __restrict__ totals, int32_t d) {
+  const int64_t chunksF = (int64_t)totals[0] * strideF / 16;
+  const int64_t chunksA = (int64_t)totals[1] * strideA / 16;
   const int64_t n = chunksF + chunksA;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
        c += (int64_t)gridDim.x * blockDim.x) {
@@ -48,7 +127,7 @@ __global__ __launch_bounds__(256) void gather_records_kernel(
     const int64_t stride = a ? strideA : strideF;
     const int64_t base = a ? offA : 0;
     const int64_t slot = b / stride, in = b - slot * stride;
-    const int32_t col = (a ? colA : colF)[slot];
+    const int32_t col = min(max((a ? colA : colF)[slot], 0), d - 1);  // never outside the blob
     const uint4 v = *reinterpret_cast<const uint4*>(host + base + (int64_t)col * stride + in);
     *reinterpret_cast<uint4*>(staging + base + b) = v;
   }
@@ -106,15 +185,19 @@ int launch_zero_f32(float* y, int64_t n, hipStream_t s) {
   return SPAX_OK;
 }
 
-int launch_gather_records(const spax_layout* L, const void* host_dev, void* staging,
-                          const int32_t* colF, int32_t nF_slots, const int32_t* colA,
-                          int32_t nA_slots, hipStream_t s) {
-  const int64_t cF = (int64_t)nF_slots * L->stride_F / 16, cA = (int64_t)nA_slots * L->stride_A / 16;
-  if (cF + cA == 0) return SPAX_OK;
-  const int64_t blocks = std::min<int64_t>((cF + cA + 255) / 256, 4096);
+int launch_merge_and_gather(const spax_layout* L, const void* host_dev, void* staging,
+                            const int32_t* full_idx, const int32_t* approx_idx,
+                            const int32_t* counts, int32_t gap, uint32_t* listF, uint32_t* listA,
+                            int32_t* colF, int32_t* colA, int32_t* totals, hipStream_t s) {
+  hipLaunchKernelGGL(merge_ranges_kernel, dim3(2), dim3(kMergeThreads), 0, s, full_idx,
+                     approx_idx, counts, L->d_in, gap, listF, listA, colF, colA, totals);
+  SPAX_HIP_CHECK(hipGetLastError());
+  // grid for the largest possible move (every column of both regions)
+  const int64_t most = (L->d_in * L->stride_F + L->d_in * L->stride_A) / 16;
+  const int64_t blocks = std::min<int64_t>((most + 255) / 256, 4096);
   hipLaunchKernelGGL(gather_records_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      static_cast<const uint8_t*>(host_dev), static_cast<uint8_t*>(staging), colF,
-                     cF, L->stride_F, colA, cA, L->stride_A, L->off_A);
+                     L->stride_F, colA, L->stride_A, L->off_A, totals, L->d_in);
   SPAX_HIP_CHECK(hipGetLastError());
   return SPAX_OK;
 }

@@ -1,6 +1,8 @@
 // Pinned-host path: the packed blob stays in host memory; per call only the selected column
-// records cross PCIe, as merged ranges copied with hipMemcpyAsync into a compacted staging
-// area, and the tiered GEMV runs over the staged records.
+// records cross PCIe, as merged ranges, into a compacted staging area, and the tiered GEMV
+// runs over the staged records.  Gather transfer: the ranges are merged on the device and one
+// copy kernel reads them from the mapped blob (nothing waits for the host).  Memcpy transfer:
+// the lists come back to the host, which merges them and issues one hipMemcpyAsync per range.
 //
 // Pages: SpAx Abstract (weights offloaded to system memory; per token, read each column in
 // full, as an approximation, or not at all); eigenradar commentary on SpAx, "The route outside
@@ -64,17 +66,72 @@ int32_t build_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t*
   });
 }
 
+namespace {
+
+// Workspace layout after the staging copy of the blob: FULL entries, APPROX entries, FULL slot
+// table, APPROX slot table (d int32 each), then the device-merge totals.
+struct PinnedTables {
+  uint32_t *listF, *listA;
+  int32_t *colF, *colA, *totals;
+};
+PinnedTables pinned_tables(const spax_layout* L, void* ws) {
+  const int d = L->d_in;
+  PinnedTables t;
+  t.listF = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + aligned_size((size_t)L->total_bytes));
+  t.listA = t.listF + d;
+  t.colF = reinterpret_cast<int32_t*>(t.listA + d);
+  t.colA = t.colF + d;
+  t.totals = t.colA + d;
+  return t;
+}
+constexpr int kTotals = 6;
+
+// Gather transfer with the ranges merged on the device: nothing waits for the host unless
+// the byte account is asked for.
+int tiered_gemv_pinned_device_merge(const spax_layout* L, const void* host_dev,
+                                    const uint16_t* x, const int32_t* full_idx,
+                                    const int32_t* approx_idx, const int32_t* counts, float* y,
+                                    int32_t gap, void* ws, spax_move_stats* stats,
+                                    hipStream_t s) {
+  const PinnedTables t = pinned_tables(L, ws);
+  int rc = launch_merge_and_gather(L, host_dev, ws, full_idx, approx_idx, counts, gap, t.listF,
+                                   t.listA, t.colF, t.colA, t.totals, s);
+  if (rc) return rc;
+  rc = launch_tiered_gemv(L, gemv_plan(L), ws, x, reinterpret_cast<const int32_t*>(t.listF),
+                          reinterpret_cast<const int32_t*>(t.listA), counts, y, false, s, true);
+  if (rc) return rc;
+  if (stats) {
+    int32_t h[kTotals];
+    SPAX_HIP_CHECK(hipMemcpyAsync(h, t.totals, sizeof(h), hipMemcpyDeviceToHost, s));
+    SPAX_HIP_CHECK(hipStreamSynchronize(s));
+    stats->selected_bytes = (int64_t)h[4] * L->stride_F + (int64_t)h[5] * L->stride_A;
+    stats->moved_bytes = (int64_t)h[0] * L->stride_F + (int64_t)h[1] * L->stride_A;
+    stats->list_bytes = 0;
+    stats->n_ranges = h[2] + h[3];
+    stats->n_full = h[4];
+    stats->n_approx = h[5];
+    stats->reserved0 = 0;
+  }
+  return SPAX_OK;
+}
+
+}  // namespace
+
 int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void* host_dev,
                        const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
                        const int32_t* counts, float* y, int32_t gap, int32_t transfer, void* ws,
                        spax_move_stats* stats, hipStream_t s) {
+  if (transfer == SPAX_PINNED_GATHER)
+    return tiered_gemv_pinned_device_merge(L, host_dev, x, full_idx, approx_idx, counts, y, gap,
+                                           ws, stats, s);
+  // SPAX_PINNED_MEMCPY: the ranges are merged on the host, one hipMemcpyAsync each
   const int d = L->d_in;
   int dev = 0;
   SPAX_HIP_CHECK(hipGetDevice(&dev));
   if (dev < 0 || dev >= 64) return fail(SPAX_ERR_UNSUPPORTED, "device index %d", dev);
   Scratch& sc = g_scratch[dev];
   std::lock_guard<std::mutex> lock(sc.mu);
-  const size_t need = 16 + 24 * (size_t)d;  // counts, two lists in, two lists out, 2 tables
+  const size_t need = 16 + 16 * (size_t)d;  // counts, two lists in, two compacted lists out
   if (sc.pending) {
     SPAX_HIP_CHECK(hipEventSynchronize(sc.done));
     sc.pending = false;
@@ -94,9 +151,6 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
   int32_t* h_apx = h_full + d;
   uint32_t* h_outF = reinterpret_cast<uint32_t*>(h_apx + d);
   uint32_t* h_outA = h_outF + d;
-  int32_t* h_colF = reinterpret_cast<int32_t*>(h_outA + d);  // staging slot -> column
-  int32_t* h_colA = h_colF + d;
-  const bool gather = transfer == SPAX_PINNED_GATHER;
 
   // ---- the mask, back on the host
   SPAX_HIP_CHECK(hipMemcpyAsync(h_counts, counts, 12, hipMemcpyDeviceToHost, s));
@@ -112,55 +166,38 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
   int64_t moved = 0;
   int n_ranges = 0;
   int rc = SPAX_OK;
-  const auto region = [&](const int32_t* idx, int n, uint32_t* out, int32_t* col, int64_t off,
-                          int64_t stride) {
+  const auto region = [&](const int32_t* idx, int n, uint32_t* out, int64_t off, int64_t stride) {
     int32_t slot = 0;
     const int r = for_ranges(idx, n, gap, [&](int32_t f, int32_t c, int32_t e0, int32_t ne) {
       if (rc) return;
       for (int32_t k = 0; k < ne; ++k)
         out[e0 + k] = (uint32_t)(slot + (idx[e0 + k] - f)) | ((uint32_t)idx[e0 + k] << 16);
-      if (gather) {
-        for (int32_t k = 0; k < c; ++k) col[slot + k] = f + k;
-      } else {
-        const hipError_t e = hipMemcpyAsync(staging + off + (int64_t)slot * stride,
-                                            host + off + (int64_t)f * stride, (size_t)c * stride,
-                                            hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) rc = hip_fail(e, "hipMemcpyAsync of a record range");
-      }
+      const hipError_t e = hipMemcpyAsync(staging + off + (int64_t)slot * stride,
+                                          host + off + (int64_t)f * stride, (size_t)c * stride,
+                                          hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) rc = hip_fail(e, "hipMemcpyAsync of a record range");
       moved += (int64_t)c * stride;
       slot += c;
     });
     if (r < 0 && !rc) rc = fail(SPAX_ERR_PARAM, "column list read back is not ascending");
     if (r > 0) n_ranges += r;
-    return slot;
   };
-  const int32_t slotsF = region(h_full, nF, h_outF, h_colF, 0, L->stride_F);
+  region(h_full, nF, h_outF, 0, L->stride_F);
   if (rc) return rc;
-  const int32_t slotsA = region(h_apx, nA, h_outA, h_colA, L->off_A, L->stride_A);
+  region(h_apx, nA, h_outA, L->off_A, L->stride_A);
   if (rc) return rc;
-  uint32_t* d_listF = reinterpret_cast<uint32_t*>(staging + aligned_size((size_t)L->total_bytes));
-  uint32_t* d_listA = d_listF + d;
-  int32_t* d_colF = reinterpret_cast<int32_t*>(d_listA + d);
-  int32_t* d_colA = d_colF + d;
-  // The host tables and their device copies have the same layout (four arrays of d entries:
-  // FULL list, APPROX list, FULL slot columns, APPROX slot columns), so one upload of the span
-  // that holds the used entries replaces four (each upload costs more to enqueue than to move).
-  size_t words = 0;
-  if (nF) words = (size_t)nF;
-  if (nA) words = (size_t)d + (size_t)nA;
-  if (gather && slotsF) words = 2 * (size_t)d + (size_t)slotsF;
-  if (gather && slotsA) words = 3 * (size_t)d + (size_t)slotsA;
-  if (words) SPAX_HIP_CHECK(hipMemcpyAsync(d_listF, h_outF, 4 * words, hipMemcpyHostToDevice, s));
+  // The two host lists and their device copies have the same layout (d entries each), so one
+  // upload of the span that holds the used entries replaces two (an upload costs more to
+  // enqueue than to move).
+  const PinnedTables t = pinned_tables(L, ws);
+  const size_t words = nA ? (size_t)d + (size_t)nA : (size_t)nF;
+  if (words) SPAX_HIP_CHECK(hipMemcpyAsync(t.listF, h_outF, 4 * words, hipMemcpyHostToDevice, s));
   SPAX_HIP_CHECK(hipEventRecord(sc.done, s));
   sc.pending = true;
-  if (gather) {
-    rc = launch_gather_records(L, host_dev, staging, d_colF, slotsF, d_colA, slotsA, s);
-    if (rc) return rc;
-  }
 
   // ---- the GEMV over the staged records (counts are still the device's)
-  rc = launch_tiered_gemv(L, gemv_plan(L), staging, x, reinterpret_cast<const int32_t*>(d_listF),
-                          reinterpret_cast<const int32_t*>(d_listA), counts, y, false, s, true);
+  rc = launch_tiered_gemv(L, gemv_plan(L), staging, x, reinterpret_cast<const int32_t*>(t.listF),
+                          reinterpret_cast<const int32_t*>(t.listA), counts, y, false, s, true);
   if (rc) return rc;
   if (stats) {
     stats->selected_bytes = (int64_t)nF * L->stride_F + (int64_t)nA * L->stride_A;
@@ -175,7 +212,7 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
 }
 
 size_t pinned_workspace_bytes(const spax_layout* L) {
-  return aligned_size((size_t)L->total_bytes) + 16 * (size_t)L->d_in;
+  return aligned_size((size_t)L->total_bytes) + 16 * (size_t)L->d_in + 4 * kTotals;
 }
 
 }  // namespace spax

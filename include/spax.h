@@ -215,27 +215,30 @@ int spax_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* firs
 typedef struct spax_move_stats {
   int64_t selected_bytes;  /* n_full * stride_F + n_approx * stride_A                   */
   int64_t moved_bytes;     /* record bytes copied host -> device (selected + merged gaps) */
-  int64_t list_bytes;      /* list bytes copied host -> device: one upload of the span of
-                              the host tables (FULL and APPROX compacted entries, then for
-                              the gather transfer the FULL and APPROX slot -> column tables;
-                              d_in entries each) that holds every used entry              */
-  int32_t n_ranges;        /* record copies enqueued (FULL ranges + APPROX ranges)       */
+  int64_t list_bytes;      /* list bytes copied host -> device: 0 for SPAX_PINNED_GATHER
+                              (the lists never leave the device); for SPAX_PINNED_MEMCPY one
+                              upload of the span of the two compacted host lists (d_in
+                              entries each) that holds every used entry                 */
+  int32_t n_ranges;        /* merged ranges (FULL + APPROX)                               */
   int32_t n_full, n_approx;
   int32_t reserved0;
 } spax_move_stats;
 
 /* spax_tiered_gemv_pinned: how the ranges cross PCIe */
 enum {
-  /* one hipMemcpyAsync per range (host-driven DMA) */
+  /* the lists come back to the host (the call synchronizes `stream`), which merges the
+   * ranges and issues one hipMemcpyAsync per range (host-driven DMA) */
   SPAX_PINNED_MEMCPY = 0,
-  /* one copy kernel for all ranges: the device reads the mapped pinned blob (zero-copy) and
-   * writes the compacted staging area; the range list goes over as one slot -> column table */
+  /* the ranges are merged on the device (one kernel, two workgroups) and one copy kernel
+   * reads them from the mapped pinned blob (zero-copy) into the compacted staging area:
+   * nothing waits for the host, so the call is asynchronous unless `stats` is requested */
   SPAX_PINNED_GATHER = 1
 };
 
 /* Device workspace for spax_tiered_gemv_pinned: a compacted staging copy of the blob's
  * records (total_bytes, for the case that every column is selected), two compacted lists and
- * two slot -> column tables (4 * d_in bytes each); 0 if *L is not initialised. */
+ * two slot -> column tables (4 * d_in bytes each) and 24 bytes of totals; 0 if *L is not
+ * initialised. */
 size_t spax_pinned_workspace_bytes(const spax_layout* L);
 
 /*
@@ -246,18 +249,21 @@ size_t spax_pinned_workspace_bytes(const spax_layout* L);
  *   gap   : range merging, as for spax_column_ranges.
  *   transfer : SPAX_PINNED_MEMCPY or SPAX_PINNED_GATHER (same bytes moved, same result).
  *   ws    : device, >= spax_pinned_workspace_bytes(L) bytes, 256-byte aligned.
- *   stats : may be NULL.
- * Reads counts and lists back to the host (this synchronizes `stream`), merges the selected
- * columns of each region into ranges, copies the ranges host -> device (see `transfer`) into
- * a compacted staging area of ws (a range's columns land in consecutive slots, ranges in
- * order), copies the compacted lists (staging slot | channel << 16),
- * then runs the tiered GEMV over the staged records.  y equals spax_tiered_gemv's on a device
- * copy of the blob up to the order of fp32 additions.  Returns with the copies and the GEMV
- * enqueued on `stream`.  Library-owned pinned buffers hold the lists; a later call waits until
- * the previous call's list copy has completed before reusing them.
+ *   stats : host, may be NULL (the byte account; requesting it synchronizes `stream`).
+ * Merges the selected columns of each region into ranges (on the device for
+ * SPAX_PINNED_GATHER; on the host, after reading counts and lists back, for
+ * SPAX_PINNED_MEMCPY), moves the ranges host -> device (see `transfer`) into a compacted
+ * staging area of ws (a range's columns land in consecutive slots, ranges in order) with the
+ * compacted lists (staging slot | channel << 16), then runs the tiered GEMV over the staged
+ * records.  y equals spax_tiered_gemv's on a device copy of the blob up to the order of fp32
+ * additions.  Returns with the work enqueued on `stream`; with `stats` it also waits for the
+ * byte account.  SPAX_PINNED_MEMCPY: library-owned pinned buffers hold the lists; a later
+ * call waits until the previous call's list copy has completed before reusing them.
+ * SPAX_PINNED_GATHER on lists that are not strictly ascending gives an unspecified y (never
+ * an access outside the blob or ws).
  * Errors: as spax_tiered_gemv, plus SPAX_ERR_PARAM (gap < 0, unknown transfer, packed_host
- * not pinned host memory mapped for the device, lists read back not ascending) and
- * SPAX_ERR_WORKSPACE.
+ * not pinned host memory mapped for the device, and for SPAX_PINNED_MEMCPY lists read back not
+ * ascending) and SPAX_ERR_WORKSPACE.
  */
 int spax_tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
                             const int32_t* full_idx, const int32_t* approx_idx,

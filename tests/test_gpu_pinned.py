@@ -95,21 +95,13 @@ def test_pinned_matches_oracle_and_device_path(env, fmt, G, gap, transfer):
 
 
 def expected_upload(d, led, transfer):
-    """Bytes of the one list upload: the four host tables (FULL entries, APPROX entries, FULL
-    slot columns, APPROX slot columns; d entries each) up to the last one in use."""
-    nf = sum(c for _, c in led["ranges_full"])   # staging slots: columns moved, gaps included
-    na = sum(c for _, c in led["ranges_approx"])
+    """Bytes of list data sent host -> device: none for the gather transfer (the ranges are
+    merged on the device); for the memcpy transfer one upload of the two compacted host lists
+    (d entries each) up to the last one in use."""
+    if transfer == 1:
+        return 0
     lf, la = led["n_full"], led["n_approx"]
-    words = 0
-    if lf:
-        words = lf
-    if la:
-        words = d + la
-    if transfer == 1 and nf:
-        words = 2 * d + nf
-    if transfer == 1 and na:
-        words = 3 * d + na
-    return 4 * words
+    return 4 * (d + la if la else lf)
 
 
 @pytest.mark.parametrize("transfer", [0, 1])
