@@ -141,3 +141,58 @@ def test_pinned_rejects_device_blob(env):
     with pytest.raises(spax.SpaxError) as e:
         spax.spax_tiered_gemv_pinned(L, packed, b["x"], b["f"], b["a"], b["c"], y, 0, ws)
     assert "pinned" in str(e.value)
+
+
+def test_pinned_gather_without_account_and_in_a_graph(env):
+    """The gather transfer merges the ranges on the device, so a call without the byte account
+    waits for nothing and can be captured into a HIP graph: y from replays (outputs clobbered
+    in between) equals y from the eager call with the account."""
+    torch, spax, dev = env
+    d_in, d_out = 3000, [1024, 512]
+    nF, nA = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
+    L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 64, 21, nF, nA)
+    y_ref, st = run_pinned(env, L, host, b, 2, transfer=1)
+    assert st.n_full == nF and st.n_approx == nA and st.list_bytes == 0
+    ws = torch.empty(spax.spax_pinned_workspace_bytes(L), dtype=torch.uint8, device=dev)
+    y = torch.full((int(L.d_out_total),), float("nan"), dtype=torch.float32, device=dev)
+    assert spax.spax_tiered_gemv_pinned(L, host, b["x"], b["f"], b["a"], b["c"], y, 2, ws,
+                                        transfer=1, stats=False) is None
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), y_ref) <= 1e-6
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        spax.spax_tiered_gemv_pinned(L, host, b["x"], b["f"], b["a"], b["c"], y, 2, ws,
+                                     transfer=1, stats=False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        spax.spax_tiered_gemv_pinned(L, host, b["x"], b["f"], b["a"], b["c"], y, 2, ws,
+                                     transfer=1, stats=False)
+    for _ in range(3):
+        y.fill_(float("nan"))
+        ws.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert rel_l2(y.cpu().numpy(), y_ref) <= 1e-6
+
+
+def test_pinned_gather_malformed_lists_stay_inside(env):
+    """Lists that are not ascending and hold out-of-range channels (the device merge cannot
+    return an error): the call completes, every access stays inside the blob and the
+    workspace (indices and slots are clamped on the device), and y is finite."""
+    torch, spax, dev = env
+    d_in, d_out = 1000, [512]
+    L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 128, 23, 40, 60)
+    rng = np.random.default_rng(5)
+    bad_f = rng.integers(-50, d_in + 50, size=d_in).astype(np.int32)   # unordered, out of range
+    bad_a = np.concatenate([np.arange(d_in - 1, -1, -1)]).astype(np.int32)  # descending
+    b["f"].copy_(torch.from_numpy(bad_f))
+    b["a"].copy_(torch.from_numpy(bad_a))
+    b["c"].copy_(torch.tensor([700, 900, 0], dtype=torch.int32))
+    for gap in (0, 5, d_in):
+        y, st = run_pinned(env, L, host, b, gap, transfer=1)
+        assert np.isfinite(y).all()
+        assert 0 <= st.moved_bytes <= d_in * (L.stride_F + L.stride_A)
