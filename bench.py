@@ -1,7 +1,7 @@
 """Benchmark of the tiered activation-sparse decoding GEMV on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode7b] [--sparsity 0.5]
-                    [--no-cpu-baseline] [--no-batched] [--control none|full|skip]
+                    [--no-cpu-baseline] [--no-batched] [--no-separate] [--control none|full|skip]
 
 Default workload (decode7b): one step is one token of a 32-layer 7B-shaped decoder: for each
 layer and each projection group (q|k|v, o, gate|up, down) one TopK-Guided tier mask (s +-
@@ -29,6 +29,8 @@ per launch, over its average launch duration (the timed step's event time over i
 ``cpu_baseline`` times the oracle (float64 NumPy) on a bounded sample of the same workload on
 the host cores.  ``batched`` is the same step in the batched launch form (all masks in one
 launch, all GEMVs in one), legal here only because the synthetic inputs are independent.
+``separate`` is the same step through the two stand-alone kernels per phase, the mask kernel
+of spax_build_tiers and the GEMV kernel of spax_tiered_gemv.
 ``token_us`` gives the median and 90th percentile over the timed tokens, each timed on its
 own after the timed region.  ``--control full|skip`` replaces the tier rule by all-FULL or
 all-SKIP masks: controls for the hardware byte counters.  ``read_probe`` gives what a plain
@@ -81,6 +83,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip timing the batched step form")
+    ap.add_argument("--no-separate", action="store_true",
+                    help="skip timing the two-launch step form")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the plain streaming-read ceiling and floor")
     ap.add_argument("--no-dense", action="store_true",
@@ -395,6 +399,26 @@ def read_probe(spax, torch, dev, launch_bytes, reps=8):
                     "each reading that launch's selected byte count"}
 
 
+def time_form(stack, flags, args):
+    """ms per step of the same step in another launch form (warm-up, then the timed steps
+    between two events on the launch stream); the stack returns to the default form."""
+    import torch
+    stack.flags = flags
+    try:
+        for t in range(args.warmup):
+            stack.step(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(args.steps):
+            stack.step(args.warmup + t)
+        e1.record()
+        torch.cuda.synchronize()
+    finally:
+        stack.flags = 0
+    return e0.elapsed_time(e1) / args.steps
+
+
 def dense_baseline(stack, reps=10):
     """The same step without tiers, as context for the speedup over dense decoding: per phase
     one torch fp16 matrix-vector product (the vendor BLAS) of the phase's dense weights with
@@ -516,18 +540,7 @@ def device_bench(args, spax, torch, dev):
     # layer-serial value, never as it
     batched = None
     if not args.no_batched:
-        stack.flags = spax.STEP_BATCHED
-        for t in range(args.warmup):
-            stack.step(t)
-        torch.cuda.synchronize()
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0.record()
-        for t in range(args.steps):
-            stack.step(args.warmup + t)
-        b1.record()
-        torch.cuda.synchronize()
-        stack.flags = spax.STEP_DEFAULT
-        bt_ms = b0.elapsed_time(b1) / args.steps
+        bt_ms = time_form(stack, spax.STEP_BATCHED, args)
         bgbs = bytes_per_step / (bt_ms * 1e-3) / 1e9
         batched = {"value": round(bt_ms * 1e3 / per_tok, 2), "unit": "us/token",
                    "achieved_GBps": round(bgbs, 1), "frac": round(bgbs / HBM_PEAK_GBS, 4),
@@ -535,6 +548,20 @@ def device_bench(args, spax, torch, dev):
                            "one persistent launch; valid only because the phase inputs are "
                            "independent"}
         log(f"[bench] batched step: {bt_ms * 1e3:.1f} us, {bgbs:.1f} GB/s")
+
+    # ---- the two-launch form of the same step (per phase, the stand-alone mask kernel of
+    # spax_build_tiers, then the stand-alone GEMV kernel of spax_tiered_gemv): what a caller
+    # of those two entry points gets, reported beside the fused value
+    separate = None
+    if not args.no_separate:
+        separate = {"value": round(time_form(stack, spax.STEP_SEPARATE, args) * 1e3 / per_tok, 2),
+                    "unit": "us/token",
+                    "form": f"SPAX_STEP_SEPARATE: per phase a build_tiers_kernel launch and a "
+                            f"tiered_gemv_kernel launch ({2 * n_ph} launches per step), phases in order"}
+        sgbs = bytes_per_step / (separate["value"] * per_tok * 1e-6) / 1e9
+        separate["achieved_GBps"] = round(sgbs, 1)
+        separate["frac"] = round(sgbs / HBM_PEAK_GBS, 4)
+        log(f"[bench] two-launch step: {separate['value'] * per_tok:.1f} us, {sgbs:.1f} GB/s")
 
     dense = None
     if not args.no_dense and spec["fmt"] == 0 and args.control == "none":
@@ -587,6 +614,7 @@ def device_bench(args, spax, torch, dev):
                                                if probe else None)},
         "cpu_baseline": cpu,
         "batched": batched,
+        "separate": separate,
         "token_us": token_us,
         "read_probe": probe,
         "dense_baseline": dense,
