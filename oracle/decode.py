@@ -38,13 +38,3 @@ def decode_step(phases):
 def selected_bytes(layout: pack.Layout, counts) -> int:
     """Bytes of the column records a mask selects (the per-token byte ledger)."""
     return int(counts[0]) * layout.stride_F + int(counts[1]) * layout.stride_A
-
-
-def dense_bytes(layout: pack.Layout) -> int:
-    return layout.d_in * layout.stride_F
-
-
-def record_bytes(layout: pack.Layout):
-    """Unpadded (F, A) record sizes."""
-    return layout.rec_F, layout.rec_A
-

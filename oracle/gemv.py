@@ -71,11 +71,3 @@ def tiered_gemv_loops(full_cols, approx_cols, x, full_idx, approx_idx):
             y[r] += float(x[j]) * approx_cols[j][r]
     return y
 
-
-def split_rows(layout: pack.Layout, y: np.ndarray):
-    """Split a fused output back into one vector per matrix."""
-    out, r0 = [], 0
-    for r in layout.d_out:
-        out.append(y[r0:r0 + r])
-        r0 += r
-    return out

@@ -14,9 +14,6 @@ unselected channels are merged, and the gap columns are moved too.
 
 from __future__ import annotations
 
-import numpy as np
-
-
 def runs(sel_idx, gap: int = 0):
     """Ascending channel indices -> list of (first, count) ranges after gap merging."""
     idx = [int(v) for v in sel_idx]
@@ -50,8 +47,3 @@ def compact_positions(ranges):
             slot += 1
     return out
 
-
-def selected_mask(d: int, sel_idx) -> np.ndarray:
-    m = np.zeros(d, dtype=bool)
-    m[np.asarray(sel_idx, dtype=np.int64)] = True
-    return m

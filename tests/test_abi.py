@@ -207,10 +207,22 @@ def test_gemv_and_pack_validation():
 
 
 @needs_no_gpu
+def _fake_phase(L, params, i=0, **over):
+    """A phase whose buffers sit at distinct fake addresses (1 MiB apart), phase i in its own
+    16 MiB window; keyword arguments replace single addresses."""
+    MB = 1 << 20
+    base = FAKE + i * 16 * MB
+    a = dict(packed=base, x=base + MB, tier=base + 2 * MB, f=base + 3 * MB, a=base + 4 * MB,
+             c=base + 5 * MB, y=base + 6 * MB)
+    a.update(over)
+    return spax.make_phase(L, a["packed"], a["x"], params, a["tier"], a["f"], a["a"], a["c"],
+                           a["y"])
+
+
 def test_decode_step_validates_all_phases_first():
     L = spax.spax_layout_init(64, [512], 0, 128, 64)
-    good = spax.make_phase(L, FAKE, FAKE, spax.topk_params(4, 4), 0, FAKE, FAKE, FAKE, FAKE)
-    bad = spax.make_phase(L, FAKE, FAKE, spax.topk_params(40, 40), 0, FAKE, FAKE, FAKE, FAKE)
+    good = _fake_phase(L, spax.topk_params(4, 4))
+    bad = _fake_phase(L, spax.topk_params(40, 40))
     arr = spax.phase_array([good, good, bad])
     ws = spax.spax_step_workspace_bytes(arr)
     assert spax.spax_gemv_workspace_bytes(L) == 0
@@ -258,6 +270,53 @@ def test_batched_step_validation():
     assert e.value.status == _lib.SPAX_ERR_PARAM
 
 
+@needs_no_gpu
+@pytest.mark.parametrize("flags", [0, 1, 2])
+def test_step_rejects_aliasing_within_a_phase(flags):
+    """Within one phase no output may share a byte with another output or with the phase's
+    x or blob (its kernels read and write them concurrently); checked before any launch in
+    every launch form.  Across phases buffers may be shared (stream order)."""
+    MB = 1 << 20
+    L = spax.spax_layout_init(64, [512], 0, 128, 64)
+    p = spax.topk_params(4, 4)
+    for over in [dict(y=FAKE + MB), dict(y=FAKE), dict(y=FAKE + 3 * MB + 128),
+                 dict(f=FAKE + 2 * MB), dict(c=FAKE + 4 * MB + 252), dict(tier=FAKE + MB + 64),
+                 dict(a=FAKE + 16)]:
+        # phase 1's window starts 16 MiB on; the override is shifted into it
+        arr = spax.phase_array([_fake_phase(L, p, 0),
+                                _fake_phase(L, p, 1, **{k: v + 16 * MB for k, v in over.items()})])
+        ws = spax.spax_step_workspace_bytes(arr)
+        with pytest.raises(spax.SpaxError) as e:
+            spax.spax_decode_step_projections(arr, FAKE + 512 * MB, ws_bytes=ws, flags=flags,
+                                              stream=0)
+        assert e.value.status == _lib.SPAX_ERR_PARAM and "phase 1" in str(e.value), over
+        assert "overlaps" in str(e.value)
+
+
+@needs_no_gpu
+def test_batched_step_rejects_output_on_another_phase_blob():
+    MB = 1 << 20
+    L = spax.spax_layout_init(64, [512], 0, 128, 64)
+    p = spax.topk_params(4, 4)
+    arr = spax.phase_array([_fake_phase(L, p, 0), _fake_phase(L, p, 1, y=FAKE + 256)])
+    ws = spax.spax_step_workspace_bytes(arr)
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections(arr, FAKE + 512 * MB, ws_bytes=ws, flags=2, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_PARAM and "overlap" in str(e.value)
+    # the layer-serial forms allow it (phase 1 runs after phase 0 in stream order); only
+    # validation is exercised here, so a form that passed it would launch: not called
+
+
+@needs_no_gpu
+def test_gemv_rejects_y_on_blob_or_x():
+    L = spax.spax_layout_init(64, [512], 0, 128, 64)
+    MB = 1 << 20
+    for y in (FAKE + 4096, FAKE + MB - 16):
+        r = _lib.lib.spax_tiered_gemv(C.byref(L), FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 3 * MB,
+                                      FAKE + 4 * MB, y, 0, 0, 0)
+        assert r == _lib.SPAX_ERR_PARAM, y
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_column_ranges_match_oracle(seed):
     """Host range builder of the pinned path against oracle/ranges.py (integer, exact)."""
@@ -285,7 +344,9 @@ def test_pinned_gemv_validation():
     L = spax.spax_layout_init(64, [512], 0, 128, 64)
     need = spax.spax_pinned_workspace_bytes(L)
     assert need >= int(L.total_bytes) + 16 * 64
-    args = dict(x=FAKE, full_idx=FAKE, approx_idx=FAKE, counts=FAKE, y=FAKE)
+    MB = 1 << 20
+    args = dict(x=FAKE + MB, full_idx=FAKE + 2 * MB, approx_idx=FAKE + 3 * MB,
+                counts=FAKE + 4 * MB, y=FAKE + 5 * MB)
 
     def call(packed=FAKE, gap=0, ws=FAKE, ws_bytes=need, transfer=0):
         return spax.spax_tiered_gemv_pinned(L, packed, args["x"], args["full_idx"],

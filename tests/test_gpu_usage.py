@@ -8,9 +8,9 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import gemv as ogemv
 from oracle import pack as opack
 from oracle import tiers as otiers
+from tests.parity_util import check_y_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +46,7 @@ def test_readme_usage():
     assert list(cc) == list(wc)
     assert np.array_equal(f.cpu().numpy()[:cc[0]], wf)
     assert np.array_equal(a.cpu().numpy()[:cc[1]], wa)
-    ref = ogemv.tiered_gemv(opack.Layout(d_in, d_out, 0, 128, 128), Ws, x16, wf, wa)
-    got = y.cpu().numpy().astype(np.float64)
-    assert np.linalg.norm(got - ref) <= 1e-3 * np.linalg.norm(ref)
-    assert math.isfinite(float(np.abs(got).max()))
+    check_y_oracle(y.cpu().numpy(), opack.Layout(d_in, d_out, 0, 128, 128), Ws, x16, wf, wa)
 
 
 def test_c_abi_demo():

@@ -193,20 +193,64 @@ def test_ranges_characterised_by_their_gaps(gap):
             assert f1 - (f0 + c0) > gap
 
 
-def test_decode_step_matches_per_phase_calls():
-    rng = np.random.default_rng(11)
+def _exact_level_matrix(rng, d_in, d_out, G):
+    """Column-major fp16 (d_in, d_out) whose every group of G rows holds only the values
+    z, z + s, z + 2s, z + 3s, both ends present, with s a power of two and z a multiple of
+    s: the two-bit quantizer then recovers s and z exactly and reconstructs every value."""
+    W = np.empty((d_in, d_out), dtype=np.float16)
+    for j in range(d_in):
+        for g0 in range(0, d_out, G):
+            s = 2.0 ** int(rng.integers(-9, -5))
+            z = s * int(rng.integers(-6, 3))
+            q = rng.integers(0, 4, G)
+            q[int(rng.integers(0, G))] = 0
+            q[int(rng.integers(0, G))] = 3
+            W[j, g0:g0 + G] = (z + s * q).astype(np.float16)
+    return W
+
+
+def test_decode_step_pinned_by_brute_force():
+    """O5: each phase's mask comes from its own x and parameters, and its y from its own
+    weights.  Three phases, two with the same d_in but different x, so a step that crossed
+    the phases' inputs fails.  Expected masks: brute-force sort by (|x| descending, index)
+    for TopK, float comparison for the threshold, and TopK-Guided with a one-count band
+    (delta = 0), which must equal TopK at that count (TopK-Guided section 2.1).  Expected y:
+    NumPy's dense float64 product over the kept columns; the weights take exact two-bit
+    levels, so the approximation reconstructs them and FULL and APPROX columns contribute
+    their plain values."""
+    rng = np.random.default_rng(77)
+    vals = np.array([0, 0.25, -0.25, 0.5, -1, 1.5, 2, -2, 3], np.float16)
+    specs = [
+        (6, [64], dict(mode=tiers.MODE_TOPK, n_full=2, n_approx=2)),
+        (9, [64, 64], dict(mode=tiers.MODE_THRESHOLD, tau_skip=0.5, tau_full=1.5)),
+        (6, [128], dict(mode=tiers.MODE_TOPK_GUIDED, tau=0.3, n_lo=3, n_hi=3, num=1, den=3)),
+    ]
     phases = []
-    for name, d_in, d_out in [("qkv", 64, [128, 64, 64]), ("o", 64, [64]), ("down", 128, [64])]:
+    for d_in, d_out, targs in specs:
         L = pack.Layout(d_in, d_out, pack.FMT_FP16, 128, 64)
-        Ws = [(rng.standard_normal((d_in, r)) * 0.02).astype(np.float16) for r in d_out]
-        x = rng.laplace(size=d_in).astype(np.float16)
-        n_lo, n_hi = tiers.guided_bounds(d_in, 0.5, 0.05)
-        phases.append(dict(layout=L, Ws=Ws, x=x,
-                           tier_args=dict(mode=tiers.MODE_TOPK_GUIDED, tau=0.69, n_lo=n_lo,
-                                          n_hi=n_hi, num=3, den=10)))
+        Ws = [_exact_level_matrix(rng, d_in, r, 64) for r in d_out]
+        x = rng.choice(vals, d_in)
+        phases.append(dict(layout=L, Ws=Ws, x=x, tier_args=targs))
+    assert not np.array_equal(phases[0]["x"], phases[2]["x"])
     out = decode.decode_step(phases)
+    assert len(out) == len(phases)
     for ph, (tier, f, a, c, y) in zip(phases, out):
-        assert abs(c[2] / ph["layout"].d_in - 0.5) <= 0.05 + 1e-12
-        assert np.allclose(y, gemv.tiered_gemv(ph["layout"], ph["Ws"], ph["x"], f, a))
-        parts = gemv.split_rows(ph["layout"], y)
-        assert [p.size for p in parts] == ph["layout"].d_out
+        x = ph["x"].astype(np.float64)
+        d = x.size
+        order = sorted(range(d), key=lambda j: (-abs(x[j]), j))
+        t = ph["tier_args"]
+        if t["mode"] == tiers.MODE_THRESHOLD:
+            want_f = [j for j in range(d) if abs(x[j]) >= 1.5]
+            want_a = [j for j in range(d) if 0.5 <= abs(x[j]) < 1.5]
+        elif t["mode"] == tiers.MODE_TOPK:
+            want_f, want_a = sorted(order[:2]), sorted(order[2:4])
+        else:  # band [3, 3]: 3 kept, 1 of them APPROX (round-half-up of 3/3 = 1)
+            want_f, want_a = sorted(order[:2]), sorted(order[2:3])
+        assert list(f) == want_f and list(a) == want_a
+        assert list(c) == [len(want_f), len(want_a), d - len(want_f) - len(want_a)]
+        assert [int(v) for v in tier] == [2 if j in want_f else 1 if j in want_a else 0
+                                          for j in range(d)]
+        W = np.concatenate(ph["Ws"], axis=1).astype(np.float64)      # (d_in, T)
+        kept = sorted(want_f + want_a)
+        ref = W[kept].T @ x[kept] if kept else np.zeros(W.shape[1])
+        assert np.array_equal(y, ref) or np.allclose(y, ref, rtol=0, atol=1e-15)

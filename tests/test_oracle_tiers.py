@@ -150,10 +150,19 @@ def test_guided_realised_sparsity_within_delta(seed):
     s = float(rng.choice([0.3, 0.5, 0.7, rng.uniform(0.05, 0.95)]))
     delta = float(rng.choice([0.01, 0.0, 0.05]))
     n_lo, n_hi = tiers.guided_bounds(d, s, delta)
-    if n_lo > n_hi:
-        pytest.skip("empty integer band (d*delta < 1 and s*d not an integer)")
     x = (rng.laplace(size=d) * rng.lognormal(0, 0.7)).astype(np.float16)
     tau = -math.log(1 - s)
+    if n_lo > n_hi:
+        # An empty integer band: no skip count n has n/d within +-delta of s (brute force
+        # over every count), and the mask refuses the band.  Then delta = 1/d, whose band
+        # always holds an integer, is checked instead.
+        assert not any(s - delta - 1e-12 <= n / d <= s + delta + 1e-12 for n in range(d + 1))
+        with pytest.raises(ValueError):
+            tiers.build_tiers(x, tiers.MODE_TOPK_GUIDED, tau=tau, n_lo=n_lo, n_hi=n_hi,
+                              num=3, den=10)
+        delta = 1.0 / d
+        n_lo, n_hi = tiers.guided_bounds(d, s, delta)
+        assert n_lo <= n_hi
     tier, f, a, cnt = tiers.build_tiers(x, tiers.MODE_TOPK_GUIDED, tau=tau, n_lo=n_lo,
                                         n_hi=n_hi, num=3, den=10)
     n_skip = int(cnt[2])
