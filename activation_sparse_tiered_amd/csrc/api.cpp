@@ -45,6 +45,7 @@ int check_independent(const spax_step* st) {
       if (p && n) r.push_back(Range{(uintptr_t)p, (uintptr_t)p + n, i, out});
     };
     add(ph.x, 2 * (size_t)L->d_in, false);
+    add(ph.packed, (size_t)L->total_bytes, false);
     add(ph.tier, (size_t)L->d_in, true);
     add(ph.full_idx, 4 * (size_t)L->d_in, true);
     add(ph.approx_idx, 4 * (size_t)L->d_in, true);
@@ -64,6 +65,34 @@ int check_independent(const spax_step* st) {
   return SPAX_OK;
 }
 
+// Within one phase of a step, no output (tier bytes, lists, counts, y) shares a byte with
+// another output or with the phase's inputs (x, blob): the phase's kernels read and write
+// them concurrently.  Phases may share buffers with each other (stream order).
+int check_phase_aliasing(const spax_phase& ph) {
+  const spax_layout* L = ph.layout;
+  const size_t d = (size_t)L->d_in;
+  struct Buf {
+    const void* p;
+    size_t n;
+    const char* name;
+  };
+  const Buf out[] = {{ph.tier, d, "tier"},
+                     {ph.full_idx, 4 * d, "full_idx"},
+                     {ph.approx_idx, 4 * d, "approx_idx"},
+                     {ph.counts, 12, "counts"},
+                     {ph.y, 4 * (size_t)L->d_out_total, "y"}};
+  const Buf in[] = {{ph.x, 4 * ((d + 1) / 2), "x"}, {ph.packed, (size_t)L->total_bytes, "packed"}};
+  for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
+    for (size_t k = i + 1; k < sizeof(out) / sizeof(out[0]); ++k)
+      if (overlaps(out[i].p, out[i].n, out[k].p, out[k].n))
+        return fail(SPAX_ERR_PARAM, "%s overlaps %s of the same phase", out[i].name, out[k].name);
+    for (const Buf& b : in)
+      if (overlaps(out[i].p, out[i].n, b.p, b.n))
+        return fail(SPAX_ERR_PARAM, "%s overlaps %s of the same phase", out[i].name, b.name);
+  }
+  return SPAX_OK;
+}
+
 int check_gemv_args(const spax_layout* L, const void* packed, const uint16_t* x,
                     const int32_t* full_idx, const int32_t* approx_idx, const int32_t* counts,
                     const float* y, const void* ws, size_t ws_bytes, GemvPlan* plan) {
@@ -76,6 +105,9 @@ int check_gemv_args(const spax_layout* L, const void* packed, const uint16_t* x,
   if (!aligned(x, 4) || !aligned(full_idx, 4) || !aligned(approx_idx, 4) || !aligned(counts, 4) ||
       !aligned(y, 16))
     return fail(SPAX_ERR_ALIGN, "x/lists/counts must be 4-byte aligned and y 16-byte aligned");
+  if (overlaps(y, 4 * (size_t)L->d_out_total, packed, (size_t)L->total_bytes) ||
+      overlaps(y, 4 * (size_t)L->d_out_total, x, 4 * (((size_t)L->d_in + 1) / 2)))
+    return fail(SPAX_ERR_PARAM, "y overlaps the blob or x");
   *plan = gemv_plan(L);
   if (plan->ws_bytes > 0 && !ws) return fail(SPAX_ERR_NULL, "workspace is NULL");
   if (ws_bytes < plan->ws_bytes)
@@ -201,6 +233,8 @@ int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
     GemvPlan plan;
     st = check_gemv_args(ph.layout, ph.packed, ph.x, ph.full_idx, ph.approx_idx, ph.counts, ph.y,
                          step->ws, step->ws_bytes, &plan);
+    if (st) return phase_fail(st, i);
+    st = check_phase_aliasing(ph);
     if (st) return phase_fail(st, i);
   }
   if (batched) {

@@ -121,17 +121,10 @@ __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDe
   }
 }
 
-int env_or(const char* name, int dflt) {
-  const char* v = getenv(name);
-  const int x = v ? atoi(v) : 0;
-  return x > 0 ? x : dflt;
-}
-
 // Column chunks of a batched phase: about 2048 input channels each, so a work item streams
-// hundreds of columns and its fixed cost (lists, reduction, atomics) stays small;
-// SPAX_BATCH_CHANNELS overrides.
+// hundreds of columns and its fixed cost (lists, reduction, atomics) stays small.
 GemvPlan batched_plan(const spax_layout* L) {
-  static const int channels = env_or("SPAX_BATCH_CHANNELS", 2048);
+  constexpr int channels = 2048;
   GemvPlan p{};
   p.n_tiles = (int32_t)((L->d_out_total + kTileRows - 1) / kTileRows);
   int k = (L->d_in + channels - 1) / channels;
@@ -243,13 +236,13 @@ int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s) {
     SPAX_HIP_CHECK(hipEventRecord(st->events[1], s));
     SPAX_HIP_CHECK(hipEventRecord(st->events[2], s));
   }
-  // as many workgroups as can be resident at once (SPAX_BATCH_WGS_PER_CU overrides)
+  // as many workgroups as can be resident at once
   static const int per_cu = [] {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, batched_gemv_kernel, kGemvThreads, 0) !=
             hipSuccess || occ < 1)
       occ = 2;
-    return env_or("SPAX_BATCH_WGS_PER_CU", occ);
+    return occ;
   }();
   const int64_t cap = (int64_t)n_cu * per_cu;
   const int64_t grid = items < cap ? items : cap;

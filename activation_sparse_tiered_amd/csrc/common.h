@@ -71,6 +71,11 @@ int launch_zero_f32(float* y, int64_t n, hipStream_t s);
 constexpr int64_t kMaskClearMax = 65536;
 
 // ------------------------------------------------------------------ decode step
+// True if [a, a + na) and [b, b + nb) share a byte (false if either is empty or NULL).
+bool overlaps(const void* a, size_t na, const void* b, size_t nb);
+// True if [p, p + n) shares a byte with any buffer phase `ph` reads or writes: its x (whole
+// dwords), tier bytes, both lists (d_in entries each), counts, blob and y.
+bool phase_touches(const spax_phase& ph, const void* p, size_t n);
 // The fused mask+GEMV kernel keeps the activations and its list slices in LDS.
 constexpr int32_t kFusedMaxDin = 16384;
 constexpr size_t kFusedMaxDynLds = 48 * 1024;

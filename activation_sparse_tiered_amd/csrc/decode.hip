@@ -354,11 +354,9 @@ GemvPlan fused_plan(const spax_layout* L) {
   GemvPlan p{};
   const int64_t T = L->d_out_total;
   p.n_tiles = (int32_t)((T + kTileRows - 1) / kTileRows);
-  static const int target = [] {
-    const char* v = getenv("SPAX_FUSED_WGS");
-    return v ? atoi(v) : 0;
-  }();
-  const int wgs = (target > 1 ? target : cu_count()) - 1;  // one more writes the mask outputs
+  // More workgroups than compute units measured slower (a second resident workgroup per CU
+  // shares its LDS and issue slots with the first).
+  const int wgs = cu_count() - 1;  // one more writes the mask outputs
   int k = wgs / p.n_tiles;
   const int kmax = L->d_in / 16 > 1 ? L->d_in / 16 : 1;
   if (k > kmax) k = kmax;
@@ -380,12 +378,22 @@ FusedLds fused_lds(const spax_layout* L, const GemvPlan& plan) {
   return f;
 }
 
+}  // namespace
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
   const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
   return pa < pb + nb && pb < pa + na;
 }
 
-}  // namespace
+bool phase_touches(const spax_phase& ph, const void* p, size_t n) {
+  const spax_layout* L = ph.layout;
+  const size_t d = (size_t)L->d_in;
+  return overlaps(ph.x, 4 * ((d + 1) / 2), p, n) || overlaps(ph.tier, d, p, n) ||
+         overlaps(ph.full_idx, 4 * d, p, n) || overlaps(ph.approx_idx, 4 * d, p, n) ||
+         overlaps(ph.counts, 12, p, n) || overlaps(ph.packed, (size_t)L->total_bytes, p, n) ||
+         overlaps(ph.y, 4 * (size_t)L->d_out_total, p, n);
+}
 
 bool fused_phase_ok(const spax_layout* L) {
   if (L->d_in > kFusedMaxDin) return false;
@@ -397,20 +405,26 @@ int launch_decode_step(const spax_step* st, hipStream_t s) {
   const int n = st->n_phases;
   const bool separate = (st->flags & SPAX_STEP_SEPARATE) != 0;
   auto fused_phase_ok = [&](const spax_layout* L) { return !separate && spax::fused_phase_ok(L); };
+  auto plan_of = [&](const spax_layout* L) { return fused_phase_ok(L) ? fused_plan(L) : gemv_plan(L); };
+  // Launch i clears the y of phase i + 1 as a side job only when phase i is one fused launch,
+  // phase i + 1 accumulates through atomics, and that y shares no byte with anything phase i
+  // reads or writes: under stream order phase i + 1 may reuse phase i's buffers, and its y
+  // must not be zeroed while launch i still uses them.  Otherwise phase i + 1 clears its own
+  // y with a kernel right before its launch.
+  auto clears_next = [&](int i) {
+    if (i + 1 >= n) return false;
+    const spax_phase& nx = st->phases[i + 1];
+    return fused_phase_ok(st->phases[i].layout) && plan_of(nx.layout).n_chunks > 1 &&
+           !phase_touches(st->phases[i], nx.y, 4 * (size_t)nx.layout->d_out_total);
+  };
   for (int i = 0; i < n; ++i) {
     const spax_phase& ph = st->phases[i];
     const spax_layout* L = ph.layout;
     TierArgs ta;
     tier_args_from_params(&ph.params, L->d_in, &ta);
-    const GemvPlan plan = fused_phase_ok(L) ? fused_plan(L) : gemv_plan(L);
-    const size_t ybytes = (size_t)L->d_out_total * 4;
+    const GemvPlan plan = plan_of(L);
     // Was this group's y cleared by the previous launch?
-    bool cleared = false;
-    if (i > 0) {
-      const spax_phase& pp = st->phases[i - 1];
-      cleared = fused_phase_ok(pp.layout) && plan.n_chunks > 1 &&
-                !overlaps(pp.y, (size_t)pp.layout->d_out_total * 4, ph.y, ybytes);
-    }
+    bool cleared = i > 0 && clears_next(i - 1);
     if (!fused_phase_ok(L)) {
       // Large input vectors: stand-alone mask kernel (which clears y) + GEMV.
       const bool clear_in_mask = plan.n_chunks > 1 && L->d_out_total <= kMaskClearMax && !cleared;
@@ -447,13 +461,10 @@ int launch_decode_step(const spax_step* st, hipStream_t s) {
     a.y = ph.y;
     a.y_next = nullptr;
     a.n_next4 = 0;
-    if (i + 1 < n) {
+    if (clears_next(i)) {
       const spax_phase& nx = st->phases[i + 1];
-      const GemvPlan np = fused_phase_ok(nx.layout) ? fused_plan(nx.layout) : gemv_plan(nx.layout);
-      if (np.n_chunks > 1 && !overlaps(ph.y, ybytes, nx.y, (size_t)nx.layout->d_out_total * 4)) {
-        a.y_next = reinterpret_cast<float4*>(nx.y);
-        a.n_next4 = (int32_t)((nx.layout->d_out_total + 3) / 4);  // rows <= 2^24
-      }
+      a.y_next = reinterpret_cast<float4*>(nx.y);
+      a.n_next4 = (int32_t)((nx.layout->d_out_total + 3) / 4);  // rows <= 2^24
     }
     const FusedLds f = fused_lds(L, plan);
     a.wave_cap = f.wave_cap;

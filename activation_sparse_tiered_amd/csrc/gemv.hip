@@ -12,7 +12,6 @@
 // fence writes back and invalidates the L2 of the caller's XCD.  The order in which chunks
 // land is not fixed, so y may differ in the last bits between runs.
 #include <algorithm>
-#include <cstdlib>
 
 #include "gemv_core.h"
 
@@ -138,21 +137,15 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ p, i
   if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
-}
-
 }  // namespace
 
 GemvPlan gemv_plan(const spax_layout* L) {
   GemvPlan p{};
   const int64_t T = L->d_out_total;
   p.n_tiles = (int32_t)((T + kTileRows - 1) / kTileRows);
-  // Split-K: aim for about `target` resident workgroups, but keep >= 16 input channels per
-  // chunk.
-  static const int target = env_int("SPAX_GEMV_TARGET_WGS", 1024);
+  // Split-K: aim for about 1024 workgroups (four per compute unit), but keep >= 16 input
+  // channels per chunk.
+  constexpr int target = 1024;
   int k = (target + p.n_tiles / 2) / p.n_tiles;
   const int kmax = L->d_in / 16 > 1 ? L->d_in / 16 : 1;
   if (k > kmax) k = kmax;

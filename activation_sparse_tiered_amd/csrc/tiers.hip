@@ -5,14 +5,14 @@
 // lives in mask_core.h; this kernel writes the tier bytes, both ascending index lists and
 // the counts to global memory.
 #include <climits>
-#include <cstdlib>
 
 #include "mask_core.h"
 
 namespace spax {
 namespace {
 
-constexpr int kTierThreadsDefault = 1024;
+// One workgroup of 16 waves: the kernel is issue- and latency-bound inside one CU.
+constexpr int kTierThreads = 1024;
 
 template <int NT>
 __global__ __launch_bounds__(NT) void build_tiers_kernel(
@@ -34,21 +34,8 @@ int launch_build_tiers(const TierArgs& a, const uint16_t* x, uint8_t* tier, int3
                        hipStream_t s) {
   const int32_t n4 = y_zero ? (int32_t)((n_zero + 3) / 4) : 0;
   float4* yz = reinterpret_cast<float4*>(y_zero);
-  // Workgroup size: the kernel is issue- and latency-bound inside one CU.
-  static const int nt = [] {
-    const char* v = getenv("SPAX_TIER_THREADS");
-    const int t = v ? atoi(v) : 0;
-    return (t == 256 || t == 512 || t == 1024) ? t : kTierThreadsDefault;
-  }();
-  if (nt == 256)
-    hipLaunchKernelGGL(build_tiers_kernel<256>, dim3(1), dim3(256), 0, s, a, x, tier, full_idx,
-                       approx_idx, counts, yz, n4);
-  else if (nt == 512)
-    hipLaunchKernelGGL(build_tiers_kernel<512>, dim3(1), dim3(512), 0, s, a, x, tier, full_idx,
-                       approx_idx, counts, yz, n4);
-  else
-    hipLaunchKernelGGL(build_tiers_kernel<1024>, dim3(1), dim3(1024), 0, s, a, x, tier, full_idx,
-                       approx_idx, counts, yz, n4);
+  hipLaunchKernelGGL(build_tiers_kernel<kTierThreads>, dim3(1), dim3(kTierThreads), 0, s, a, x,
+                     tier, full_idx, approx_idx, counts, yz, n4);
   SPAX_HIP_CHECK(hipGetLastError());
   return SPAX_OK;
 }
