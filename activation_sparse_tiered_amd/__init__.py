@@ -19,6 +19,7 @@ from ._lib import (FMT_FP16, FMT_INT4, MAX_DIN, MAX_MATS, MODE_THRESHOLD, MODE_T
 __all__ = [
     "spax_layout_init", "spax_pack_columns", "spax_build_tiers", "spax_gemv_workspace_bytes",
     "spax_tiered_gemv", "spax_step_workspace_bytes", "spax_decode_step_projections",
+    "spax_decode_step_projections_noalloc",
     "spax_key_threshold", "spax_counts_from_fractions", "spax_guided_bounds", "spax_version",
     "spax_column_ranges", "spax_pinned_workspace_bytes", "spax_tiered_gemv_pinned", "MoveStats",
     "spax_read_probe",
@@ -188,10 +189,7 @@ def spax_step_workspace_bytes(phases) -> int:
     return int(lib.spax_step_workspace_bytes(arr, len(arr)))
 
 
-def spax_decode_step_projections(phases, ws, ws_bytes: int | None = None, flags: int = 0,
-                                 stream=None, events=None) -> None:
-    """``events``: optional list of 2 * n_phases torch.cuda.Event(enable_timing=True);
-    events[2i] -> events[2i+1] then brackets phase i's GEMV launch on the stream."""
+def _step(phases, ws, ws_bytes, flags, events):
     arr = phases if isinstance(phases, C.Array) else phase_array(phases)
     if ws_bytes is None:
         ws_bytes = _nbytes(ws)
@@ -206,8 +204,28 @@ def spax_decode_step_projections(phases, ws, ws_bytes: int | None = None, flags:
             raise ValueError("need 2 * n_phases events")
         ev = (C.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
         st.events = C.cast(ev, C.POINTER(C.c_void_p))
+        st._keep = (arr, ev)
+    else:
+        st._keep = (arr,)
+    return st
+
+
+def spax_decode_step_projections(phases, ws, ws_bytes: int | None = None, flags: int = 0,
+                                 stream=None, events=None) -> None:
+    """``events``: optional list of 2 * n_phases torch.cuda.Event(enable_timing=True);
+    events[2i] -> events[2i+1] then brackets phase i's GEMV launch on the stream."""
+    st = _step(phases, ws, ws_bytes, flags, events)
     check(lib.spax_decode_step_projections(C.byref(st), _stream(stream)),
           "spax_decode_step_projections")
+
+
+def spax_decode_step_projections_noalloc(phases, flags: int = 0, stream=None,
+                                         events=None) -> None:
+    """The same step with no workspace: the batched form keeps its descriptor tables in the
+    library's static device scratch (calls on one GPU must not overlap)."""
+    st = _step(phases, None, 0, flags, events)
+    check(lib.spax_decode_step_projections_noalloc(C.byref(st), _stream(stream)),
+          "spax_decode_step_projections_noalloc")
 
 
 # ------------------------------------------------------------------ diagnostics

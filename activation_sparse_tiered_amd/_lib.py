@@ -99,6 +99,7 @@ def _load():
         "spax_tiered_gemv": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, P, C.c_size_t, P]),
         "spax_step_workspace_bytes": (C.c_size_t, [C.POINTER(Phase), C.c_int32]),
         "spax_decode_step_projections": (C.c_int, [C.POINTER(Step), P]),
+        "spax_decode_step_projections_noalloc": (C.c_int, [C.POINTER(Step), P]),
         "spax_column_ranges": (C.c_int, [P, C.c_int32, C.c_int32, P, P, C.POINTER(C.c_int32)]),
         "spax_pinned_workspace_bytes": (C.c_size_t, [C.POINTER(Layout)]),
         "spax_tiered_gemv_pinned": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, C.c_int32,

@@ -115,6 +115,51 @@ int check_gemv_args(const spax_layout* L, const void* packed, const uint16_t* x,
   return SPAX_OK;
 }
 
+// Every check of spax_decode_step_projections, before anything is enqueued.  noalloc: the
+// workspace is not used (the batched form's tables go to the static scratch, whose size
+// bounds the number of phases).
+int validate_step(const spax_step* step, bool noalloc) {
+  if (!step || !step->phases) return fail(SPAX_ERR_NULL, "step and step->phases are required");
+  if (step->n_phases < 1) return fail(SPAX_ERR_SHAPE, "n_phases %d < 1", step->n_phases);
+  if (step->flags & ~(SPAX_STEP_SEPARATE | SPAX_STEP_BATCHED))
+    return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags 0x%x", step->flags);
+  const bool batched = (step->flags & SPAX_STEP_BATCHED) != 0;
+  if (batched && (step->flags & SPAX_STEP_SEPARATE))
+    return fail(SPAX_ERR_PARAM, "SPAX_STEP_BATCHED cannot be combined with SPAX_STEP_SEPARATE");
+  // The per-phase GEMV needs no workspace (checked against a size of 0 when none is used).
+  const void* ws = noalloc ? nullptr : step->ws;
+  const size_t ws_bytes = noalloc ? 0 : step->ws_bytes;
+  for (int i = 0; i < step->n_phases; ++i) {
+    const spax_phase& ph = step->phases[i];
+    if (!ph.layout) return fail(SPAX_ERR_NULL, "phase %d: layout is NULL", i);
+    int st = check_tier_outputs(ph.x, ph.layout->d_in, ph.full_idx, ph.approx_idx, ph.counts);
+    if (st) return phase_fail(st, i);
+    TierArgs a;
+    st = tier_args_from_params(&ph.params, ph.layout->d_in, &a);
+    if (st) return phase_fail(st, i);
+    GemvPlan plan;
+    st = check_gemv_args(ph.layout, ph.packed, ph.x, ph.full_idx, ph.approx_idx, ph.counts, ph.y,
+                         ws, ws_bytes, &plan);
+    if (st) return phase_fail(st, i);
+    st = check_phase_aliasing(ph);
+    if (st) return phase_fail(st, i);
+  }
+  if (batched) {
+    const size_t need = batched_workspace_bytes(step->n_phases);
+    if (noalloc) {
+      if (need > kStaticScratchBytes)
+        return fail(SPAX_ERR_WORKSPACE, "SPAX_STEP_BATCHED over %d phases needs %zu bytes of "
+                    "tables; the static scratch holds %zu", step->n_phases, need,
+                    kStaticScratchBytes);
+    } else if (!step->ws || step->ws_bytes < need) {
+      return fail(SPAX_ERR_WORKSPACE, "SPAX_STEP_BATCHED needs a workspace of %zu bytes", need);
+    }
+    int st = check_independent(step);
+    if (st) return st;
+  }
+  return SPAX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -214,37 +259,16 @@ size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases) {
 
 int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
   clear_error();
-  if (!step || !step->phases) return fail(SPAX_ERR_NULL, "step and step->phases are required");
-  if (step->n_phases < 1) return fail(SPAX_ERR_SHAPE, "n_phases %d < 1", step->n_phases);
-  if (step->flags & ~(SPAX_STEP_SEPARATE | SPAX_STEP_BATCHED))
-    return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags 0x%x", step->flags);
-  const bool batched = (step->flags & SPAX_STEP_BATCHED) != 0;
-  if (batched && (step->flags & SPAX_STEP_SEPARATE))
-    return fail(SPAX_ERR_PARAM, "SPAX_STEP_BATCHED cannot be combined with SPAX_STEP_SEPARATE");
-  // Validate every phase before enqueueing anything.
-  for (int i = 0; i < step->n_phases; ++i) {
-    const spax_phase& ph = step->phases[i];
-    if (!ph.layout) return fail(SPAX_ERR_NULL, "phase %d: layout is NULL", i);
-    int st = check_tier_outputs(ph.x, ph.layout->d_in, ph.full_idx, ph.approx_idx, ph.counts);
-    if (st) return phase_fail(st, i);
-    TierArgs a;
-    st = tier_args_from_params(&ph.params, ph.layout->d_in, &a);
-    if (st) return phase_fail(st, i);
-    GemvPlan plan;
-    st = check_gemv_args(ph.layout, ph.packed, ph.x, ph.full_idx, ph.approx_idx, ph.counts, ph.y,
-                         step->ws, step->ws_bytes, &plan);
-    if (st) return phase_fail(st, i);
-    st = check_phase_aliasing(ph);
-    if (st) return phase_fail(st, i);
-  }
-  if (batched) {
-    const size_t need = batched_workspace_bytes(step->n_phases);
-    if (!step->ws || step->ws_bytes < need)
-      return fail(SPAX_ERR_WORKSPACE, "SPAX_STEP_BATCHED needs a workspace of %zu bytes", need);
-    int st = check_independent(step);
-    if (st) return st;
-  }
-  return launch_decode_step(step, stream);
+  int st = validate_step(step, false);
+  if (st) return st;
+  return launch_decode_step(step, stream, false);
+}
+
+int spax_decode_step_projections_noalloc(const spax_step* step, hipStream_t stream) {
+  clear_error();
+  int st = validate_step(step, true);
+  if (st) return st;
+  return launch_decode_step(step, stream, true);
 }
 
 }  // extern "C"

@@ -183,15 +183,12 @@ int stage_and_copy(const void* src, size_t bytes, void* dst, hipStream_t s) {
   return SPAX_OK;
 }
 
-}  // namespace
-
-size_t batched_workspace_bytes(int n_phases) { return n_phases > 0 ? table_bytes(n_phases) : 0; }
-
-int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s) {
+// The descriptor tables of a batched step, written into `table` (table_bytes(n) bytes).
+// Returns the number of GEMV work items, or -1 (error set) if there are too many.
+int64_t build_tables(const spax_step* st, char* table) {
   const int n = st->n_phases;
-  std::vector<char> table(table_bytes(n));
-  MaskDesc* md = reinterpret_cast<MaskDesc*>(table.data());
-  GemvDesc* gd = reinterpret_cast<GemvDesc*>(table.data() + aligned_size((size_t)n * sizeof(MaskDesc)));
+  MaskDesc* md = reinterpret_cast<MaskDesc*>(table);
+  GemvDesc* gd = reinterpret_cast<GemvDesc*>(table + aligned_size((size_t)n * sizeof(MaskDesc)));
   int64_t items = 0;
   for (int i = 0; i < n; ++i) {
     const spax_phase& ph = st->phases[i];
@@ -220,11 +217,19 @@ int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s) {
     gd[i] = g;
     items += (int64_t)plan.n_tiles * plan.n_chunks;
   }
-  if (items > INT32_MAX) return fail(SPAX_ERR_SHAPE, "too many work items (%lld)", (long long)items);
-  int rc = stage_and_copy(table.data(), table.size(), st->ws, s);
-  if (rc) return rc;
-  const auto* dmd = static_cast<const MaskDesc*>(st->ws);
-  const auto* dgd = reinterpret_cast<const GemvDesc*>(static_cast<const char*>(st->ws) +
+  if (items > INT32_MAX) {
+    fail(SPAX_ERR_SHAPE, "too many work items (%lld)", (long long)items);
+    return -1;
+  }
+  return items;
+}
+
+// The two launches over tables already on the device (in stream order).
+int launch_from_tables(const spax_step* st, int n_cu, const void* dtables, int64_t items,
+                       hipStream_t s) {
+  const int n = st->n_phases;
+  const auto* dmd = static_cast<const MaskDesc*>(dtables);
+  const auto* dgd = reinterpret_cast<const GemvDesc*>(static_cast<const char*>(dtables) +
                                                       aligned_size((size_t)n * sizeof(MaskDesc)));
   // events (optional): [0, 1] bracket the mask launch and [2, 3] the GEMV launch; with one
   // phase, [0, 1] bracket both.
@@ -253,6 +258,68 @@ int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s) {
   }
   if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[four ? 3 : 1], s));
   return SPAX_OK;
+}
+
+// ---- the entry point that allocates nothing: descriptor tables in a file-scope device array
+//
+// Each device holds its own copy of `scratch`; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name in host code is a
+// host-side stand-in, not a device address).  The host side of the tables is one static
+// buffer, reused after the event of its last copy has completed.
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+struct StaticScratch {
+  std::mutex mu;
+  void* dev_ptr[64] = {};           // scratch on each device
+  hipEvent_t copied[64] = {};       // the last table copy from `host` to that device
+  bool pending[64] = {};
+  alignas(256) char host[kStaticScratchBytes];
+};
+StaticScratch g_static;
+
+}  // namespace
+
+size_t batched_workspace_bytes(int n_phases) { return n_phases > 0 ? table_bytes(n_phases) : 0; }
+
+int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s) {
+  const int n = st->n_phases;
+  std::vector<char> table(table_bytes(n));
+  const int64_t items = build_tables(st, table.data());
+  if (items < 0) return SPAX_ERR_SHAPE;
+  int rc = stage_and_copy(table.data(), table.size(), st->ws, s);
+  if (rc) return rc;
+  return launch_from_tables(st, n_cu, st->ws, items, s);
+}
+
+int launch_decode_step_batched_static(const spax_step* st, int n_cu, hipStream_t s) {
+  const size_t bytes = table_bytes(st->n_phases);
+  if (bytes > kStaticScratchBytes)
+    return fail(SPAX_ERR_WORKSPACE, "%d phases need %zu bytes of descriptor tables; the static "
+                "scratch holds %zu", st->n_phases, bytes, kStaticScratchBytes);
+  int dev = 0;
+  SPAX_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(SPAX_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_static.mu);
+  if (!g_static.dev_ptr[dev]) {  // once per device, with that device current
+    void* p = nullptr;
+    SPAX_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(SPAX_ERR_HIP, "hipGetSymbolAddress returned NULL for the scratch");
+    SPAX_HIP_CHECK(hipEventCreateWithFlags(&g_static.copied[dev], hipEventDisableTiming));
+    g_static.dev_ptr[dev] = p;
+  }
+  // The host buffer is shared by every device: wait for each copy still reading it.
+  for (int d = 0; d < 64; ++d) {
+    if (!g_static.pending[d]) continue;
+    SPAX_HIP_CHECK(hipEventSynchronize(g_static.copied[d]));
+    g_static.pending[d] = false;
+  }
+  const int64_t items = build_tables(st, g_static.host);
+  if (items < 0) return SPAX_ERR_SHAPE;
+  void* dtables = g_static.dev_ptr[dev];
+  SPAX_HIP_CHECK(hipMemcpyAsync(dtables, g_static.host, bytes, hipMemcpyHostToDevice, s));
+  SPAX_HIP_CHECK(hipEventRecord(g_static.copied[dev], s));
+  g_static.pending[dev] = true;
+  return launch_from_tables(st, n_cu, dtables, items, s);
 }
 
 }  // namespace spax

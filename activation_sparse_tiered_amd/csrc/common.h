@@ -80,11 +80,15 @@ bool phase_touches(const spax_phase& ph, const void* p, size_t n);
 constexpr int32_t kFusedMaxDin = 16384;
 constexpr size_t kFusedMaxDynLds = 48 * 1024;
 bool fused_phase_ok(const spax_layout* L);
-// Enqueue a validated step.
-int launch_decode_step(const spax_step* st, hipStream_t s);
 // SPAX_STEP_BATCHED: workspace for the descriptor tables, and the two launches.
 size_t batched_workspace_bytes(int n_phases);
 int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s);
+// The same with the descriptor tables in the library's static device scratch (no workspace,
+// no allocation); at most kStaticScratchBytes of tables.
+constexpr size_t kStaticScratchBytes = 256 * 1024;
+int launch_decode_step_batched_static(const spax_step* st, int n_cu, hipStream_t s);
+// Enqueue a validated step; noalloc: the batched form takes its tables from the static scratch.
+int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc);
 
 inline size_t aligned_size(size_t b) { return (b + 255) / 256 * 256; }
 

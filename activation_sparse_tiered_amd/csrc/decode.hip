@@ -400,8 +400,10 @@ bool fused_phase_ok(const spax_layout* L) {
   return fused_lds(L, fused_plan(L)).bytes <= kFusedMaxDynLds;
 }
 
-int launch_decode_step(const spax_step* st, hipStream_t s) {
-  if (st->flags & SPAX_STEP_BATCHED) return launch_decode_step_batched(st, cu_count(), s);
+int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
+  if (st->flags & SPAX_STEP_BATCHED)
+    return noalloc ? launch_decode_step_batched_static(st, cu_count(), s)
+                   : launch_decode_step_batched(st, cu_count(), s);
   const int n = st->n_phases;
   const bool separate = (st->flags & SPAX_STEP_SEPARATE) != 0;
   auto fused_phase_ok = [&](const spax_layout* L) { return !separate && spax::fused_phase_ok(L); };

@@ -294,6 +294,30 @@ def test_step_rejects_aliasing_within_a_phase(flags):
 
 
 @needs_no_gpu
+def test_noalloc_step_validation():
+    """spax_decode_step_projections_noalloc validates like the step with a workspace (every
+    phase first), ignores the workspace, and rejects a batched step whose tables exceed the
+    static scratch."""
+    MB = 1 << 20
+    L = spax.spax_layout_init(64, [512], 0, 128, 64)
+    good = _fake_phase(L, spax.topk_params(4, 4))
+    bad = _fake_phase(L, spax.topk_params(40, 40))
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections_noalloc([good, good, bad], stream=0)
+    assert e.value.status == _lib.SPAX_ERR_PARAM and "phase 2" in str(e.value)
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections_noalloc([good], flags=3, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_PARAM
+    many = [_fake_phase(L, spax.topk_params(4, 4), 0, tier=FAKE + 64 * MB + 4096 * i,
+                        f=FAKE + 128 * MB + 4096 * i, a=FAKE + 192 * MB + 4096 * i,
+                        c=FAKE + 256 * MB + 4096 * i, y=FAKE + 320 * MB + 4096 * i)
+            for i in range(1300)]
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections_noalloc(many, flags=2, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_WORKSPACE and "static scratch" in str(e.value)
+
+
+@needs_no_gpu
 def test_batched_step_rejects_output_on_another_phase_blob():
     MB = 1 << 20
     L = spax.spax_layout_init(64, [512], 0, 128, 64)
