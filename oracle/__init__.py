@@ -18,7 +18,8 @@ What it computes, and where that is defined:
 * "TopK-Guided: Adaptive, Budget-Aware Activation Sparsity for Efficient LLM
   Inference" (arXiv:2610.01763), section 2.1 "TopK-Guided Masking": a per-token
   natural sparsity estimated from a calibrated threshold, clipped to +-delta around the
-  target, then TopK.
+  target, then TopK; section 2.2 and Appendix D: per-block targets from measured
+  sensitivity and a greedy split of a block's target over its projections.
 
 Modules:
 
@@ -28,7 +29,10 @@ Modules:
 * :mod:`oracle.quant`  -- min-max round-to-nearest group quantizer (2-bit and 4-bit).
 * :mod:`oracle.pack`   -- byte-exact column-major packed blob and its decoder.
 * :mod:`oracle.gemv`   -- float64 tiered GEMV, from the fp16 master and from a blob.
-* :mod:`oracle.ranges` -- merged column ranges for the host-resident path.
+* :mod:`oracle.ranges` -- merged column ranges for the host-resident path, and the bytes
+  physically read from block storage.
+* :mod:`oracle.budgets` -- sensitivity-aware block targets and the greedy per-projection
+  allocation that produce the per-phase TopK-Guided targets.
 * :mod:`oracle.decode` -- one decode step over several projections.
 
 Floating point: the GEMV is float64.  Where floating point decides an integer (a
@@ -41,4 +45,4 @@ round-to-nearest is the quantizer the SpAx authors used (the pages do not say; o
 quantizer's internal consistency and its error bound are pinned), and model quality.
 """
 
-from . import tiers, quant, pack, gemv, ranges, decode  # noqa: F401
+from . import tiers, quant, pack, gemv, ranges, decode, budgets  # noqa: F401

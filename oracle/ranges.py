@@ -10,6 +10,13 @@ that bytes selected and bytes physically moved be counted apart.
 Reading (listed in the design doc): a range is a maximal run of consecutive selected channels
 of one tier, in the packed (channel) order; two runs whose gap is at most ``gap``
 unselected channels are merged, and the gap columns are moved too.
+
+Storage granularity (same paragraph: coarse storage granularity can move more bytes than a
+selected column needs; last paragraph: for NVMe, selected bytes and bytes physically read
+are separate entries).  Reading (listed in the design doc): the blob sits on a device read in
+blocks of ``block`` bytes, the blob starting on a block boundary; each merged range is one
+read request, and a request reads every block its bytes touch.  Two requests that touch one
+block each read it.
 """
 
 from __future__ import annotations
@@ -47,3 +54,21 @@ def compact_positions(ranges):
             slot += 1
     return out
 
+
+def storage_ledger(full_idx, approx_idx, stride_F: int, stride_A: int, off_A: int,
+                   block: int, gap: int = 0):
+    """Bytes selected, bytes of the merged record ranges, and bytes physically read at a
+    storage granularity of ``block`` bytes, with the counts of ranges and blocks."""
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    reads = []
+    for idx, stride, off in ((full_idx, stride_F, 0), (approx_idx, stride_A, off_A)):
+        for first, count in runs(idx, gap):
+            begin = off + first * stride
+            end = begin + count * stride
+            reads.append((begin // block, -(-end // block)))   # blocks [b0, b1)
+    led = ledger(full_idx, approx_idx, stride_F, stride_A, gap)
+    n_blocks = sum(b1 - b0 for b0, b1 in reads)
+    return {"selected_bytes": led["selected_bytes"], "moved_bytes": led["moved_bytes"],
+            "read_bytes": n_blocks * block, "n_ranges": led["n_ranges"],
+            "n_blocks": n_blocks}
