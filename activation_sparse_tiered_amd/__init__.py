@@ -13,8 +13,9 @@ import ctypes as C
 STEP_DEFAULT, STEP_SEPARATE, STEP_BATCHED = 0, 1, 2
 
 from ._lib import (FMT_FP16, FMT_INT4, MAX_DIN, MAX_MATS, MODE_THRESHOLD, MODE_TOPK,  # noqa: F401
-                   MODE_TOPK_GUIDED, TIER_APPROX, TIER_FULL, TIER_SKIP, Layout, MoveStats,
-                   Phase, SpaxError, Step, TierParams, check, lib, LIB_PATH)
+                   MODE_TOPK_GUIDED, TIER_APPROX, TIER_FULL, TIER_SKIP, BLOCK_ERROR_FN,
+                   SPAX_ERR_WORKSPACE, Layout, MoveStats, Phase, SpaxError, Step, StorageStats,
+                   TierParams, check, lib, LIB_PATH)
 
 __all__ = [
     "spax_layout_init", "spax_pack_columns", "spax_build_tiers", "spax_gemv_workspace_bytes",
@@ -22,7 +23,8 @@ __all__ = [
     "spax_decode_step_projections_noalloc",
     "spax_key_threshold", "spax_counts_from_fractions", "spax_guided_bounds", "spax_version",
     "spax_column_ranges", "spax_pinned_workspace_bytes", "spax_tiered_gemv_pinned", "MoveStats",
-    "spax_read_probe",
+    "spax_read_probe", "spax_storage_ledger", "StorageStats", "spax_block_sparsity",
+    "spax_greedy_allocation", "spax_allocation_at",
     "topk_params", "threshold_params", "guided_params", "make_phase", "Layout", "TierParams",
     "Phase", "Step", "SpaxError", "LIB_PATH",
 ]
@@ -137,6 +139,20 @@ def spax_column_ranges(idx, gap: int = 0):
     return [(int(first[i]), int(count[i])) for i in range(nr.value)]
 
 
+def spax_storage_ledger(layout: Layout, full_idx, approx_idx, gap: int = 0,
+                        block_bytes: int = 4096) -> StorageStats:
+    """Bytes selected against bytes physically read at a storage granularity (host lists)."""
+    import numpy as np
+    f = np.ascontiguousarray(np.asarray(full_idx, dtype=np.int32))
+    a = np.ascontiguousarray(np.asarray(approx_idx, dtype=np.int32))
+    out = StorageStats()
+    check(lib.spax_storage_ledger(C.byref(layout), f.ctypes.data if f.size else None,
+                                  int(f.size), a.ctypes.data if a.size else None, int(a.size),
+                                  int(gap), int(block_bytes), C.byref(out)),
+          "spax_storage_ledger")
+    return out
+
+
 def spax_pinned_workspace_bytes(layout: Layout) -> int:
     return int(lib.spax_pinned_workspace_bytes(C.byref(layout)))
 
@@ -246,6 +262,54 @@ def spax_read_probe(buf, out, nbytes: int | None = None, offset: int = 0, stream
                               int(min(words, 2**31 - 1)), C.byref(n), _stream(stream)),
           "spax_read_probe")
     return int(n.value)
+
+
+# ------------------------------------------------------------------ sparsity budgets (host)
+
+def spax_block_sparsity(sens, s: float, lam: float, s_min: float = 0.05, s_max: float = 0.95):
+    """Per-block sparsity targets from block sensitivities (float64 array)."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(sens, dtype=np.float64))
+    out = np.zeros(max(1, a.size), dtype=np.float64)
+    check(lib.spax_block_sparsity(a.ctypes.data if a.size else None, int(a.size), float(s),
+                                  float(lam), float(s_min), float(s_max), out.ctypes.data),
+          "spax_block_sparsity")
+    return out[:a.size]
+
+
+def spax_greedy_allocation(params, alpha: float, P_max: float, block_error):
+    """The greedy walk's rows as a float64 array [n_rows, 1 + n_mats] (P, then p per matrix).
+    ``block_error(p)``: error of a trial allocation (a float64 array) -> float."""
+    import numpy as np
+    f = np.ascontiguousarray(np.asarray(params, dtype=np.float64))
+    n = int(f.size)
+
+    def _cb(p, n_mats, user):
+        return float(block_error(np.ctypeslib.as_array(p, shape=(n_mats,)).copy()))
+
+    cb = BLOCK_ERROR_FN(_cb)
+    cap = 64
+    while True:
+        rows = np.zeros((cap, 1 + n), dtype=np.float64)
+        nr = C.c_int32()
+        st = lib.spax_greedy_allocation(f.ctypes.data if n else None, n, float(alpha),
+                                        float(P_max), cb, None, rows.ctypes.data, cap,
+                                        C.byref(nr))
+        if st == SPAX_ERR_WORKSPACE and nr.value > cap:
+            cap = nr.value
+            continue
+        check(st, "spax_greedy_allocation")
+        return rows[:nr.value].copy()
+
+
+def spax_allocation_at(rows, target: float):
+    import numpy as np
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.float64))
+    n_mats = r.shape[1] - 1
+    p = np.zeros(max(1, n_mats), dtype=np.float64)
+    check(lib.spax_allocation_at(r.ctypes.data, int(r.shape[0]), int(n_mats), float(target),
+                                 p.ctypes.data), "spax_allocation_at")
+    return p[:n_mats]
 
 
 # ------------------------------------------------------------------ host helpers

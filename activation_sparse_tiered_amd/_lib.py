@@ -57,6 +57,12 @@ class Step(C.Structure):
                 ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("events", C.POINTER(C.c_void_p))]
 
 
+class StorageStats(C.Structure):
+    _fields_ = [("selected_bytes", C.c_int64), ("moved_bytes", C.c_int64),
+                ("read_bytes", C.c_int64), ("n_blocks", C.c_int64), ("n_ranges", C.c_int32),
+                ("reserved0", C.c_int32)]
+
+
 class MoveStats(C.Structure):
     _fields_ = [("selected_bytes", C.c_int64), ("moved_bytes", C.c_int64),
                 ("list_bytes", C.c_int64), ("n_ranges", C.c_int32), ("n_full", C.c_int32),
@@ -74,6 +80,10 @@ def _hip_runtimes():
     except OSError:
         pass
     return out
+
+
+# double (*)(const double* p, int32_t n_mats, void* user)
+BLOCK_ERROR_FN = C.CFUNCTYPE(C.c_double, C.POINTER(C.c_double), C.c_int32, C.c_void_p)
 
 
 def _load():
@@ -102,6 +112,8 @@ def _load():
         "spax_decode_step_projections_noalloc": (C.c_int, [C.POINTER(Step), P]),
         "spax_column_ranges": (C.c_int, [P, C.c_int32, C.c_int32, P, P, C.POINTER(C.c_int32)]),
         "spax_pinned_workspace_bytes": (C.c_size_t, [C.POINTER(Layout)]),
+        "spax_storage_ledger": (C.c_int, [C.POINTER(Layout), P, C.c_int32, P, C.c_int32,
+                                          C.c_int32, C.c_int64, C.POINTER(StorageStats)]),
         "spax_tiered_gemv_pinned": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, C.c_int32,
                                               C.c_int32, P, C.c_size_t, C.POINTER(MoveStats), P]),
         "spax_read_probe": (C.c_int, [P, C.c_size_t, P, C.c_int32, C.POINTER(C.c_int32), P]),
@@ -110,6 +122,12 @@ def _load():
                                                  C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
         "spax_guided_bounds": (C.c_int, [C.c_int32, C.c_double, C.c_double,
                                          C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
+        "spax_block_sparsity": (C.c_int, [P, C.c_int32, C.c_double, C.c_double, C.c_double,
+                                          C.c_double, P]),
+        "spax_greedy_allocation": (C.c_int, [P, C.c_int32, C.c_double, C.c_double,
+                                             BLOCK_ERROR_FN, P, P, C.c_int32,
+                                             C.POINTER(C.c_int32)]),
+        "spax_allocation_at": (C.c_int, [P, C.c_int32, C.c_int32, C.c_double, P]),
         "spax_status_string": (C.c_char_p, [C.c_int]),
         "spax_last_error": (C.c_char_p, []),
         "spax_version": (C.c_char_p, []),

@@ -30,7 +30,7 @@ FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["host.cpp", "api.cpp", "pack.hip", "tiers.hip", "gemv.hip", "decode.hip", "batch.hip",
-           "pinned.cpp", "probe.hip"]
+           "pinned.cpp", "probe.hip", "budgets.cpp"]
 
 
 def hipcc() -> str:

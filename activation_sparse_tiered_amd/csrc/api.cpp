@@ -214,6 +214,27 @@ int spax_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* firs
   return SPAX_OK;
 }
 
+int spax_storage_ledger(const spax_layout* L, const int32_t* full_idx, int32_t n_full,
+                        const int32_t* approx_idx, int32_t n_approx, int32_t gap,
+                        int64_t block_bytes, spax_storage_stats* out) {
+  clear_error();
+  if (!L || !out || (n_full > 0 && !full_idx) || (n_approx > 0 && !approx_idx))
+    return fail(SPAX_ERR_NULL, "layout, out and the non-empty lists are required");
+  if (!layout_ok(L)) return fail(SPAX_ERR_SHAPE, "layout not initialised by spax_layout_init");
+  if (n_full < 0 || n_approx < 0 || n_full > L->d_in || n_approx > L->d_in ||
+      (int64_t)n_full + n_approx > L->d_in)
+    return fail(SPAX_ERR_PARAM, "list lengths (%d, %d) out of range for d_in %d", n_full,
+                n_approx, L->d_in);
+  if (gap < 0 || block_bytes < 1)
+    return fail(SPAX_ERR_PARAM, "gap %d must be >= 0 and block_bytes %lld >= 1", gap,
+                (long long)block_bytes);
+  for (int32_t i = 0; i < n_full; ++i)
+    if (full_idx[i] >= L->d_in) return fail(SPAX_ERR_PARAM, "full_idx[%d] >= d_in", i);
+  for (int32_t i = 0; i < n_approx; ++i)
+    if (approx_idx[i] >= L->d_in) return fail(SPAX_ERR_PARAM, "approx_idx[%d] >= d_in", i);
+  return storage_ledger(L, full_idx, n_full, approx_idx, n_approx, gap, block_bytes, out);
+}
+
 size_t spax_pinned_workspace_bytes(const spax_layout* L) {
   if (!L || !layout_ok(L)) return 0;
   return pinned_workspace_bytes(L);

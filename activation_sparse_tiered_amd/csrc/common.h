@@ -97,6 +97,10 @@ inline size_t aligned_size(size_t b) { return (b + 255) / 256 * 256; }
 int32_t build_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* first,
                             int32_t* count);
 size_t pinned_workspace_bytes(const spax_layout* L);
+// spax_storage_ledger after validation.
+int storage_ledger(const spax_layout* L, const int32_t* full_idx, int32_t n_full,
+                   const int32_t* approx_idx, int32_t n_approx, int32_t gap, int64_t block,
+                   spax_storage_stats* out);
 // Validated arguments; see spax_tiered_gemv_pinned.  host_dev: the device's address of the
 // pinned blob (for SPAX_PINNED_GATHER).
 int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void* host_dev,

@@ -211,6 +211,33 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
   return SPAX_OK;
 }
 
+// Byte ledger of one mask at a storage granularity (host only): each merged range of a region
+// is one read request, rounded out to whole blocks of the blob (which starts on a block
+// boundary).
+int storage_ledger(const spax_layout* L, const int32_t* full_idx, int32_t n_full,
+                   const int32_t* approx_idx, int32_t n_approx, int32_t gap, int64_t block,
+                   spax_storage_stats* out) {
+  spax_storage_stats st{};
+  const struct {
+    const int32_t* idx;
+    int32_t n;
+    int64_t stride, off;
+  } regions[2] = {{full_idx, n_full, L->stride_F, 0}, {approx_idx, n_approx, L->stride_A, L->off_A}};
+  for (const auto& r : regions) {
+    const int nr = for_ranges(r.idx, r.n, gap, [&](int32_t f, int32_t c, int32_t, int32_t) {
+      const int64_t begin = r.off + (int64_t)f * r.stride, end = begin + (int64_t)c * r.stride;
+      st.moved_bytes += (int64_t)c * r.stride;
+      st.n_blocks += (end + block - 1) / block - begin / block;
+    });
+    if (nr < 0) return fail(SPAX_ERR_PARAM, "lists must be ascending, distinct and non-negative");
+    st.n_ranges += nr;
+    st.selected_bytes += (int64_t)r.n * r.stride;
+  }
+  st.read_bytes = st.n_blocks * block;
+  *out = st;
+  return SPAX_OK;
+}
+
 size_t pinned_workspace_bytes(const spax_layout* L) {
   return aligned_size((size_t)L->total_bytes) + 16 * (size_t)L->d_in + 4 * kTotals;
 }

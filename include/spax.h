@@ -211,6 +211,35 @@ int spax_tiered_gemv(const spax_layout* L, const void* packed, const uint16_t* x
 int spax_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* first,
                        int32_t* count, int32_t* n_ranges);
 
+/* Byte ledger of one mask read from block storage (spax_storage_ledger). */
+typedef struct spax_storage_stats {
+  int64_t selected_bytes;  /* n_full * stride_F + n_approx * stride_A                         */
+  int64_t moved_bytes;     /* bytes of the merged record ranges (selected + merged gaps)       */
+  int64_t read_bytes;      /* bytes physically read: n_blocks * block_bytes                    */
+  int64_t n_blocks;        /* blocks read, each range rounded out to block boundaries          */
+  int32_t n_ranges;        /* merged ranges (FULL + APPROX) = read requests                    */
+  int32_t reserved0;
+} spax_storage_stats;
+
+/*
+ * Bytes selected against bytes physically read when the blob sits on block storage (host
+ * helper).  Pages: eigenradar commentary on SpAx, "The route outside GPU memory", third
+ * paragraph (coarse storage granularity can move more bytes than a selected column needs) and
+ * last paragraph (for NVMe, selected bytes and bytes physically read are separate entries);
+ * the SpAx Abstract reports the flash-offloaded case apart.
+ * The blob (laid out by *L) starts on a block boundary; the selected columns of each region
+ * are merged into ranges as by spax_column_ranges (gap); each range is one read request that
+ * reads every block of block_bytes its bytes touch (a block touched by two requests is read
+ * twice).
+ *   full_idx, approx_idx : host, n_full / n_approx ascending distinct channels < d_in.
+ *   out : host.
+ * Errors: SPAX_ERR_NULL, SPAX_ERR_SHAPE (layout not initialised), SPAX_ERR_PARAM (lengths out
+ * of range, gap < 0, block_bytes < 1, a list not ascending / distinct / inside [0, d_in)).
+ */
+int spax_storage_ledger(const spax_layout* L, const int32_t* full_idx, int32_t n_full,
+                        const int32_t* approx_idx, int32_t n_approx, int32_t gap,
+                        int64_t block_bytes, spax_storage_stats* out);
+
 /* Byte account of one spax_tiered_gemv_pinned call. */
 typedef struct spax_move_stats {
   int64_t selected_bytes;  /* n_full * stride_F + n_approx * stride_A                   */
@@ -386,6 +415,52 @@ int spax_counts_from_fractions(int32_t d, double p_full, double p_approx,
 /* TopK-Guided +-delta band on the skip count (section 2.1): n_lo = max(0,
  * ceil(d*(s - delta) - 1e-9)), n_hi = min(d, floor(d*(s + delta) + 1e-9)). */
 int spax_guided_bounds(int32_t d, double s, double delta, int32_t* n_lo, int32_t* n_hi);
+
+/* ---------------------------------------------------------------- sparsity budgets (host) */
+
+/*
+ * Per-block sparsity targets from measured sensitivities (TopK-Guided, arXiv:2610.01763,
+ * section 2.2 "Sensitivity-Aware Block Sparsity": blocks more sensitive than average get less
+ * sparsity, the global budget moves to robust blocks, lambda sets how much moves, targets are
+ * clamped; the pages clamp to [0.05, 0.95]).  Host only.
+ *   sens    : n_blocks finite positive sensitivities (e.g. each block's output change at a
+ *             probe sparsity, from a calibration pass).
+ *   s_block : n_blocks outputs.  u_b = s + lambda * (mean(sens) - sens_b) / mean(sens);
+ *             s_block[b] = min(max(u_b + c, s_min), s_max) with the shift c that makes the
+ *             mean of s_block equal s (c = 0 when nothing is clamped).
+ * Errors: SPAX_ERR_NULL; SPAX_ERR_PARAM (n_blocks < 1, lambda < 0, s outside [s_min, s_max],
+ * a sensitivity not finite and positive).
+ */
+int spax_block_sparsity(const double* sens, int32_t n_blocks, double s, double lambda,
+                        double s_min, double s_max, double* s_block);
+
+/* Block output error of a trial allocation p[0..n_mats) (caller-defined, e.g. measured on
+ * calibration tokens). */
+typedef double (*spax_block_error_fn)(const double* p, int32_t n_mats, void* user);
+
+/*
+ * Greedy split of a block's sparsity over its matrices (TopK-Guided Appendix D "Block-wise
+ * Greedy Sparsity Allocation", Table 4).  Host only.  From p = 0, each round tries one
+ * increment alpha * mean(params) / params[m] on every matrix m that stays <= 1, keeps the one
+ * whose trial allocation has the least block_error (ties: lower m), and records the row
+ * (P, p[0..n_mats)), P = sum params[m] p[m] / sum params[m]; every increment moves P by
+ * alpha / n_mats.  The first row is (0, zeros); the walk stops once P >= P_max or no matrix
+ * can step.  Matrices that share one activation vector share one tier mask, so in a decoder
+ * layer the units are the projection groups (q|k|v, o, gate|up, down).
+ *   rows   : host, cap rows of (1 + n_mats) doubles; n_rows receives the rows recorded.
+ * Errors: SPAX_ERR_NULL, SPAX_ERR_PARAM (n_mats outside 1..64, alpha <= 0, P_max > 1, a
+ * parameter count not finite and positive), SPAX_ERR_WORKSPACE (more rows than cap;
+ * *n_rows then holds the number needed).
+ */
+int spax_greedy_allocation(const double* params, int32_t n_mats, double alpha, double P_max,
+                           spax_block_error_fn block_error, void* user, double* rows,
+                           int32_t cap, int32_t* n_rows);
+
+/* The allocation recorded for a block target (Appendix D: allocations are recorded against
+ * the block's overall sparsity): p = the first row of `rows` whose P >= target (the last row
+ * if none; zeros for target <= 0).  Host only.  Errors: SPAX_ERR_NULL, SPAX_ERR_PARAM. */
+int spax_allocation_at(const double* rows, int32_t n_rows, int32_t n_mats, double target,
+                       double* p);
 
 const char* spax_status_string(int status);
 const char* spax_last_error(void);   /* thread-local; "" if none */
