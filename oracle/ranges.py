@@ -21,6 +21,9 @@ block each read it.
 
 from __future__ import annotations
 
+import numpy as np
+
+
 def runs(sel_idx, gap: int = 0):
     """Ascending channel indices -> list of (first, count) ranges after gap merging."""
     idx = [int(v) for v in sel_idx]
@@ -72,3 +75,18 @@ def storage_ledger(full_idx, approx_idx, stride_F: int, stride_A: int, off_A: in
     return {"selected_bytes": led["selected_bytes"], "moved_bytes": led["moved_bytes"],
             "read_bytes": n_blocks * block, "n_ranges": led["n_ranges"],
             "n_blocks": n_blocks}
+
+
+def placement_order(calib_tiers, stride_F: int, stride_A: int):
+    """Offline placement of the column records (same paragraph: jointly accessed columns are
+    placed together).  Reading (listed in the design doc): from calibration masks (one tier array
+    per calibration token: 2 FULL, 1 APPROX, 0 SKIP), each channel scores the bytes it made
+    selected (stride_F per FULL, stride_A per APPROX); records are placed by descending score,
+    equal scores by channel index.  Returns ``order``: position p of the placed blob holds
+    channel order[p]."""
+    t = np.asarray(calib_tiers)
+    if t.ndim != 2:
+        raise ValueError("calibration tiers must be (tokens, d)")
+    score = ((t == 2).sum(axis=0).astype(np.int64) * stride_F +
+             (t == 1).sum(axis=0).astype(np.int64) * stride_A)
+    return np.lexsort((np.arange(t.shape[1]), -score)).astype(np.int32)

@@ -90,3 +90,47 @@ def test_abi_errors():
         with pytest.raises(spax.SpaxError) as e:
             spax.spax_storage_ledger(L, f, a, gap, block)
         assert e.value.status == _lib.SPAX_ERR_PARAM, (f, a, gap, block)
+
+
+# ---------------------------------------------------------------- placement
+
+def test_placement_hand_worked():
+    """Scores with stride_F = 8192, stride_A = 1152 over three tokens:
+    channel 0: F, F, S -> 16384; 1: A, A, A -> 3456; 2: S, S, S -> 0; 3: F, A, S -> 9344;
+    4: F, F, S -> 16384.  Order: 0, 4 (16384; ties by index), 3, 1, 2."""
+    t = np.array([[2, 1, 0, 2, 2], [2, 1, 0, 1, 2], [0, 1, 0, 0, 0]])
+    assert ranges.placement_order(t, 8192, 1152).tolist() == [0, 4, 3, 1, 2]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_placement_joins_columns_always_used_together(seed):
+    """If every calibration token selects the same FULL set and the same APPROX set, the
+    placed blob holds each set as one contiguous run (FULL first, then APPROX), so each token
+    reads one range per region; and the order is a permutation."""
+    rng = np.random.default_rng(seed)
+    d = int(rng.integers(3, 300))
+    tier = rng.integers(0, 3, d)
+    calib = np.tile(tier, (int(rng.integers(1, 6)), 1))
+    order = ranges.placement_order(calib, 8192, 1152)
+    assert sorted(order.tolist()) == list(range(d))
+    placed = tier[order]                      # the tier of the channel at each position
+    full_pos = np.flatnonzero(placed == 2)
+    apx_pos = np.flatnonzero(placed == 1)
+    assert len(ranges.runs(full_pos)) <= 1 and len(ranges.runs(apx_pos)) <= 1
+    if full_pos.size and apx_pos.size:
+        assert full_pos.max() < apx_pos.min()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_placement_abi_matches_oracle(seed):
+    rng = np.random.default_rng(70 + seed)
+    d = int(rng.integers(1, 5000))
+    L = spax.spax_layout_init(d, [1024], 0, 128, 128)
+    T = int(rng.integers(1, 20))
+    calib = rng.choice([0, 1, 2], size=(T, d), p=[0.5, 0.3, 0.2]).astype(np.uint8)
+    got = spax.spax_placement_order(L, calib)
+    assert np.array_equal(got, ranges.placement_order(calib, int(L.stride_F), int(L.stride_A)))
+    with pytest.raises(spax.SpaxError):
+        bad = calib.copy()
+        bad[0, 0] = 3
+        spax.spax_placement_order(L, bad)
