@@ -18,7 +18,8 @@ from ._lib import (FMT_FP16, FMT_INT4, MAX_DIN, MAX_MATS, MODE_THRESHOLD, MODE_T
                    TierParams, check, lib, LIB_PATH)
 
 __all__ = [
-    "spax_layout_init", "spax_pack_columns", "spax_build_tiers", "spax_gemv_workspace_bytes",
+    "spax_layout_init", "spax_pack_columns", "spax_pack_columns_placed", "spax_placement_order",
+    "spax_build_tiers", "spax_gemv_workspace_bytes",
     "spax_tiered_gemv", "spax_step_workspace_bytes", "spax_decode_step_projections",
     "spax_decode_step_projections_noalloc",
     "spax_key_threshold", "spax_counts_from_fractions", "spax_guided_bounds", "spax_version",
@@ -70,6 +71,26 @@ def spax_pack_columns(layout: Layout, Ws, packed, stream=None) -> None:
     arr = (C.c_void_p * max(1, len(Ws)))(*[_ptr(w) for w in Ws])
     check(lib.spax_pack_columns(C.byref(layout), arr, _ptr(packed), _stream(stream)),
           "spax_pack_columns")
+
+
+def spax_pack_columns_placed(layout: Layout, Ws, perm, packed, stream=None) -> None:
+    """Pack with record p holding column perm[p] (perm: device int32 tensor of d_in)."""
+    arr = (C.c_void_p * max(1, len(Ws)))(*[_ptr(w) for w in Ws])
+    check(lib.spax_pack_columns_placed(C.byref(layout), arr, _ptr(perm), _ptr(packed),
+                                       _stream(stream)), "spax_pack_columns_placed")
+
+
+def spax_placement_order(layout: Layout, tiers):
+    """Placement from calibration masks: ``tiers`` (n_tokens, d_in) uint8 on the host; returns
+    the int32 order (position p holds channel order[p])."""
+    import numpy as np
+    t = np.ascontiguousarray(np.asarray(tiers, dtype=np.uint8))
+    if t.ndim == 1:
+        t = t[None, :]
+    order = np.zeros(int(layout.d_in), dtype=np.int32)
+    check(lib.spax_placement_order(C.byref(layout), t.ctypes.data if t.size else None,
+                                   int(t.shape[0]), order.ctypes.data), "spax_placement_order")
+    return order
 
 
 # ------------------------------------------------------------------ tier masks
@@ -157,7 +178,7 @@ def spax_pinned_workspace_bytes(layout: Layout) -> int:
     return int(lib.spax_pinned_workspace_bytes(C.byref(layout)))
 
 
-PINNED_MEMCPY, PINNED_GATHER = 0, 1
+PINNED_MEMCPY, PINNED_GATHER, PINNED_HOSTGATHER = 0, 1, 2
 
 
 def spax_tiered_gemv_pinned(layout: Layout, packed_host, x, full_idx, approx_idx, counts, y,

@@ -104,6 +104,9 @@ def _load():
     sig = {
         "spax_layout_init": (C.c_int, [C.POINTER(Layout)]),
         "spax_pack_columns": (C.c_int, [C.POINTER(Layout), C.POINTER(C.c_void_p), P, P]),
+        "spax_pack_columns_placed": (C.c_int, [C.POINTER(Layout), C.POINTER(C.c_void_p), P, P,
+                                               P]),
+        "spax_placement_order": (C.c_int, [C.POINTER(Layout), P, C.c_int32, P]),
         "spax_build_tiers": (C.c_int, [P, C.c_int32, C.POINTER(TierParams), P, P, P, P, P]),
         "spax_gemv_workspace_bytes": (C.c_size_t, [C.POINTER(Layout)]),
         "spax_tiered_gemv": (C.c_int, [C.POINTER(Layout), P, P, P, P, P, P, P, C.c_size_t, P]),

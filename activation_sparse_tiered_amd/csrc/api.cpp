@@ -164,9 +164,8 @@ int validate_step(const spax_step* step, bool noalloc) {
 
 extern "C" {
 
-int spax_pack_columns(const spax_layout* L, const uint16_t* const* W, void* packed,
-                      hipStream_t stream) {
-  clear_error();
+namespace {
+int check_pack_args(const spax_layout* L, const uint16_t* const* W, const void* packed) {
   if (!L || !W || !packed) return fail(SPAX_ERR_NULL, "layout, W and packed are required");
   if (!layout_ok(L)) return fail(SPAX_ERR_SHAPE, "layout not initialised by spax_layout_init");
   if (!aligned(packed, 256)) return fail(SPAX_ERR_ALIGN, "packed must be 256-byte aligned");
@@ -174,7 +173,36 @@ int spax_pack_columns(const spax_layout* L, const uint16_t* const* W, void* pack
     if (!W[m]) return fail(SPAX_ERR_NULL, "W[%d] is NULL", m);
     if (!aligned(W[m], 16)) return fail(SPAX_ERR_ALIGN, "W[%d] must be 16-byte aligned", m);
   }
-  return launch_pack(L, W, packed, stream);
+  return SPAX_OK;
+}
+}  // namespace
+
+int spax_pack_columns(const spax_layout* L, const uint16_t* const* W, void* packed,
+                      hipStream_t stream) {
+  clear_error();
+  int st = check_pack_args(L, W, packed);
+  if (st) return st;
+  return launch_pack(L, W, nullptr, packed, stream);
+}
+
+int spax_pack_columns_placed(const spax_layout* L, const uint16_t* const* W,
+                             const int32_t* perm, void* packed, hipStream_t stream) {
+  clear_error();
+  int st = check_pack_args(L, W, packed);
+  if (st) return st;
+  if (!perm) return fail(SPAX_ERR_NULL, "perm is required");
+  if (!aligned(perm, 4)) return fail(SPAX_ERR_ALIGN, "perm must be 4-byte aligned");
+  return launch_pack(L, W, perm, packed, stream);
+}
+
+int spax_placement_order(const spax_layout* L, const uint8_t* tiers, int32_t n_tokens,
+                         int32_t* order) {
+  clear_error();
+  if (!L || !order || (n_tokens > 0 && !tiers))
+    return fail(SPAX_ERR_NULL, "layout, tiers and order are required");
+  if (!layout_ok(L)) return fail(SPAX_ERR_SHAPE, "layout not initialised by spax_layout_init");
+  if (n_tokens < 0) return fail(SPAX_ERR_PARAM, "n_tokens %d < 0", n_tokens);
+  return placement_order(L, tiers, n_tokens, order);
 }
 
 int spax_build_tiers(const uint16_t* x, int32_t d_in, const spax_tier_params* p, uint8_t* tier,
@@ -251,7 +279,8 @@ int spax_tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const
   int st = check_gemv_args(L, packed_host, x, full_idx, approx_idx, counts, y, nullptr, 0, &plan);
   if (st) return st;
   if (gap < 0) return fail(SPAX_ERR_PARAM, "gap %d < 0", gap);
-  if (transfer != SPAX_PINNED_MEMCPY && transfer != SPAX_PINNED_GATHER)
+  if (transfer != SPAX_PINNED_MEMCPY && transfer != SPAX_PINNED_GATHER &&
+      transfer != SPAX_PINNED_HOSTGATHER)
     return fail(SPAX_ERR_PARAM, "unknown transfer %d", transfer);
   if (!ws) return fail(SPAX_ERR_NULL, "ws is required");
   if (!aligned(ws, 256)) return fail(SPAX_ERR_ALIGN, "ws must be 256-byte aligned");

@@ -8,9 +8,10 @@
 // launch and ramp cost, so it shows what the byte account alone allows.
 //
 // Launch 1: one 1024-thread workgroup per phase runs the stand-alone mask (mask_core.h,
-// tiers_to_global) and clears the phase's y.  Launch 2: a persistent grid walks the work items
-// of all phases, (row tile, column chunk) pairs numbered phase after phase, each handled like
-// one workgroup of the stand-alone GEMV (gemv_core.h, gemv_item).  The per-phase arguments
+// tiers_to_global) and clears the phase's y.  Then, per base format present (fp16, int4), one
+// persistent grid walks the work items of that format's phases, (row tile, column chunk)
+// pairs numbered phase after phase, each handled like one workgroup of the stand-alone GEMV
+// (gemv_core.h, gemv_item; an int4 tile is 2048 rows, 32 per lane).  The per-phase arguments
 // reach the device as two descriptor tables copied into the caller's workspace from a
 // library-owned ring of pinned host buffers.
 #include <cstdint>
@@ -98,9 +99,12 @@ __device__ __forceinline__ GemvDesc uniform_desc(const GemvDesc& g) {
   return u;
 }
 
+// The work items of the phases whose base format is FMT (one launch per format present, so
+// each format gets its own register and LDS budget).
+template <int FMT>
 __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDesc* __restrict__ gd,
                                                                     int n_phases, int n_items) {
-  __shared__ float red[gemv::kWaves][kTileRows];
+  __shared__ float red[gemv::kWaves * gemv::ItemRows<FMT>::tile];
   // Item i runs on XCD i % 8 (the grid is a multiple of 8 or holds one item per
   // workgroup), so the XCD-aware order applies to the item index.  Only the speed depends on
   // this: the order is a bijection whatever the grid.
@@ -111,12 +115,8 @@ __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDe
     const int local = item - g.item0;
     const int tile = (int)((uint32_t)local % (uint32_t)g.sh.n_tiles);
     const int chunk = (int)((uint32_t)local / (uint32_t)g.sh.n_tiles);
-    if (g.fmt == SPAX_FMT_FP16)
-      gemv::gemv_item<SPAX_FMT_FP16>(g.sh, g.packed, g.x32, g.full_idx, g.approx_idx, g.counts,
-                                     g.y, tile, chunk, red);
-    else
-      gemv::gemv_item<SPAX_FMT_INT4>(g.sh, g.packed, g.x32, g.full_idx, g.approx_idx, g.counts,
-                                     g.y, tile, chunk, red);
+    gemv::gemv_item<FMT>(g.sh, g.packed, g.x32, g.full_idx, g.approx_idx, g.counts, g.y, tile,
+                         chunk, red);
     __syncthreads();  // red is reused by the next item
   }
 }
@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDe
 GemvPlan batched_plan(const spax_layout* L) {
   constexpr int channels = 2048;
   GemvPlan p{};
-  p.n_tiles = (int32_t)((L->d_out_total + kTileRows - 1) / kTileRows);
+  const int rows = gemv_tile_rows(L);
+  p.n_tiles = (int32_t)((L->d_out_total + rows - 1) / rows);
   int k = (L->d_in + channels - 1) / channels;
   const int kmax = L->d_in / 16 > 1 ? L->d_in / 16 : 1;
   p.n_chunks = k < 1 ? 1 : (k > kmax ? kmax : k);
@@ -183,13 +184,23 @@ int stage_and_copy(const void* src, size_t bytes, void* dst, hipStream_t s) {
   return SPAX_OK;
 }
 
-// The descriptor tables of a batched step, written into `table` (table_bytes(n) bytes).
-// Returns the number of GEMV work items, or -1 (error set) if there are too many.
-int64_t build_tables(const spax_step* st, char* table) {
+// Work items of a batched step's GEMV launches: the fp16 phases' and the int4 phases'.
+struct BatchItems {
+  int32_t n_phases[2];  // phases per base format (their descriptors: fp16 first, then int4)
+  int64_t items[2];     // work items per base format
+};
+
+// The descriptor tables of a batched step, written into `table` (table_bytes(n) bytes): the
+// mask descriptors in phase order, then the GEMV descriptors grouped by base format (fp16
+// phases first), each group numbering its work items from 0.  Returns false (error set) if
+// there are too many work items.
+bool build_tables(const spax_step* st, char* table, BatchItems* bi) {
   const int n = st->n_phases;
   MaskDesc* md = reinterpret_cast<MaskDesc*>(table);
   GemvDesc* gd = reinterpret_cast<GemvDesc*>(table + aligned_size((size_t)n * sizeof(MaskDesc)));
-  int64_t items = 0;
+  *bi = BatchItems{};
+  for (int i = 0; i < n; ++i) bi->n_phases[st->phases[i].layout->base_fmt == SPAX_FMT_INT4]++;
+  int slot[2] = {0, bi->n_phases[0]};
   for (int i = 0; i < n; ++i) {
     const spax_phase& ph = st->phases[i];
     const spax_layout* L = ph.layout;
@@ -203,6 +214,7 @@ int64_t build_tables(const spax_step* st, char* table) {
     m.y = reinterpret_cast<float4*>(ph.y);
     m.n_zero4 = (int32_t)((L->d_out_total + 3) / 4);
     md[i] = m;
+    const int f = L->base_fmt == SPAX_FMT_INT4;
     const GemvPlan plan = batched_plan(L);
     GemvDesc g{};
     g.sh = gemv_shape(L, plan);
@@ -212,26 +224,47 @@ int64_t build_tables(const spax_step* st, char* table) {
     g.approx_idx = ph.approx_idx;
     g.counts = ph.counts;
     g.y = ph.y;
-    g.item0 = (int32_t)items;
+    g.item0 = (int32_t)bi->items[f];
     g.fmt = L->base_fmt;
-    gd[i] = g;
-    items += (int64_t)plan.n_tiles * plan.n_chunks;
+    gd[slot[f]++] = g;
+    bi->items[f] += (int64_t)plan.n_tiles * plan.n_chunks;
+    if (bi->items[f] > INT32_MAX) {
+      fail(SPAX_ERR_SHAPE, "too many work items (%lld)", (long long)bi->items[f]);
+      return false;
+    }
   }
-  if (items > INT32_MAX) {
-    fail(SPAX_ERR_SHAPE, "too many work items (%lld)", (long long)items);
-    return -1;
-  }
-  return items;
+  return true;
 }
 
-// The two launches over tables already on the device (in stream order).
-int launch_from_tables(const spax_step* st, int n_cu, const void* dtables, int64_t items,
+template <int FMT>
+int launch_gemvs(const GemvDesc* dgd, int n_phases, int64_t items, int n_cu, hipStream_t s) {
+  // as many workgroups as can be resident at once
+  static const int per_cu = [] {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, batched_gemv_kernel<FMT>,
+                                                     kGemvThreads, 0) != hipSuccess || occ < 1)
+      occ = 2;
+    return occ;
+  }();
+  const int64_t cap = (int64_t)n_cu * per_cu;
+  const int64_t grid = items < cap ? items : cap;
+  if (grid > 0) {
+    hipLaunchKernelGGL(batched_gemv_kernel<FMT>, dim3((unsigned)grid), dim3(kGemvThreads), 0, s,
+                       dgd, n_phases, (int)items);
+    SPAX_HIP_CHECK(hipGetLastError());
+  }
+  return SPAX_OK;
+}
+
+// The launches over tables already on the device (in stream order): all masks, then the
+// GEMVs of the fp16 phases and of the int4 phases.
+int launch_from_tables(const spax_step* st, int n_cu, const void* dtables, const BatchItems& bi,
                        hipStream_t s) {
   const int n = st->n_phases;
   const auto* dmd = static_cast<const MaskDesc*>(dtables);
   const auto* dgd = reinterpret_cast<const GemvDesc*>(static_cast<const char*>(dtables) +
                                                       aligned_size((size_t)n * sizeof(MaskDesc)));
-  // events (optional): [0, 1] bracket the mask launch and [2, 3] the GEMV launch; with one
+  // events (optional): [0, 1] bracket the mask launch and [2, 3] the GEMV launches; with one
   // phase, [0, 1] bracket both.
   const bool four = st->events && n >= 2;
   if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[0], s));
@@ -241,21 +274,10 @@ int launch_from_tables(const spax_step* st, int n_cu, const void* dtables, int64
     SPAX_HIP_CHECK(hipEventRecord(st->events[1], s));
     SPAX_HIP_CHECK(hipEventRecord(st->events[2], s));
   }
-  // as many workgroups as can be resident at once
-  static const int per_cu = [] {
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, batched_gemv_kernel, kGemvThreads, 0) !=
-            hipSuccess || occ < 1)
-      occ = 2;
-    return occ;
-  }();
-  const int64_t cap = (int64_t)n_cu * per_cu;
-  const int64_t grid = items < cap ? items : cap;
-  if (grid > 0) {
-    hipLaunchKernelGGL(batched_gemv_kernel, dim3((unsigned)grid), dim3(kGemvThreads), 0, s, dgd,
-                       n, (int)items);
-    SPAX_HIP_CHECK(hipGetLastError());
-  }
+  int rc = launch_gemvs<SPAX_FMT_FP16>(dgd, bi.n_phases[0], bi.items[0], n_cu, s);
+  if (rc) return rc;
+  rc = launch_gemvs<SPAX_FMT_INT4>(dgd + bi.n_phases[0], bi.n_phases[1], bi.items[1], n_cu, s);
+  if (rc) return rc;
   if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[four ? 3 : 1], s));
   return SPAX_OK;
 }
@@ -284,11 +306,11 @@ size_t batched_workspace_bytes(int n_phases) { return n_phases > 0 ? table_bytes
 int launch_decode_step_batched(const spax_step* st, int n_cu, hipStream_t s) {
   const int n = st->n_phases;
   std::vector<char> table(table_bytes(n));
-  const int64_t items = build_tables(st, table.data());
-  if (items < 0) return SPAX_ERR_SHAPE;
+  BatchItems bi;
+  if (!build_tables(st, table.data(), &bi)) return SPAX_ERR_SHAPE;
   int rc = stage_and_copy(table.data(), table.size(), st->ws, s);
   if (rc) return rc;
-  return launch_from_tables(st, n_cu, st->ws, items, s);
+  return launch_from_tables(st, n_cu, st->ws, bi, s);
 }
 
 int launch_decode_step_batched_static(const spax_step* st, int n_cu, hipStream_t s) {
@@ -313,13 +335,13 @@ int launch_decode_step_batched_static(const spax_step* st, int n_cu, hipStream_t
     SPAX_HIP_CHECK(hipEventSynchronize(g_static.copied[d]));
     g_static.pending[d] = false;
   }
-  const int64_t items = build_tables(st, g_static.host);
-  if (items < 0) return SPAX_ERR_SHAPE;
+  BatchItems bi;
+  if (!build_tables(st, g_static.host, &bi)) return SPAX_ERR_SHAPE;
   void* dtables = g_static.dev_ptr[dev];
   SPAX_HIP_CHECK(hipMemcpyAsync(dtables, g_static.host, bytes, hipMemcpyHostToDevice, s));
   SPAX_HIP_CHECK(hipEventRecord(g_static.copied[dev], s));
   g_static.pending[dev] = true;
-  return launch_from_tables(st, n_cu, dtables, items, s);
+  return launch_from_tables(st, n_cu, dtables, bi, s);
 }
 
 }  // namespace spax

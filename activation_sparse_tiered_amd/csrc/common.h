@@ -48,10 +48,16 @@ int launch_build_tiers(const TierArgs& a, const uint16_t* x, uint8_t* tier, int3
                        hipStream_t s);
 
 // ------------------------------------------------------------------ pack
-int launch_pack(const spax_layout* L, const uint16_t* const* W, void* packed, hipStream_t s);
+int launch_pack(const spax_layout* L, const uint16_t* const* W, const int32_t* perm,
+                void* packed, hipStream_t s);
 
 // ------------------------------------------------------------------ gemv
 constexpr int kTileRows = 512;       // rows per workgroup tile (64 lanes x 8 rows)
+// Rows per tile of the stand-alone and batched GEMVs: an int4 layout's lanes own 32 rows
+// each (one 16-byte code load per column), an fp16 layout's 8.
+inline int gemv_tile_rows(const spax_layout* L) {
+  return L->base_fmt == SPAX_FMT_INT4 ? 2048 : kTileRows;
+}
 #ifndef SPAX_GEMV_THREADS
 #define SPAX_GEMV_THREADS 512
 #endif
@@ -59,7 +65,7 @@ constexpr int kGemvThreads = SPAX_GEMV_THREADS;  // waves that share one tile, s
 constexpr int64_t kMaxRowsTotal = (int64_t)1 << 24;  // largest d_out_total of a layout
 
 struct GemvPlan {
-  int32_t n_tiles;   // ceil(d_out_total / kTileRows)
+  int32_t n_tiles;   // ceil(d_out_total / tile rows)
   int32_t n_chunks;  // split-K factor over the selected column lists
   size_t ws_bytes;   // workspace the launch needs (currently none)
 };
@@ -97,6 +103,9 @@ inline size_t aligned_size(size_t b) { return (b + 255) / 256 * 256; }
 int32_t build_column_ranges(const int32_t* idx, int32_t n, int32_t gap, int32_t* first,
                             int32_t* count);
 size_t pinned_workspace_bytes(const spax_layout* L);
+// spax_placement_order after validation.
+int placement_order(const spax_layout* L, const uint8_t* tiers, int32_t n_tokens,
+                    int32_t* order);
 // spax_storage_ledger after validation.
 int storage_ledger(const spax_layout* L, const int32_t* full_idx, int32_t n_full,
                    const int32_t* approx_idx, int32_t n_approx, int32_t gap, int64_t block,

@@ -7,12 +7,16 @@
 // GPU.  Every selected byte feeds exactly one multiply-add, so the loops are built to keep
 // many 16-byte loads in flight, not to reuse data; MFMA does not apply.
 //
-// Lane mapping: a row tile is 512 rows; lane l of a wavefront owns rows [8l, 8l+8) of it.
+// Lane mapping: lane l of a wavefront owns RPL consecutive rows [RPL l, RPL l + RPL) of a
+// 64 RPL-row tile.  RPL = 8 (fp16 layouts, and the fused decode kernel):
 //   FULL fp16 : one 16-byte load per column (8 halves), fp32 FMA with fp16 operands;
 //   FULL int4 : 4 bytes of codes (8 nibbles) + the (s, z) word of the lane's group;
 //   APPROX 2b : 2 bytes of codes (8 two-bit codes) + the (s, z) word of the lane's group.
-// A group spans >= 64 rows, so the zero-point term is the same for a lane's 8 rows and is
-// summed once per column into zsum (see fma_int4x8 for the form the codes take).
+// RPL = 32 (int4 layouts in the stand-alone and batched GEMVs): one 16-byte load of 32 int4
+// codes, or one 8-byte load of 32 two-bit codes, plus the group's (s, z) word per column, so a
+// wave keeps as many bytes in flight per column as an fp16 wave.
+// A group spans >= 64 rows, so the zero-point term is the same for all of a lane's rows and
+// is summed once per column into zsum (see fma_int4x8 for the form the codes take).
 #pragma once
 
 #include "common.h"
@@ -46,7 +50,7 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-__device__ __forceinline__ void fma_fp16x8(float (&acc)[8], float xv, const uint4& v) {
+__device__ __forceinline__ void fma_fp16x8(float* acc, float xv, const uint4& v) {
   acc[0] = fmaf(xv, half_lo(v.x), acc[0]);
   acc[1] = fmaf(xv, half_hi(v.x), acc[1]);
   acc[2] = fmaf(xv, half_lo(v.y), acc[2]);
@@ -74,7 +78,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t k) {
 }
 
 // 8 int4 codes (row n in bits [4n+3:4n]) times a = 16 x s: acc[r] += a (1 + q_r / 16).
-__device__ __forceinline__ void fma_int4x8(float (&acc)[8], float a, uint32_t c) {
+__device__ __forceinline__ void fma_int4x8(float* acc, float a, uint32_t c) {
   const uint32_t m = 0x03C003C0u;  // mantissa bits 6..9 of both halves
   const uint32_t h0 = and_or(c << 6, m, kOne16x2);  // rows 0, 4
   const uint32_t h1 = and_or(c << 2, m, kOne16x2);  // rows 1, 5
@@ -108,7 +112,7 @@ __device__ __forceinline__ uint32_t spread_sel(uint32_t k0) {
 
 // 8 two-bit codes (row 4k+i in bits [2i+1:2i] of byte k0+k of w, k0 given through sel) times
 // a = 4 x s: acc[r] += a (1 + q_r / 4).
-__device__ __forceinline__ void fma_int2x8(float (&acc)[8], float a, uint32_t w, uint32_t sel) {
+__device__ __forceinline__ void fma_int2x8(float* acc, float a, uint32_t w, uint32_t sel) {
   const uint32_t p = __builtin_amdgcn_perm(0u, w, sel);  // rows 0..3 at bits 8.., 4..7 at 24..
   const uint32_t m = 0x03000300u;  // mantissa bits 8..9 of both halves
   const uint32_t h0 = and_or(p, m, kOne16x2);        // rows 0, 4
@@ -169,6 +173,11 @@ struct Record {
   }
   __device__ __forceinline__ uint32_t word(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ __forceinline__ uint2 stream64(uint32_t off) const {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, SPAX_NT_LOADS ? 2 : 0);
+    return make_uint2(v.x, v.y);
   }
   __device__ __forceinline__ uint4 stream128(uint32_t off) const {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -280,44 +289,50 @@ struct EarlyColumns {
 };
 
 // A lane's byte offsets inside a column record for its rows of the tile.
-template <int FMT>
+template <int FMT, int RPL = 8>
 struct TileOffsets {
-  uint32_t loffA4;  // two-bit codes: the aligned dword that holds the lane's 2 bytes (a 16-bit
-                    // load would be widened right after it is issued, which makes it wait)
-  uint32_t selA;    // byte selector for those 2 bytes
+  static_assert(RPL == 8 || (RPL == 32 && FMT == SPAX_FMT_INT4), "rows per lane: 8, or 32 for int4");
+  uint32_t loffA;   // two-bit codes.  RPL 8: the aligned dword that holds the lane's 2 bytes (a
+                    // 16-bit load would be widened right after it is issued, which makes it
+                    // wait); RPL 32: the lane's 8 bytes
+  uint32_t selA;    // RPL 8: byte selector for those 2 bytes
   uint32_t szoffA;  // (s, z) word of the lane's two-bit group
   uint32_t loffF;   // FULL codes (fp16 rows or int4 codes)
   uint32_t szoffF;  // (s, z) word of the lane's int4 group
   __device__ __forceinline__ TileOffsets(const Shape& sh, int row)
-      : loffA4(((uint32_t)row / 4u) & ~3u),
+      : loffA(RPL == 8 ? (((uint32_t)row / 4u) & ~3u) : (uint32_t)row / 4u),
         selA(spread_sel(((uint32_t)row / 4u) & 2u)),
         szoffA((uint32_t)(sh.T / 4) + (uint32_t)(row / sh.approx_group) * 4u),
         loffF(FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u),
         szoffF((uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u) {}
 };
 
-// The registers of one round: up to kUnroll FULL and kUnroll APPROX columns.
-template <int FMT>
+// The registers of one round: up to kUnroll FULL and kUnroll APPROX columns.  RPL 8: vf holds
+// a fp16 column's 8 halves, cf / ca a dword of int4 / two-bit codes.  RPL 32: vf holds 32 int4
+// codes, va 32 two-bit codes (in .x, .y).
+template <int FMT, int RPL = 8>
 struct RoundLoads {
   float xf[kUnroll], xa[kUnroll];
   uint4 vf[kUnroll];
+  uint2 va[kUnroll];
   uint32_t cf[kUnroll], sf[kUnroll], ca[kUnroll], sa[kUnroll];
 };
 
 // Issues the loads of FULL columns [fi, fi + nf) of srcF and APPROX columns [ai, ai + na) of
 // srcA (counts wave-uniform, at most kUnroll, may be <= 0).  Slots past a count keep zero
 // data and a zero activation.
-template <int FMT, class SrcF, class SrcA>
+template <int FMT, int RPL = 8, class SrcF, class SrcA>
 __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __restrict__ packed,
-                                            const TileOffsets<FMT>& g, const SrcF& srcF, int fi,
-                                            int nf, const SrcA& srcA, int ai, int na,
-                                            RoundLoads<FMT>& r) {
+                                            const TileOffsets<FMT, RPL>& g, const SrcF& srcF,
+                                            int fi, int nf, const SrcA& srcA, int ai, int na,
+                                            RoundLoads<FMT, RPL>& r) {
   const uint8_t* regionA = packed + sh.off_A;
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     r.xf[u] = 0.0f;
     r.xa[u] = 0.0f;
     r.vf[u] = make_uint4(0u, 0u, 0u, 0u);
+    r.va[u] = make_uint2(0u, 0u);
     r.cf[u] = r.sf[u] = r.ca[u] = r.sa[u] = 0u;
   }
 #pragma unroll
@@ -326,12 +341,12 @@ __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __re
       int j;
       srcF.get(fi + u, j, r.xf[u]);
       const Record rec(packed + (int64_t)j * sh.stride_F, sh.stride_F);
-      if (FMT == SPAX_FMT_FP16) {
+      if (FMT == SPAX_FMT_FP16 || RPL == 32) {
         r.vf[u] = rec.stream128(g.loffF);
       } else {
         r.cf[u] = rec.stream32(g.loffF);
-        r.sf[u] = rec.word(g.szoffF);
       }
+      if (FMT == SPAX_FMT_INT4) r.sf[u] = rec.word(g.szoffF);
     }
   }
 #pragma unroll
@@ -340,7 +355,8 @@ __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __re
       int j;
       srcA.get(ai + u, j, r.xa[u]);
       const Record rec(regionA + (int64_t)j * sh.stride_A, sh.stride_A);
-      r.ca[u] = rec.stream32(g.loffA4);
+      if (RPL == 32) r.va[u] = rec.stream64(g.loffA);
+      else r.ca[u] = rec.stream32(g.loffA);
       r.sa[u] = rec.word(g.szoffA);
     }
   }
@@ -351,24 +367,39 @@ __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __re
 // every load makes the branches visible as complete to the compiler's wait tracking, which
 // otherwise assumes loads of a skipped block are still in flight in the next round and waits
 // for each of them there.
-template <int FMT>
-__device__ __forceinline__ void finish_round(const RoundLoads<FMT>& r, const TileOffsets<FMT>& g,
-                                             int nf, int na, float (&acc)[8], float& zsum) {
+template <int FMT, int RPL = 8>
+__device__ __forceinline__ void finish_round(const RoundLoads<FMT, RPL>& r,
+                                             const TileOffsets<FMT, RPL>& g, int nf, int na,
+                                             float (&acc)[RPL], float& zsum) {
   __builtin_amdgcn_s_waitcnt(0);
   if (nf > 0) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (FMT == SPAX_FMT_FP16) {
         fma_fp16x8(acc, r.xf[u], r.vf[u]);
-      } else {
+      } else if (RPL == 8) {
         fma_int4x8(acc, group_terms<4>(r.xf[u], r.sf[u], zsum), r.cf[u]);
+      } else {  // 32 rows: dword k of the 16 bytes holds rows 8k .. 8k + 7
+        const float a = group_terms<4>(r.xf[u], r.sf[u], zsum);
+        fma_int4x8(acc, a, r.vf[u].x);
+        fma_int4x8(acc + 8, a, r.vf[u].y);
+        fma_int4x8(acc + 16, a, r.vf[u].z);
+        fma_int4x8(acc + 24, a, r.vf[u].w);
       }
     }
   }
   if (na > 0) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      fma_int2x8(acc, group_terms<2>(r.xa[u], r.sa[u], zsum), r.ca[u], g.selA);
+      if (RPL == 8) {
+        fma_int2x8(acc, group_terms<2>(r.xa[u], r.sa[u], zsum), r.ca[u], g.selA);
+      } else {  // 32 rows: bytes 2k, 2k + 1 of the 8 bytes hold rows 8k .. 8k + 7
+        const float a = group_terms<2>(r.xa[u], r.sa[u], zsum);
+        fma_int2x8(acc, a, r.va[u].x, spread_sel(0u));
+        fma_int2x8(acc + 8, a, r.va[u].x, spread_sel(2u));
+        fma_int2x8(acc + 16, a, r.va[u].y, spread_sel(0u));
+        fma_int2x8(acc + 24, a, r.va[u].y, spread_sel(2u));
+      }
     }
   }
 }
@@ -382,18 +413,18 @@ __device__ __forceinline__ void finish_round(const RoundLoads<FMT>& r, const Til
 // the previous round are still in flight and makes every load wait for all earlier ones.
 // `row` is the lane's first row (or 0 for lanes past the last row, which read valid memory
 // and are never stored).
-template <int FMT, class SrcF, class SrcA>
+template <int FMT, int RPL = 8, class SrcF, class SrcA>
 __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* __restrict__ packed,
                                                int row, int fb, int fe, const SrcF& srcF, int ab,
-                                               int ae, const SrcA& srcA, float (&acc)[8],
+                                               int ae, const SrcA& srcA, float (&acc)[RPL],
                                                float& zsum) {
-  const TileOffsets<FMT> g(sh, row);
+  const TileOffsets<FMT, RPL> g(sh, row);
   int fi = fb, ai = ab;
   while (fi < fe || ai < ae) {
     const int nf = min(fe - fi, kUnroll), na = min(ae - ai, kUnroll);  // may be <= 0
-    RoundLoads<FMT> r;
-    issue_round<FMT>(sh, packed, g, srcF, fi, nf, srcA, ai, na, r);
-    finish_round<FMT>(r, g, nf, na, acc, zsum);
+    RoundLoads<FMT, RPL> r;
+    issue_round<FMT, RPL>(sh, packed, g, srcF, fi, nf, srcA, ai, na, r);
+    finish_round<FMT, RPL>(r, g, nf, na, acc, zsum);
     fi += max(nf, 0);
     ai += max(na, 0);
   }
@@ -425,33 +456,45 @@ __device__ __forceinline__ void wave_range(int b, int e, int wave, int& wb, int&
 }
 
 // Reduce the NW waves' partial rows through LDS, then write (one chunk) or atomically add
-// (several chunks, y zeroed beforehand in stream order) the tile into y.
-template <int NW>
-__device__ __forceinline__ void finish_tile(float (*red)[kTileRows], const float (&acc)[8],
+// (several chunks, y zeroed beforehand in stream order) the 64 RPL-row tile into y.
+template <int NW, int RPL = 8>
+__device__ __forceinline__ void finish_tile(float (*red)[64 * RPL], const float (&acc)[RPL],
                                             float zsum, int wave, int lane, int row0, int T,
                                             int n_chunks, float* __restrict__ y) {
-  const int tid = threadIdx.x;
-  float4* dst = reinterpret_cast<float4*>(&red[wave][lane * 8]);
-  dst[0] = make_float4(acc[0] + zsum, acc[1] + zsum, acc[2] + zsum, acc[3] + zsum);
-  dst[1] = make_float4(acc[4] + zsum, acc[5] + zsum, acc[6] + zsum, acc[7] + zsum);
-  __syncthreads();
-  const int grow = row0 + tid;
-  if (tid < kTileRows && grow < T) {
-    float sum = 0.0f;
+  constexpr int kRows = 64 * RPL;
+  float4* dst = reinterpret_cast<float4*>(&red[wave][lane * RPL]);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) sum += red[w][tid];
-    // Several chunks meet through hardware fp32 atomics at device scope; y is read only after
-    // the kernel ends, so no device-scope fence is needed.
-    if (n_chunks == 1) y[grow] = sum;
-    else unsafeAtomicAdd(&y[grow], sum);
+  for (int q = 0; q < RPL / 4; ++q)
+    dst[q] = make_float4(acc[4 * q] + zsum, acc[4 * q + 1] + zsum, acc[4 * q + 2] + zsum,
+                         acc[4 * q + 3] + zsum);
+  __syncthreads();
+  for (int r = (int)threadIdx.x; r < kRows; r += NW * 64) {
+    const int grow = row0 + r;
+    if (grow < T) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += red[w][r];
+      // Several chunks meet through hardware fp32 atomics at device scope; y is read only
+      // after the kernel ends, so no device-scope fence is needed.
+      if (n_chunks == 1) y[grow] = sum;
+      else unsafeAtomicAdd(&y[grow], sum);
+    }
   }
 }
+
+// Rows per lane of the stand-alone and batched GEMVs for a base format (tile = 64 RPL rows;
+// the host's gemv_tile_rows gives the same tile).
+template <int FMT>
+struct ItemRows {
+  static constexpr int rpl = FMT == SPAX_FMT_INT4 ? 32 : 8;
+  static constexpr int tile = 64 * rpl;
+};
 
 // One work item of the stand-alone GEMV: row tile `tile`, column chunk `chunk` of the lists
 // in global memory (counts and indices clamped to [0, d_in], so malformed lists cannot
 // address outside the blob).  kCompact: the lists hold slot | channel << 16 entries into a
 // compacted staging copy of the records (`packed` is then the staging buffer).  A workgroup
-// of kWaves waves; ends after the tile's atomics.
+// of kWaves waves; ends after the tile's atomics.  red: kWaves x ItemRows<FMT>::tile floats.
 template <int FMT, bool kCompact = false>
 __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __restrict__ packed,
                                           const uint32_t* __restrict__ x32,
@@ -459,14 +502,16 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
                                           const int32_t* __restrict__ approx_idx,
                                           const int32_t* __restrict__ counts,
                                           float* __restrict__ y, int tile, int chunk,
-                                          float (*red)[kTileRows]) {
+                                          float* red) {
+  constexpr int RPL = ItemRows<FMT>::rpl;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = sh.T;
-  const int row0 = tile * kTileRows;
+  const int row0 = tile * ItemRows<FMT>::tile;
   // Lanes past the last row (ragged last tile) read the record's first rows instead, which
-  // is always in bounds; their sums land in rows >= T and are never stored.
-  const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
+  // is always in bounds; their sums land in rows >= T and are never stored.  Every matrix
+  // height is a multiple of 64, so a lane's rows are all inside or all past T.
+  const int row = row0 + lane * RPL < T ? row0 + lane * RPL : 0;
   const int nF = uniform(min(max(load_global<int32_t>(counts), 0), sh.d_in));
   const int nA = uniform(min(max(load_global<int32_t>(counts + 1), 0), sh.d_in));
   const uint32_t jmax = (uint32_t)sh.d_in - 1u;
@@ -477,9 +522,9 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
   int wfb, wfe, wab, wae;
   wave_range<kWaves>(fb, fe, wave, wfb, wfe);
   wave_range<kWaves>(ab, ae, wave, wab, wae);
-  float acc[8];
+  float acc[RPL];
 #pragma unroll
-  for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
+  for (int h = 0; h < RPL; ++h) acc[h] = 0.0f;
   float zsum = 0.0f;
   const uint16_t* x16 = reinterpret_cast<const uint16_t*>(x32);
   // 64 list entries per tier and block; the channels fit the 16-bit entry field (d_in <= 32768)
@@ -487,9 +532,11 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
     const int fend = min(fi + 64, wfe), aend = min(ai + 64, wae);
     RegBlock bf, ba;
     load_blocks<kCompact>(full_idx, approx_idx, x16, fi, fend, ai, aend, jmax, bf, ba);
-    stream_columns<FMT>(sh, packed, row, fi, max(fi, fend), bf, ai, max(ai, aend), ba, acc, zsum);
+    stream_columns<FMT, RPL>(sh, packed, row, fi, max(fi, fend), bf, ai, max(ai, aend), ba, acc,
+                             zsum);
   }
-  finish_tile<kWaves>(red, acc, zsum, wave, lane, row0, T, sh.n_chunks, y);
+  finish_tile<kWaves, RPL>(reinterpret_cast<float(*)[64 * RPL]>(red), acc, zsum, wave, lane,
+                           row0, T, sh.n_chunks, y);
 }
 
 }  // namespace gemv

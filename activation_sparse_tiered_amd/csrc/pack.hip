@@ -8,6 +8,9 @@
 // fp32 with round-to-nearest-even and a correctly rounded division, so that the codes are
 // a deterministic function of the weights.
 //
+// Placement (optional): record j may hold column perm[j], so that columns used together by
+// the same tokens sit next to each other (eigenradar commentary, third paragraph).
+//
 // Thread mapping: one lane per (column j, 8 consecutive fused rows).  A quantization group
 // of G rows is G/8 consecutive lanes; since every matrix height is a multiple of G, the
 // lanes of one group are aligned inside the wavefront and reduce min/max with xor
@@ -19,6 +22,7 @@ namespace {
 
 struct PackArgs {
   const uint16_t* W[SPAX_MAX_MATS];
+  const int32_t* perm;  // record j packs column perm[j] (NULL: column j)
   uint8_t* packed;
   int32_t row_off[SPAX_MAX_MATS + 1];  // fused row where matrix m starts
   int32_t n_mats;
@@ -80,8 +84,10 @@ __global__ __launch_bounds__(256) void pack_columns_kernel(PackArgs a) {
   const int64_t rows_m = a.row_off[m + 1] - a.row_off[m];
   const int64_t lr = r0 - a.row_off[m];
 
+  // the source column of record j; clamped so that a malformed permutation stays in bounds
+  const int64_t src = a.perm ? (int64_t)min(max(a.perm[j], 0), a.d_in - 1) : j;
   uint4 raw = make_uint4(0, 0, 0, 0);
-  if (active) raw = *reinterpret_cast<const uint4*>(a.W[m] + j * rows_m + lr);
+  if (active) raw = *reinterpret_cast<const uint4*>(a.W[m] + src * rows_m + lr);
   const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
   float w[8];
 #pragma unroll
@@ -144,8 +150,10 @@ __global__ __launch_bounds__(256) void pack_columns_kernel(PackArgs a) {
 
 }  // namespace
 
-int launch_pack(const spax_layout* L, const uint16_t* const* W, void* packed, hipStream_t s) {
+int launch_pack(const spax_layout* L, const uint16_t* const* W, const int32_t* perm,
+                void* packed, hipStream_t s) {
   PackArgs a{};
+  a.perm = perm;
   a.packed = static_cast<uint8_t*>(packed);
   a.n_mats = L->n_mats;
   a.d_in = L->d_in;

@@ -9,8 +9,11 @@
 // GPU memory", third paragraph (jointly accessed columns placed together, adjacent read ranges
 // merged, coarse granularity moving more than was selected) and last paragraph (count the bytes
 // selected and the bytes moved apart).
+#include <algorithm>
 #include <cstring>
 #include <mutex>
+#include <thread>
+#include <vector>
 
 #include "common.h"
 
@@ -51,9 +54,47 @@ struct Scratch {
   std::mutex mu;
   char* host = nullptr;
   size_t bytes = 0;
+  char* stage = nullptr;     // SPAX_PINNED_HOSTGATHER: the gathered records
+  size_t stage_bytes = 0;
   hipEvent_t done = nullptr;
   bool pending = false;
 };
+
+// One host-side copy of a range's records into the staging buffer.
+struct CopyJob {
+  const uint8_t* src;
+  int64_t dst_off;  // byte offset in the staging buffer; jobs follow each other without gaps
+  int64_t bytes;
+};
+
+// Copies the jobs' bytes into `dst` with up to `threads` host threads, each taking one
+// contiguous share of the destination (the jobs tile [0, total) in order).
+void gather_on_host(const std::vector<CopyJob>& jobs, int64_t total, uint8_t* dst, int threads) {
+  auto work = [&](int64_t b, int64_t e) {
+    // first job that ends after b
+    size_t k = std::upper_bound(jobs.begin(), jobs.end(), b,
+                                [](int64_t v, const CopyJob& j) { return v < j.dst_off + j.bytes; }) -
+               jobs.begin();
+    for (; k < jobs.size() && jobs[k].dst_off < e; ++k) {
+      const int64_t lo = std::max(b, jobs[k].dst_off);
+      const int64_t hi = std::min(e, jobs[k].dst_off + jobs[k].bytes);
+      std::memcpy(dst + lo, jobs[k].src + (lo - jobs[k].dst_off), (size_t)(hi - lo));
+    }
+  };
+  if (threads <= 1 || total < ((int64_t)4 << 20)) {
+    work(0, total);
+    return;
+  }
+  std::vector<std::thread> pool;
+  for (int t = 0; t < threads; ++t)
+    pool.emplace_back(work, total * t / threads, total * (t + 1) / threads);
+  for (auto& th : pool) th.join();
+}
+
+int host_gather_threads() {
+  const unsigned n = std::thread::hardware_concurrency();
+  return n == 0 ? 1 : (int)std::min(16u, n);
+}
 Scratch g_scratch[64];
 
 }  // namespace
@@ -124,7 +165,11 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
   if (transfer == SPAX_PINNED_GATHER)
     return tiered_gemv_pinned_device_merge(L, host_dev, x, full_idx, approx_idx, counts, y, gap,
                                            ws, stats, s);
-  // SPAX_PINNED_MEMCPY: the ranges are merged on the host, one hipMemcpyAsync each
+  // SPAX_PINNED_MEMCPY: the ranges are merged on the host, one hipMemcpyAsync each.
+  // SPAX_PINNED_HOSTGATHER: the ranges are merged on the host, host threads copy their records
+  // into one pinned staging buffer (FULL records, then APPROX records) and one hipMemcpyAsync
+  // moves it; region A of the staged records then starts right after the FULL records.
+  const bool host_gather = transfer == SPAX_PINNED_HOSTGATHER;
   const int d = L->d_in;
   int dev = 0;
   SPAX_HIP_CHECK(hipGetDevice(&dev));
@@ -166,26 +211,50 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
   int64_t moved = 0;
   int n_ranges = 0;
   int rc = SPAX_OK;
-  const auto region = [&](const int32_t* idx, int n, uint32_t* out, int64_t off, int64_t stride) {
+  std::vector<CopyJob> jobs;
+  // stage_off: where the region's first slot lands in the staging area
+  const auto region = [&](const int32_t* idx, int n, uint32_t* out, int64_t off, int64_t stride,
+                          int64_t stage_off) {
     int32_t slot = 0;
     const int r = for_ranges(idx, n, gap, [&](int32_t f, int32_t c, int32_t e0, int32_t ne) {
       if (rc) return;
       for (int32_t k = 0; k < ne; ++k)
         out[e0 + k] = (uint32_t)(slot + (idx[e0 + k] - f)) | ((uint32_t)idx[e0 + k] << 16);
-      const hipError_t e = hipMemcpyAsync(staging + off + (int64_t)slot * stride,
-                                          host + off + (int64_t)f * stride, (size_t)c * stride,
-                                          hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) rc = hip_fail(e, "hipMemcpyAsync of a record range");
+      const uint8_t* src = host + off + (int64_t)f * stride;
+      if (host_gather) {
+        jobs.push_back(CopyJob{src, stage_off + (int64_t)slot * stride, (int64_t)c * stride});
+      } else {
+        const hipError_t e = hipMemcpyAsync(staging + stage_off + (int64_t)slot * stride, src,
+                                            (size_t)c * stride, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) rc = hip_fail(e, "hipMemcpyAsync of a record range");
+      }
       moved += (int64_t)c * stride;
       slot += c;
     });
     if (r < 0 && !rc) rc = fail(SPAX_ERR_PARAM, "column list read back is not ascending");
     if (r > 0) n_ranges += r;
   };
-  region(h_full, nF, h_outF, 0, L->stride_F);
+  region(h_full, nF, h_outF, 0, L->stride_F, 0);
   if (rc) return rc;
-  region(h_apx, nA, h_outA, L->off_A, L->stride_A);
+  const int64_t movedF = moved;  // host gather: the APPROX records follow the FULL ones
+  region(h_apx, nA, h_outA, L->off_A, L->stride_A, host_gather ? movedF : L->off_A);
   if (rc) return rc;
+  spax_layout staged = *L;
+  if (host_gather) {
+    if (sc.stage_bytes < (size_t)moved) {
+      if (sc.stage) SPAX_HIP_CHECK(hipHostFree(sc.stage));
+      sc.stage = nullptr;
+      sc.stage_bytes = 0;
+      void* h = nullptr;
+      SPAX_HIP_CHECK(hipHostMalloc(&h, (size_t)moved, hipHostMallocDefault));
+      sc.stage = static_cast<char*>(h);
+      sc.stage_bytes = (size_t)moved;
+    }
+    gather_on_host(jobs, moved, reinterpret_cast<uint8_t*>(sc.stage), host_gather_threads());
+    if (moved > 0)
+      SPAX_HIP_CHECK(hipMemcpyAsync(staging, sc.stage, (size_t)moved, hipMemcpyHostToDevice, s));
+    staged.off_A = movedF;  // the GEMV reads region A of the staged records here
+  }
   // The two host lists and their device copies have the same layout (d entries each), so one
   // upload of the span that holds the used entries replaces two (an upload costs more to
   // enqueue than to move).
@@ -196,7 +265,8 @@ int tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const void
   sc.pending = true;
 
   // ---- the GEMV over the staged records (counts are still the device's)
-  rc = launch_tiered_gemv(L, gemv_plan(L), staging, x, reinterpret_cast<const int32_t*>(t.listF),
+  rc = launch_tiered_gemv(&staged, gemv_plan(L), staging, x,
+                          reinterpret_cast<const int32_t*>(t.listF),
                           reinterpret_cast<const int32_t*>(t.listA), counts, y, false, s, true);
   if (rc) return rc;
   if (stats) {
@@ -235,6 +305,25 @@ int storage_ledger(const spax_layout* L, const int32_t* full_idx, int32_t n_full
   }
   st.read_bytes = st.n_blocks * block;
   *out = st;
+  return SPAX_OK;
+}
+
+// Channels by descending bytes selected over the calibration masks (stride_F per FULL,
+// stride_A per APPROX), equal scores by channel index.
+int placement_order(const spax_layout* L, const uint8_t* tiers, int32_t n_tokens,
+                    int32_t* order) {
+  const int d = L->d_in;
+  std::vector<int64_t> score(d, 0);
+  for (int32_t t = 0; t < n_tokens; ++t) {
+    const uint8_t* row = tiers + (size_t)t * d;
+    for (int j = 0; j < d; ++j) {
+      if (row[j] > SPAX_TIER_FULL)
+        return fail(SPAX_ERR_PARAM, "tiers[%d][%d] = %d is not a tier", t, j, (int)row[j]);
+      score[j] += row[j] == SPAX_TIER_FULL ? L->stride_F : row[j] == SPAX_TIER_APPROX ? L->stride_A : 0;
+    }
+  }
+  for (int j = 0; j < d; ++j) order[j] = j;
+  std::stable_sort(order, order + d, [&](int32_t a, int32_t b) { return score[a] > score[b]; });
   return SPAX_OK;
 }
 

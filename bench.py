@@ -99,8 +99,11 @@ def parse():
                     help="decode workloads: replace the tier rule by all-FULL (reads the dense "
                          "bytes) or all-SKIP (reads almost nothing), as byte-counter controls")
     ap.add_argument("--gap", type=int, default=0, help="host8b: range merging gap (columns)")
-    ap.add_argument("--transfer", default="gather", choices=["memcpy", "gather"],
-                    help="host8b: one hipMemcpyAsync per range, or one copy kernel")
+    ap.add_argument("--transfer", default="gather", choices=["memcpy", "gather", "hostgather"],
+                    help="host8b: one hipMemcpyAsync per range, one copy kernel reading the "
+                         "mapped blob, or host threads gathering the ranges for one copy")
+    ap.add_argument("--sweep", action="store_true",
+                    help="host8b: also time every transfer at range gaps 0, 4 and 8")
     ap.add_argument("--placement", default="channel", choices=["channel", "frequency"],
                     help="host8b: records in channel order, or ordered by calibrated "
                          "selection frequency (jointly selected columns placed together)")
@@ -261,15 +264,33 @@ def _strip_c_comments(text: str) -> str:
     return " ".join(code.split())
 
 
+def _compiler_id():
+    """The hipcc version banner (the compiler that builds the kernels), or '' if absent."""
+    import subprocess
+    try:
+        r = subprocess.run(["hipcc", "--version"], capture_output=True, text=True, timeout=60)
+        return " ".join(r.stdout.split())
+    except (OSError, subprocess.SubprocessError):
+        return ""
+
+
 def sources_sha256():
     """sha256 over the fused kernel's sources without their comments (name, then text; in
-    the order of KERNEL_SOURCES)."""
+    the order of KERNEL_SOURCES), the build flags and the compiler's version banner: the
+    recorded byte counters stay valid only for the same code built the same way."""
     import hashlib
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_spax_build_flags", os.path.join(ROOT, "activation_sparse_tiered_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         h.update(os.path.basename(f).encode())
         with open(f, encoding="utf-8") as fh:
             h.update(_strip_c_comments(fh.read()).encode())
+    h.update(" ".join(x for x in b.FLAGS if not x.startswith("-I")).encode())
+    h.update(_compiler_id().encode())
     return h.hexdigest()
 
 
@@ -522,6 +543,19 @@ def device_bench(args, spax, torch, dev):
     log(f"[bench] fused kernel: {avg_launch_ms * 1e3:.2f} us/launch, {avg_bytes / 1e6:.2f} MB/launch, "
         f"{achieved:.1f} GB/s; selected bytes/step {bytes_per_step / 1e9:.3f} GB")
 
+    # ---- the masks of one timed token read from block storage (4 KiB blocks): selected bytes
+    # against bytes physically read
+    stack.step(args.warmup)
+    torch.cuda.synchronize()
+    lists = []
+    for b in stack.bufs:
+        cnt = b["c"].cpu().numpy()
+        lists.append((b["f"].cpu().numpy()[:cnt[0]], b["a"].cpu().numpy()[:cnt[1]]))
+    storage = storage_account(spax, stack.layouts, lists, 4096, 0)
+    for k in ("selected_GB", "moved_GB", "read_GB"):
+        storage[k] = round(storage[k] / per_tok, 4)
+    log(f"[bench] storage ledger {storage}")
+
     # ---- per-token spread: the same steps again, each between its own pair of events
     # (outside the timed region above)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -605,6 +639,11 @@ def device_bench(args, spax, torch, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(args),
+                     "traffic_source": (f"recorded: {os.path.relpath(TRAFFIC_FILE, ROOT)} "
+                                        f"(rocprofv3 FETCH_SIZE/WRITE_SIZE runs of the same "
+                                        f"sources, flags and compiler, sha256 "
+                                        f"{sources_sha256()[:16]})"
+                                        if recorded_traffic(args) is not None else None),
                      "traffic_unit": "MB per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "fused_phase_kernel<%s>" % ("fp16" if spec["fmt"] == 0 else "int4"),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 3),
@@ -618,69 +657,106 @@ def device_bench(args, spax, torch, dev):
         "token_us": token_us,
         "read_probe": probe,
         "dense_baseline": dense,
+        "storage_4KiB": storage,
     }
 
 
 def calibrated_order(spax, torch, dev, L, params, d_in, layer, group, tokens=16):
-    """Channel order for the packed records: descending selected bytes per channel over
-    `tokens` calibration activations (FULL counts stride_F bytes, APPROX stride_A), ties by
-    channel index.  Returns a device index tensor: position p holds channel order[p]."""
-    score = np.zeros(d_in, dtype=np.int64)
+    """Record order from calibration masks (spax_placement_order over the masks of `tokens`
+    calibration activations, distinct from the timed ones): channels by descending selected
+    bytes.  Returns the order as a device int32 tensor (position p holds channel order[p])."""
     tier = torch.empty(d_in, dtype=torch.uint8, device=dev)
     f = torch.empty(d_in, dtype=torch.int32, device=dev)
     a = torch.empty(d_in, dtype=torch.int32, device=dev)
     c = torch.zeros(3, dtype=torch.int32, device=dev)
+    masks = []
     for t in range(tokens):
         xc = torch.from_numpy(synth.activations(SEED, d_in, 1000 + t, 100 + layer, group,
                                                 channel_scaled=True)).to(dev)
         spax.spax_build_tiers(xc, d_in, params, tier, f, a, c)
-        tv = tier.cpu().numpy()
-        score += np.where(tv == 2, int(L.stride_F), np.where(tv == 1, int(L.stride_A), 0))
-    order = np.lexsort((np.arange(d_in), -score))
+        masks.append(tier.cpu().numpy().copy())
+    order = spax.spax_placement_order(L, np.stack(masks))
     return torch.from_numpy(order).to(dev)
+
+
+def storage_account(spax, layouts, lists, block=4096, gap=0):
+    """Bytes selected against bytes read from block storage (spax_storage_ledger, blocks of
+    `block` bytes, each merged range one read request) summed over the phases of one token.
+    ``lists``: per phase, (full_idx, approx_idx) host arrays."""
+    sel = moved = read = ranges = 0
+    for L, (f, a) in zip(layouts, lists):
+        st = spax.spax_storage_ledger(L, f, a, gap, block)
+        sel += st.selected_bytes
+        moved += st.moved_bytes
+        read += st.read_bytes
+        ranges += st.n_ranges
+    return {"block_bytes": block, "gap": gap, "selected_GB": round(sel / 1e9, 4),
+            "moved_GB": round(moved / 1e9, 4), "read_GB": round(read / 1e9, 4),
+            "read_over_selected": round(read / sel, 4) if sel else None,
+            "read_requests": int(ranges),
+            "what": "the token's masks read from block storage: each merged record range one "
+                    "request rounded out to whole blocks of the blob (spax_storage_ledger)"}
+
+
+HOST_TRANSFERS = {"memcpy": 0, "gather": 1, "hostgather": 2}
 
 
 def host_bench(args, spax, torch, dev):
     """Llama-3-8B shapes, blobs in pinned host memory: per phase a device mask, then
     spax_tiered_gemv_pinned (ranges over PCIe).  Compared with the measured single-copy pinned
-    host-to-device bandwidth."""
+    host-to-device bandwidth.  Every layer distinct (32 by default); if pinned memory runs
+    out, the layers that fit are timed and the result scaled to 32 (stated in the output)."""
     shapes = synth.decoder_phases_8b()
-    n_layers = args.layers if args.layers is not None else 4
+    want_layers = args.layers if args.layers is not None else 32
     t0 = time.time()
     phases = []
-    for l in range(n_layers):
-        for k, (name, d_in, d_out) in enumerate(shapes):
-            L = spax.spax_layout_init(d_in, d_out, 0, 128, 128)
-            dblob = torch.empty(int(L.total_bytes), dtype=torch.uint8, device=dev)
-            Ws = [synth.weights_device(SEED, d_in, r, dev, 100 + l, k, m) for m, r in enumerate(d_out)]
-            nf, na = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
-            params = spax.topk_params(nf, na)
-            x = torch.from_numpy(synth.activations(SEED, d_in, 0, 100 + l, k,
-                                                   channel_scaled=True)).to(dev)
-            if args.placement == "frequency":
-                # Offline placement: records in descending order of how many bytes each
-                # channel made selected over calibration tokens (distinct from the timed
-                # ones).  Permuting the weight columns and the activations alike leaves y
-                # unchanged; a model does it once by permuting the rows of the layer that
-                # produces x.
-                perm = calibrated_order(spax, torch, dev, L, params, d_in, l, k)
-                Ws = [w[perm] for w in Ws]
-                x = x[perm].contiguous()
-            spax.spax_pack_columns(L, Ws, dblob)
-            del Ws
-            host = torch.empty(int(L.total_bytes), dtype=torch.uint8, pin_memory=True)
-            host.copy_(dblob)
-            del dblob
-            phases.append(dict(L=L, host=host, x=x, p=params, d=d_in,
-                               f=torch.empty(d_in, dtype=torch.int32, device=dev),
-                               a=torch.empty(d_in, dtype=torch.int32, device=dev),
-                               c=torch.zeros(3, dtype=torch.int32, device=dev),
-                               y=torch.empty(int(L.d_out_total), dtype=torch.float32, device=dev)))
+    alloc_note = None
+    for l in range(want_layers):
+        built = []
+        try:
+            for k, (name, d_in, d_out) in enumerate(shapes):
+                L = spax.spax_layout_init(d_in, d_out, 0, 128, 128)
+                nf, na = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
+                params = spax.topk_params(nf, na)
+                host = torch.empty(int(L.total_bytes), dtype=torch.uint8, pin_memory=True)
+                dblob = torch.empty(int(L.total_bytes), dtype=torch.uint8, device=dev)
+                Ws = [synth.weights_device(SEED, d_in, r, dev, 100 + l, k, m)
+                      for m, r in enumerate(d_out)]
+                x = torch.from_numpy(synth.activations(SEED, d_in, 0, 100 + l, k,
+                                                       channel_scaled=True)).to(dev)
+                if args.placement == "frequency":
+                    # Offline placement from calibration masks; the activations are permuted
+                    # alike (a model does it once through the rows of the layer producing x).
+                    perm = calibrated_order(spax, torch, dev, L, params, d_in, l, k)
+                    spax.spax_pack_columns_placed(L, Ws, perm, dblob)
+                    x = x[perm.long()].contiguous()
+                else:
+                    spax.spax_pack_columns(L, Ws, dblob)
+                del Ws
+                host.copy_(dblob)
+                del dblob
+                built.append(dict(L=L, host=host, x=x, p=params, d=d_in,
+                                  f=torch.empty(d_in, dtype=torch.int32, device=dev),
+                                  a=torch.empty(d_in, dtype=torch.int32, device=dev),
+                                  c=torch.zeros(3, dtype=torch.int32, device=dev),
+                                  y=torch.empty(int(L.d_out_total), dtype=torch.float32,
+                                                device=dev)))
+        except RuntimeError as e:  # pinned (or device) memory exhausted
+            alloc_note = (f"allocation failed at layer {l} of {want_layers} "
+                          f"({str(e).splitlines()[0][:120]}); {l} layers timed")
+            log(f"[bench] host8b: {alloc_note}")
+            del built
+            torch.cuda.empty_cache()
+            break
+        phases.extend(built)
+    n_layers = len(phases) // len(shapes)
+    if n_layers == 0:
+        raise RuntimeError(f"host8b: no layer fits in pinned memory ({alloc_note})")
     torch.cuda.synchronize()
     ws = torch.empty(max(spax.spax_pinned_workspace_bytes(ph["L"]) for ph in phases),
                      dtype=torch.uint8, device=dev)
-    log(f"[bench] host8b: {n_layers} distinct layers in pinned memory "
-        f"({sum(int(ph['L'].total_bytes) for ph in phases) / 1e9:.2f} GB), "
+    pinned_gb = sum(int(ph["L"].total_bytes) for ph in phases) / 1e9
+    log(f"[bench] host8b: {n_layers} distinct layers in pinned memory ({pinned_gb:.2f} GB), "
         f"built in {time.time() - t0:.1f} s")
 
     # measured single-copy pinned host-to-device bandwidth (1 GiB)
@@ -697,16 +773,14 @@ def host_bench(args, spax, torch, dev):
     h2d = 3 * (1 << 30) / (h0.elapsed_time(h1) * 1e-3) / 1e9
     del src, dst
 
-    transfer = spax.PINNED_GATHER if args.transfer == "gather" else spax.PINNED_MEMCPY
-
-    def token(account):
+    def token(transfer, gap, account):
         # account=False: no byte account is asked for, so a call with the gather transfer
-        # does not wait for the device (the memcpy transfer always reads the lists back)
+        # does not wait for the device (the host-merged transfers always read the lists back)
         moved = sel = ranges = 0
         for ph in phases:
             spax.spax_build_tiers(ph["x"], ph["d"], ph["p"], None, ph["f"], ph["a"], ph["c"])
             st = spax.spax_tiered_gemv_pinned(ph["L"], ph["host"], ph["x"], ph["f"], ph["a"],
-                                              ph["c"], ph["y"], args.gap, ws, transfer=transfer,
+                                              ph["c"], ph["y"], gap, ws, transfer=transfer,
                                               stats=account)
             if account:
                 moved += st.moved_bytes + st.list_bytes
@@ -715,36 +789,71 @@ def host_bench(args, spax, torch, dev):
         torch.cuda.synchronize()
         return moved, sel, ranges
 
-    steps = max(1, args.steps // 8)
-    moved, sel, ranges = token(True)  # warm-up, and the byte account of the timed pass
-    t1 = time.perf_counter()
-    for _ in range(steps):
-        token(False)
-    dt = (time.perf_counter() - t1) / steps
-    r = dict(s=dt, moved=moved, sel=sel, ranges=ranges)
-    log(f"[bench] host8b: {dt * 1e3:.2f} ms for {n_layers} layers, "
-        f"{moved / dt / 1e9:.2f} GB/s moved, H2D copy {h2d:.2f} GB/s")
+    def timed(transfer, gap, steps):
+        moved, sel, ranges = token(transfer, gap, True)  # warm-up and the byte account
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            token(transfer, gap, False)
+        return (time.perf_counter() - t1) / steps, moved, sel, ranges
+
     scale = 32 / n_layers
-    gbs = r["moved"] / r["s"] / 1e9
+    steps = max(1, args.steps // 8)
+    dt, moved, sel, ranges = timed(HOST_TRANSFERS[args.transfer], args.gap, steps)
+    gbs = moved / dt / 1e9
+    log(f"[bench] host8b: {dt * 1e3:.2f} ms for {n_layers} layers, {gbs:.2f} GB/s moved, "
+        f"H2D copy {h2d:.2f} GB/s")
+
+    sweep = None
+    if args.sweep:
+        sweep = []
+        for name, tr in HOST_TRANSFERS.items():
+            for gap in (0, 4, 8):
+                d2, m2, s2, r2 = timed(tr, gap, 1)
+                sweep.append({"transfer": name, "gap": gap,
+                              "ms_per_token": round(d2 * scale * 1e3, 2),
+                              "moved_GB_per_token": round(m2 * scale / 1e9, 4),
+                              "ranges_per_token": int(r2 * scale),
+                              "moved_GBps": round(m2 / d2 / 1e9, 2),
+                              "frac_of_h2d": round(m2 / d2 / 1e9 / h2d, 4)})
+                log(f"[bench] sweep {sweep[-1]}")
+
+    # storage ledger of one token's masks (the same masks as the timed pass)
+    token(HOST_TRANSFERS[args.transfer], args.gap, False)
+    lists = []
+    for ph in phases:
+        cnt = ph["c"].cpu().numpy()
+        lists.append((ph["f"].cpu().numpy()[:cnt[0]], ph["a"].cpu().numpy()[:cnt[1]]))
+    storage = storage_account(spax, [ph["L"] for ph in phases], lists, 4096, args.gap)
+    for k in ("selected_GB", "moved_GB", "read_GB"):
+        storage[k] = round(storage[k] * scale, 4)
+    storage["read_requests"] = int(storage["read_requests"] * scale)
+    log(f"[bench] storage ledger {storage}")
+
+    layers_note = (f"{n_layers} distinct layers timed (wall clock)" +
+                   (f", scaled x{scale:g} to 32" if n_layers != 32 else "") +
+                   (f"; {alloc_note}" if alloc_note else ""))
     return {
         "metric": "pinned-host tiered GEMV µs/token (Llama-3-8B shapes); moved GB/s vs measured "
                   "pinned host-to-device bandwidth",
-        "value": round(r["s"] * scale * 1e6, 1), "unit": "us/token", "n_gpus": 1,
-        "steps": steps, "warmup": 1, "ms_per_step": round(r["s"] * scale * 1e3, 3),
+        "value": round(dt * scale * 1e6, 1), "unit": "us/token", "n_gpus": 1,
+        "steps": steps, "warmup": 1, "ms_per_step": round(dt * scale * 1e3, 3),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"host8b: Llama-3-8B shapes (q|k|v 4096->4096+1024+1024, o, "
                                f"gate|up 4096->2x14336, down 14336->4096), fp16 blobs in pinned "
-                               f"host memory, TopK 20/30/50, range gap {args.gap}, transfer {args.transfer}, "
-                               f"placement {args.placement}; {n_layers} "
-                               f"distinct layers timed (wall clock), scaled x{scale:g} to 32",
-                   "selected_GB_per_token": round(r["sel"] * scale / 1e9, 4),
-                   "moved_GB_per_token": round(r["moved"] * scale / 1e9, 4),
-                   "ranges_per_token": int(r["ranges"] * scale)},
+                               f"host memory ({pinned_gb:.1f} GB), TopK 20/30/50, range gap "
+                               f"{args.gap}, transfer {args.transfer}, placement "
+                               f"{args.placement}; {layers_note}",
+                   "layers_timed": n_layers,
+                   "selected_GB_per_token": round(sel * scale / 1e9, 4),
+                   "moved_GB_per_token": round(moved * scale / 1e9, 4),
+                   "ranges_per_token": int(ranges * scale)},
         "roofline": {"bound": "pcie", "achieved": round(gbs, 2), "peak": round(h2d, 2),
                      "unit": "GB/s", "frac": round(gbs / h2d, 4), "traffic": None,
                      "peak_note": "measured single 1 GiB pinned host-to-device copy"},
         "cpu_baseline": None,
+        "transfer_sweep": sweep,
+        "storage_4KiB": storage,
     }
 
 

@@ -118,6 +118,33 @@ int spax_layout_init(spax_layout* L);
 int spax_pack_columns(const spax_layout* L, const uint16_t* const* W, void* packed,
                       hipStream_t stream);
 
+/*
+ * Offline placement of the column records (eigenradar commentary on SpAx, "The route outside
+ * GPU memory", third paragraph: jointly accessed columns are placed together, so a token's
+ * selection reads fewer, longer ranges).  Host only.
+ *   tiers : host, n_tokens rows of d_in tier bytes (SPAX_TIER_*), the masks of calibration
+ *           tokens (e.g. spax_build_tiers' tier output copied back).
+ *   order : host, d_in entries: a permutation of [0, d_in) with channels in descending order of
+ *           the bytes they made selected (stride_F per FULL, stride_A per APPROX), equal
+ *           scores in channel order.  Position p of a placed blob holds channel order[p].
+ * Errors: SPAX_ERR_NULL, SPAX_ERR_SHAPE (layout not initialised), SPAX_ERR_PARAM (n_tokens < 0,
+ * a byte that is not a tier).
+ */
+int spax_placement_order(const spax_layout* L, const uint8_t* tiers, int32_t n_tokens,
+                         int32_t* order);
+
+/*
+ * spax_pack_columns with a placement: record p of each region holds column perm[p] (perm:
+ * device, d_in int32, a permutation such as spax_placement_order's order; entries are clamped
+ * to [0, d_in) so a malformed one repeats a column but stays in bounds).  The activation vector
+ * of a placed blob is permuted alike, x_placed[p] = x[perm[p]] (in a model, once, through the
+ * rows of the layer that produces x); masks, lists and the product then work on positions, and
+ * y is the product over the same columns.  Errors: as spax_pack_columns, plus SPAX_ERR_NULL
+ * (perm) and SPAX_ERR_ALIGN (perm not 4-byte aligned).
+ */
+int spax_pack_columns_placed(const spax_layout* L, const uint16_t* const* W,
+                             const int32_t* perm, void* packed, hipStream_t stream);
+
 /* ---------------------------------------------------------------- tier masks */
 enum { SPAX_TIER_SKIP = 0, SPAX_TIER_APPROX = 1, SPAX_TIER_FULL = 2 };
 enum { SPAX_MODE_TOPK = 0, SPAX_MODE_THRESHOLD = 1, SPAX_MODE_TOPK_GUIDED = 2 };
@@ -245,9 +272,10 @@ typedef struct spax_move_stats {
   int64_t selected_bytes;  /* n_full * stride_F + n_approx * stride_A                   */
   int64_t moved_bytes;     /* record bytes copied host -> device (selected + merged gaps) */
   int64_t list_bytes;      /* list bytes copied host -> device: 0 for SPAX_PINNED_GATHER
-                              (the lists never leave the device); for SPAX_PINNED_MEMCPY one
-                              upload of the span of the two compacted host lists (d_in
-                              entries each) that holds every used entry                 */
+                              (the lists never leave the device); for SPAX_PINNED_MEMCPY and
+                              SPAX_PINNED_HOSTGATHER one upload of the span of the two
+                              compacted host lists (d_in entries each) that holds every used
+                              entry                                                       */
   int32_t n_ranges;        /* merged ranges (FULL + APPROX)                               */
   int32_t n_full, n_approx;
   int32_t reserved0;
@@ -261,7 +289,12 @@ enum {
   /* the ranges are merged on the device (one kernel, two workgroups) and one copy kernel
    * reads them from the mapped pinned blob (zero-copy) into the compacted staging area:
    * nothing waits for the host, so the call is asynchronous unless `stats` is requested */
-  SPAX_PINNED_GATHER = 1
+  SPAX_PINNED_GATHER = 1,
+  /* the lists come back to the host (the call synchronizes `stream`), which merges the
+   * ranges; host threads copy the records of every range from the pinned blob into one
+   * library-owned pinned staging buffer (FULL records, then APPROX records, back to back) and
+   * one hipMemcpyAsync moves them (CPU gather, single DMA) */
+  SPAX_PINNED_HOSTGATHER = 2
 };
 
 /* Device workspace for spax_tiered_gemv_pinned: a compacted staging copy of the blob's
@@ -276,23 +309,26 @@ size_t spax_pinned_workspace_bytes(const spax_layout* L);
  *   x, full_idx, approx_idx, counts, y : device, as for spax_tiered_gemv (the lists as
  *                 written by spax_build_tiers: ascending).
  *   gap   : range merging, as for spax_column_ranges.
- *   transfer : SPAX_PINNED_MEMCPY or SPAX_PINNED_GATHER (same bytes moved, same result).
+ *   transfer : SPAX_PINNED_MEMCPY, SPAX_PINNED_GATHER or SPAX_PINNED_HOSTGATHER (same bytes
+ *              moved, same result).
  *   ws    : device, >= spax_pinned_workspace_bytes(L) bytes, 256-byte aligned.
  *   stats : host, may be NULL (the byte account; requesting it synchronizes `stream`).
  * Merges the selected columns of each region into ranges (on the device for
  * SPAX_PINNED_GATHER; on the host, after reading counts and lists back, for
- * SPAX_PINNED_MEMCPY), moves the ranges host -> device (see `transfer`) into a compacted
+ * SPAX_PINNED_MEMCPY and SPAX_PINNED_HOSTGATHER), moves the ranges host -> device (see `transfer`) into a compacted
  * staging area of ws (a range's columns land in consecutive slots, ranges in order) with the
  * compacted lists (staging slot | channel << 16), then runs the tiered GEMV over the staged
  * records.  y equals spax_tiered_gemv's on a device copy of the blob up to the order of fp32
  * additions.  Returns with the work enqueued on `stream`; with `stats` it also waits for the
- * byte account.  SPAX_PINNED_MEMCPY: library-owned pinned buffers hold the lists; a later
- * call waits until the previous call's list copy has completed before reusing them.
+ * byte account.  SPAX_PINNED_MEMCPY and SPAX_PINNED_HOSTGATHER: library-owned pinned buffers
+ * (allocated on first use and grown as needed) hold the lists and, for the host gather, the
+ * staged records; a later call waits until the previous call's copies from them have completed
+ * before reusing them.
  * SPAX_PINNED_GATHER on lists that are not strictly ascending gives an unspecified y (never
  * an access outside the blob or ws).
  * Errors: as spax_tiered_gemv, plus SPAX_ERR_PARAM (gap < 0, unknown transfer, packed_host
- * not pinned host memory mapped for the device, and for SPAX_PINNED_MEMCPY lists read back not
- * ascending) and SPAX_ERR_WORKSPACE.
+ * not pinned host memory mapped for the device, and for the host-merged transfers lists read
+ * back not ascending) and SPAX_ERR_WORKSPACE.
  */
 int spax_tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const uint16_t* x,
                             const int32_t* full_idx, const int32_t* approx_idx,
@@ -328,12 +364,13 @@ enum {
   /* one stand-alone mask launch (spax_build_tiers' kernel, which also clears y) and one
    * GEMV launch (spax_tiered_gemv's kernel) per phase */
   SPAX_STEP_SEPARATE = 1,
-  /* every phase's mask in one launch, then every phase's GEMV in one persistent launch.
+  /* every phase's mask in one launch, then every phase's GEMV in one persistent launch per
+   * base format present (fp16 phases, then int4 phases).
    * Only for phases that are independent: all x ready when the step is enqueued, and no
    * phase's outputs (tier, lists, counts, y) overlapping another phase's inputs or outputs
    * (checked; SPAX_ERR_PARAM).  Needs ws of spax_step_workspace_bytes bytes (per-phase
    * descriptor tables, copied from a library-owned pinned ring of host buffers, so not
-   * capturable in a graph).  events: [0, 1] bracket the mask launch, [2, 3] the GEMV launch
+   * capturable in a graph).  events: [0, 1] bracket the mask launch, [2, 3] the GEMV launches
    * (one phase: [0, 1] bracket both).  Cannot be combined with SPAX_STEP_SEPARATE. */
   SPAX_STEP_BATCHED = 2
 };

@@ -377,7 +377,7 @@ def test_pinned_gemv_validation():
                                             args["approx_idx"], args["counts"], args["y"], gap,
                                             ws, ws_bytes=ws_bytes, stream=0, transfer=transfer)
     for kw, status in ((dict(gap=-1), _lib.SPAX_ERR_PARAM), (dict(ws=0), _lib.SPAX_ERR_NULL),
-                       (dict(transfer=2), _lib.SPAX_ERR_PARAM),
+                       (dict(transfer=3), _lib.SPAX_ERR_PARAM),
                        (dict(ws_bytes=need - 1), _lib.SPAX_ERR_WORKSPACE),
                        (dict(ws=FAKE + 64), _lib.SPAX_ERR_ALIGN),
                        (dict(packed=FAKE + 64), _lib.SPAX_ERR_ALIGN),

@@ -7,7 +7,8 @@
   25% FULL / 35% APPROX / 40% skipped.
 * Llama-3-8B-shaped projections (q|k|v 4096 -> 4096 + 1024 + 1024, gate|up 4096 -> 2 x 14336,
   down 14336 -> 4096) with the blob in pinned host memory, TopK 20% / 30% / 50% of
-  channel-scaled Laplace activations, through spax_tiered_gemv_pinned in both transfer modes.
+  channel-scaled Laplace activations, through spax_tiered_gemv_pinned in all three transfer
+  modes.
 
 Masks, lists and counts are compared with the oracle bit for bit over every channel; y over
 every row, against relative L2 1e-3 and the per-row fp32 rounding bound of
@@ -109,7 +110,7 @@ PINNED_PHASES = [(name, d_in, d_out) for name, d_in, d_out in synth.decoder_phas
                  if name in ("qkv", "gateup", "down")]
 
 
-@pytest.mark.parametrize("transfer", [0, 1])
+@pytest.mark.parametrize("transfer", [0, 1, 2])
 @pytest.mark.parametrize("phase", PINNED_PHASES, ids=[p[0] for p in PINNED_PHASES])
 def test_pinned_projection_8b_full_size(env, phase, transfer):
     """A Llama-3-8B projection group through the pinned-host path: y over every row against

@@ -225,6 +225,9 @@ GEMV_CASES = [
     (257, [4096], 0, 128, 0.0, 1.0), (257, [4096], 0, 128, 1.0, 0.0),
     (64, [128], 1, 128, 0.3, 0.3), (333, [1152], 1, 128, 0.25, 0.35), (900, [4096, 512], 1, 64, 0.3, 0.3),
     (100, [640], 1, 128, 1.0, 0.0),
+    # int4 layouts use 2048-row tiles (32 rows per lane): several tiles and a ragged last one
+    (1500, [4096, 2048, 2048, 1152], 1, 128, 0.2, 0.3), (257, [2048], 1, 64, 0.0, 1.0),
+    (4000, [6144], 1, 128, 0.25, 0.35), (3, [128], 1, 64, 0.5, 0.5),
 ]
 
 

@@ -1,5 +1,7 @@
 """GPU parity of the pinned-host path (spax_tiered_gemv_pinned): the blob in pinned host
-memory, merged record ranges copied over PCIe into a compacted staging area, then the GEMV.
+memory, merged record ranges copied over PCIe into a compacted staging area (one copy per
+range, a copy kernel reading the mapped blob, or host threads gathering the ranges into one
+pinned buffer moved by one copy), then the GEMV.
 
 y against the oracle (rel-L2 <= 1e-3 and the per-row fp32 bound of tests/parity_util.py) and
 against spax_tiered_gemv on the device copy of the
@@ -61,7 +63,7 @@ def run_pinned(env, L, host, b, gap, transfer=0):
     return y.cpu().numpy(), st
 
 
-@pytest.mark.parametrize("transfer", [0, 1])
+@pytest.mark.parametrize("transfer", [0, 1, 2])
 @pytest.mark.parametrize("fmt,G", [(0, 128), (1, 128), (0, 64)])
 @pytest.mark.parametrize("gap", [0, 3])
 def test_pinned_matches_oracle_and_device_path(env, fmt, G, gap, transfer):
@@ -88,7 +90,8 @@ def test_pinned_matches_oracle_and_device_path(env, fmt, G, gap, transfer):
 
 def expected_upload(d, led, transfer):
     """Bytes of list data sent host -> device: none for the gather transfer (the ranges are
-    merged on the device); for the memcpy transfer one upload of the two compacted host lists
+    merged on the device); for the memcpy and host-gather transfers one upload of the two
+    compacted host lists
     (d entries each) up to the last one in use."""
     if transfer == 1:
         return 0
@@ -96,7 +99,7 @@ def expected_upload(d, led, transfer):
     return 4 * (d + la if la else lf)
 
 
-@pytest.mark.parametrize("transfer", [0, 1])
+@pytest.mark.parametrize("transfer", [0, 1, 2])
 def test_pinned_all_skip_and_all_full(env, transfer):
     torch, spax, dev = env
     d_in, d_out = 1000, [768]
@@ -111,7 +114,7 @@ def test_pinned_all_skip_and_all_full(env, transfer):
     assert st.n_ranges == 1 and st.moved_bytes == d_in * O.stride_F   # one range: every column
 
 
-@pytest.mark.parametrize("transfer", [0, 1])
+@pytest.mark.parametrize("transfer", [0, 1, 2])
 def test_pinned_repeated_calls_and_wide_gap(env, transfer):
     torch, spax, dev = env
     d_in, d_out = 4096, [1024]
