@@ -115,18 +115,19 @@ __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDe
     const int local = item - g.item0;
     const int tile = (int)((uint32_t)local % (uint32_t)g.sh.n_tiles);
     const int chunk = (int)((uint32_t)local / (uint32_t)g.sh.n_tiles);
-    gemv::gemv_item<FMT>(g.sh, g.packed, g.x32, g.full_idx, g.approx_idx, g.counts, g.y, tile,
-                         chunk, red);
+    gemv::gemv_item<FMT, false, gemv::ItemRows<FMT>::rpl, gemv::ItemRows<FMT>::unroll>(
+        g.sh, g.packed, g.x32, g.full_idx, g.approx_idx, g.counts, g.y, tile, chunk, red);
     __syncthreads();  // red is reused by the next item
   }
 }
 
 // Column chunks of a batched phase: about 2048 input channels each, so a work item streams
-// hundreds of columns and its fixed cost (lists, reduction, atomics) stays small.
+// hundreds of columns and its fixed cost (lists, reduction, atomics) stays small.  For int4
+// layouts (2048-row tiles) 512 to 6144 channels were measured; 2048 was the fastest.
 GemvPlan batched_plan(const spax_layout* L) {
   constexpr int channels = 2048;
   GemvPlan p{};
-  const int rows = gemv_tile_rows(L);
+  const int rows = batched_tile_rows(L);
   p.n_tiles = (int32_t)((L->d_out_total + rows - 1) / rows);
   int k = (L->d_in + channels - 1) / channels;
   const int kmax = L->d_in / 16 > 1 ? L->d_in / 16 : 1;

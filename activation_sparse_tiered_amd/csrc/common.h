@@ -53,9 +53,10 @@ int launch_pack(const spax_layout* L, const uint16_t* const* W, const int32_t* p
 
 // ------------------------------------------------------------------ gemv
 constexpr int kTileRows = 512;       // rows per workgroup tile (64 lanes x 8 rows)
-// Rows per tile of the stand-alone and batched GEMVs: an int4 layout's lanes own 32 rows
-// each (one 16-byte code load per column), an fp16 layout's 8.
-inline int gemv_tile_rows(const spax_layout* L) {
+// Rows per tile of the batched GEMV: an int4 layout's lanes own 32 rows each (one 16-byte
+// code load per column), an fp16 layout's 8.  (The stand-alone GEMV, whose launch covers one
+// phase, keeps 512-row tiles for both: it needs many small work items.)
+inline int batched_tile_rows(const spax_layout* L) {
   return L->base_fmt == SPAX_FMT_INT4 ? 2048 : kTileRows;
 }
 #ifndef SPAX_GEMV_THREADS

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
     gemv::Shape sh, const uint8_t* __restrict__ packed, const uint32_t* __restrict__ x32,
     const int32_t* __restrict__ full_idx, const int32_t* __restrict__ approx_idx,
     const int32_t* __restrict__ counts, float* __restrict__ y) {
-  __shared__ float red[kWaves * gemv::ItemRows<FMT>::tile];
+  __shared__ float red[kWaves * kTileRows];
   const int item = gemv::xcd_order((int)blockIdx.x, (int)gridDim.x);
   const int tile = (int)((uint32_t)item % (uint32_t)sh.n_tiles);
   const int chunk = (int)((uint32_t)item / (uint32_t)sh.n_tiles);
@@ -142,8 +142,7 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float4* __restrict__ p, i
 GemvPlan gemv_plan(const spax_layout* L) {
   GemvPlan p{};
   const int64_t T = L->d_out_total;
-  const int rows = gemv_tile_rows(L);
-  p.n_tiles = (int32_t)((T + rows - 1) / rows);
+  p.n_tiles = (int32_t)((T + kTileRows - 1) / kTileRows);
   // Split-K: aim for about 1024 workgroups (four per compute unit), but keep >= 16 input
   // channels per chunk.
   constexpr int target = 1024;

@@ -12,7 +12,7 @@
 //   FULL fp16 : one 16-byte load per column (8 halves), fp32 FMA with fp16 operands;
 //   FULL int4 : 4 bytes of codes (8 nibbles) + the (s, z) word of the lane's group;
 //   APPROX 2b : 2 bytes of codes (8 two-bit codes) + the (s, z) word of the lane's group.
-// RPL = 32 (int4 layouts in the stand-alone and batched GEMVs): one 16-byte load of 32 int4
+// RPL = 32 (int4 layouts in the batched GEMV): one 16-byte load of 32 int4
 // codes, or one 8-byte load of 32 two-bit codes, plus the group's (s, z) word per column, so a
 // wave keeps as many bytes in flight per column as an fp16 wave.
 // A group spans >= 64 rows, so the zero-point term is the same for all of a lane's rows and
@@ -307,28 +307,28 @@ struct TileOffsets {
         szoffF((uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u) {}
 };
 
-// The registers of one round: up to kUnroll FULL and kUnroll APPROX columns.  RPL 8: vf holds
-// a fp16 column's 8 halves, cf / ca a dword of int4 / two-bit codes.  RPL 32: vf holds 32 int4
-// codes, va 32 two-bit codes (in .x, .y).
-template <int FMT, int RPL = 8>
+// The registers of one round: up to U FULL and U APPROX columns.  RPL 8: vf holds a fp16
+// column's 8 halves, cf / ca a dword of int4 / two-bit codes.  RPL 32: vf holds 32 int4 codes,
+// va 32 two-bit codes (in .x, .y).
+template <int FMT, int RPL = 8, int U = kUnroll>
 struct RoundLoads {
-  float xf[kUnroll], xa[kUnroll];
-  uint4 vf[kUnroll];
-  uint2 va[kUnroll];
-  uint32_t cf[kUnroll], sf[kUnroll], ca[kUnroll], sa[kUnroll];
+  float xf[U], xa[U];
+  uint4 vf[U];
+  uint2 va[U];
+  uint32_t cf[U], sf[U], ca[U], sa[U];
 };
 
 // Issues the loads of FULL columns [fi, fi + nf) of srcF and APPROX columns [ai, ai + na) of
-// srcA (counts wave-uniform, at most kUnroll, may be <= 0).  Slots past a count keep zero
-// data and a zero activation.
-template <int FMT, int RPL = 8, class SrcF, class SrcA>
+// srcA (counts wave-uniform, at most U, may be <= 0).  Slots past a count keep zero data and
+// a zero activation.
+template <int FMT, int RPL = 8, int U = kUnroll, class SrcF, class SrcA>
 __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __restrict__ packed,
                                             const TileOffsets<FMT, RPL>& g, const SrcF& srcF,
                                             int fi, int nf, const SrcA& srcA, int ai, int na,
-                                            RoundLoads<FMT, RPL>& r) {
+                                            RoundLoads<FMT, RPL, U>& r) {
   const uint8_t* regionA = packed + sh.off_A;
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     r.xf[u] = 0.0f;
     r.xa[u] = 0.0f;
     r.vf[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -336,7 +336,7 @@ __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __re
     r.cf[u] = r.sf[u] = r.ca[u] = r.sa[u] = 0u;
   }
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     if (u < nf) {
       int j;
       srcF.get(fi + u, j, r.xf[u]);
@@ -350,7 +350,7 @@ __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __re
     }
   }
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     if (u < na) {
       int j;
       srcA.get(ai + u, j, r.xa[u]);
@@ -367,14 +367,14 @@ __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __re
 // every load makes the branches visible as complete to the compiler's wait tracking, which
 // otherwise assumes loads of a skipped block are still in flight in the next round and waits
 // for each of them there.
-template <int FMT, int RPL = 8>
-__device__ __forceinline__ void finish_round(const RoundLoads<FMT, RPL>& r,
+template <int FMT, int RPL = 8, int U = kUnroll>
+__device__ __forceinline__ void finish_round(const RoundLoads<FMT, RPL, U>& r,
                                              const TileOffsets<FMT, RPL>& g, int nf, int na,
                                              float (&acc)[RPL], float& zsum) {
   __builtin_amdgcn_s_waitcnt(0);
   if (nf > 0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (FMT == SPAX_FMT_FP16) {
         fma_fp16x8(acc, r.xf[u], r.vf[u]);
       } else if (RPL == 8) {
@@ -390,7 +390,7 @@ __device__ __forceinline__ void finish_round(const RoundLoads<FMT, RPL>& r,
   }
   if (na > 0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (RPL == 8) {
         fma_int2x8(acc, group_terms<2>(r.xa[u], r.sa[u], zsum), r.ca[u], g.selA);
       } else {  // 32 rows: bytes 2k, 2k + 1 of the 8 bytes hold rows 8k .. 8k + 7
@@ -413,7 +413,7 @@ __device__ __forceinline__ void finish_round(const RoundLoads<FMT, RPL>& r,
 // the previous round are still in flight and makes every load wait for all earlier ones.
 // `row` is the lane's first row (or 0 for lanes past the last row, which read valid memory
 // and are never stored).
-template <int FMT, int RPL = 8, class SrcF, class SrcA>
+template <int FMT, int RPL = 8, int U = kUnroll, class SrcF, class SrcA>
 __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* __restrict__ packed,
                                                int row, int fb, int fe, const SrcF& srcF, int ab,
                                                int ae, const SrcA& srcA, float (&acc)[RPL],
@@ -421,10 +421,10 @@ __device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* _
   const TileOffsets<FMT, RPL> g(sh, row);
   int fi = fb, ai = ab;
   while (fi < fe || ai < ae) {
-    const int nf = min(fe - fi, kUnroll), na = min(ae - ai, kUnroll);  // may be <= 0
-    RoundLoads<FMT, RPL> r;
-    issue_round<FMT, RPL>(sh, packed, g, srcF, fi, nf, srcA, ai, na, r);
-    finish_round<FMT, RPL>(r, g, nf, na, acc, zsum);
+    const int nf = min(fe - fi, U), na = min(ae - ai, U);  // may be <= 0
+    RoundLoads<FMT, RPL, U> r;
+    issue_round<FMT, RPL, U>(sh, packed, g, srcF, fi, nf, srcA, ai, na, r);
+    finish_round<FMT, RPL, U>(r, g, nf, na, acc, zsum);
     fi += max(nf, 0);
     ai += max(na, 0);
   }
@@ -482,20 +482,24 @@ __device__ __forceinline__ void finish_tile(float (*red)[64 * RPL], const float 
   }
 }
 
-// Rows per lane of the stand-alone and batched GEMVs for a base format (tile = 64 RPL rows;
-// the host's gemv_tile_rows gives the same tile).
+// Rows per lane and columns per round of the batched GEMV for a base format (tile = 64 RPL
+// rows; the host's batched_tile_rows gives the same tile).  int4: 32 rows per lane, so a wave
+// keeps four times the bytes in flight per column; 4 columns per round (6 and 8 measured
+// slower: more registers, fewer resident waves).
 template <int FMT>
 struct ItemRows {
   static constexpr int rpl = FMT == SPAX_FMT_INT4 ? 32 : 8;
   static constexpr int tile = 64 * rpl;
+  static constexpr int unroll = kUnroll;
 };
 
 // One work item of the stand-alone GEMV: row tile `tile`, column chunk `chunk` of the lists
 // in global memory (counts and indices clamped to [0, d_in], so malformed lists cannot
 // address outside the blob).  kCompact: the lists hold slot | channel << 16 entries into a
 // compacted staging copy of the records (`packed` is then the staging buffer).  A workgroup
-// of kWaves waves; ends after the tile's atomics.  red: kWaves x ItemRows<FMT>::tile floats.
-template <int FMT, bool kCompact = false>
+// of kWaves waves; RPL rows per lane (a 64 RPL-row tile), U columns per round; ends after the
+// tile's atomics.  red: kWaves x 64 RPL floats.
+template <int FMT, bool kCompact = false, int RPL = 8, int U = kUnroll>
 __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __restrict__ packed,
                                           const uint32_t* __restrict__ x32,
                                           const int32_t* __restrict__ full_idx,
@@ -503,11 +507,10 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
                                           const int32_t* __restrict__ counts,
                                           float* __restrict__ y, int tile, int chunk,
                                           float* red) {
-  constexpr int RPL = ItemRows<FMT>::rpl;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = sh.T;
-  const int row0 = tile * ItemRows<FMT>::tile;
+  const int row0 = tile * 64 * RPL;
   // Lanes past the last row (ragged last tile) read the record's first rows instead, which
   // is always in bounds; their sums land in rows >= T and are never stored.  Every matrix
   // height is a multiple of 64, so a lane's rows are all inside or all past T.
@@ -532,8 +535,8 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
     const int fend = min(fi + 64, wfe), aend = min(ai + 64, wae);
     RegBlock bf, ba;
     load_blocks<kCompact>(full_idx, approx_idx, x16, fi, fend, ai, aend, jmax, bf, ba);
-    stream_columns<FMT, RPL>(sh, packed, row, fi, max(fi, fend), bf, ai, max(ai, aend), ba, acc,
-                             zsum);
+    stream_columns<FMT, RPL, U>(sh, packed, row, fi, max(fi, fend), bf, ai, max(ai, aend), ba,
+                                acc, zsum);
   }
   finish_tile<kWaves, RPL>(reinterpret_cast<float(*)[64 * RPL]>(red), acc, zsum, wave, lane,
                            row0, T, sh.n_chunks, y);

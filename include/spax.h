@@ -100,13 +100,19 @@ typedef struct spax_layout {
 } spax_layout;
 
 /* Validate the inputs of *L and fill its derived fields.  Host only; enqueues nothing.
+ * Pages: eigenradar commentary on SpAx, "The route outside GPU memory", first paragraph (each
+ * weight column has an original and a two-bit approximate form) and third paragraph (columns
+ * used together are stored together); the SpAx Abstract's 16-bit and 4-bit weights give the
+ * two base formats.
  * Errors: SPAX_ERR_NULL; SPAX_ERR_SHAPE if n_mats, d_in, a group size or the format is
  * out of range, or any d_out[m] is not a positive multiple of approx_group (and of
  * base_group for INT4). */
 int spax_layout_init(spax_layout* L);
 
 /*
- * Pack fp16 weights into the blob (offline, once per weight set).
+ * Pack fp16 weights into the blob (offline, once per weight set).  Pages: eigenradar
+ * commentary on SpAx, "The route outside GPU memory", first and third paragraphs (an original
+ * and a two-bit form of every column, prepared ahead of decoding and stored together).
  *   W[m]   : host array of n_mats device pointers; W[m] is matrix m stored column-major
  *            as d_in records of d_out[m] fp16 values (the record of channel j is column j).
  *   packed : device pointer, total_bytes, 256-byte aligned; fully overwritten, padding
@@ -196,7 +202,10 @@ int spax_build_tiers(const uint16_t* x, int32_t d_in, const spax_tier_params* p,
 size_t spax_gemv_workspace_bytes(const spax_layout* L);
 
 /*
- * y = tiered product of one packed blob with one activation vector.
+ * y = tiered product of one packed blob with one activation vector.  Pages: SpAx Abstract
+ * (read the original weights of the largest activations, the compressed approximation for
+ * smaller ones, nothing for those closest to zero); eigenradar commentary, "The route outside
+ * GPU memory", third paragraph (the two-bit approximation is reconstructed on the GPU).
  *   packed      : device blob laid out by *L (spax_pack_columns), 256-byte aligned.
  *   x           : device, d_in fp16 activations (the same vector the mask was built from),
  *                 4-byte aligned; for odd d_in the kernels may read the two bytes that pad
@@ -412,7 +421,7 @@ int spax_decode_step_projections(const spax_step* step, hipStream_t stream);
  * step->ws and step->ws_bytes are ignored.  The only form that needs a workspace,
  * SPAX_STEP_BATCHED, keeps its descriptor tables in a static device array of the library
  * (256 KiB per GPU, held until the process ends; about 208 bytes per phase, so at most
- * 1260 phases, else SPAX_ERR_WORKSPACE), filled from a static host buffer by one copy on
+ * 1257 phases, else SPAX_ERR_WORKSPACE), filled from a static host buffer by one copy on
  * `stream`.  The call makes no hipMalloc, hipHostMalloc or hipFree call (its first call on a
  * device looks up the array's address and creates one event).  Every call on one GPU shares
  * that array: calls that overlap on one GPU (different streams, or host threads on one
@@ -441,11 +450,15 @@ int spax_read_probe(const void* p, size_t bytes, uint32_t* out, int32_t out_word
 /* ---------------------------------------------------------------- host helpers */
 
 /* K(tau): smallest fp16 magnitude key k in [0, 0x7C00] with half(k) >= tau (compared in
- * double), else 0x7C01.  Returns -1 for NaN. */
+ * double), else 0x7C01.  Returns -1 for NaN.  Pages: TopK-Guided section 2.1 (the natural
+ * sparsity of a token counts activations below a calibrated threshold); the threshold is
+ * compared on fp16 keys so the device compares integers only. */
 int32_t spax_key_threshold(double tau);
 
 /* Fixed keep fractions -> counts by cumulative round-half-up:
- * n_full = floor(p_full*d + 0.5), n_keep = floor((p_full + p_approx)*d + 0.5). */
+ * n_full = floor(p_full*d + 0.5), n_keep = floor((p_full + p_approx)*d + 0.5).  Pages:
+ * TopK-Guided Abstract and section 1 (a TopK mask keeps a fixed count per token); the pages
+ * give no rounding, cumulative round-half-up is this library's choice. */
 int spax_counts_from_fractions(int32_t d, double p_full, double p_approx,
                                int32_t* n_full, int32_t* n_approx);
 
