@@ -248,46 +248,6 @@ struct LdsBlock {
   }
 };
 
-// Up to P FULL columns whose loads are issued ahead of the rest of the work and multiplied
-// later (the fused decode kernel issues them while its mask is still being completed, so
-// their memory latency overlaps that work).  Entries as in LdsBlock.  All P loads are issued
-// (a conditional load would make the compiler copy its result right away, which waits for
-// it): slots past n load the entry the caller put there (a repeat of a used column, which
-// costs no extra HBM traffic, or column 0) and are multiplied by a zero activation.
-template <int FMT, int P>
-struct EarlyColumns {
-  float xv[P];
-  uint4 v[P];
-  uint32_t c[P], sz[P];
-  __device__ __forceinline__ void issue(const Shape& sh, const uint8_t* __restrict__ packed,
-                                        int row, const uint32_t (&e)[P], int n, uint32_t jmax) {
-    const uint32_t loffF = FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u;
-    const uint32_t szoffF = (uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u;
-#pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const uint32_t j = min(e[u] & 0xFFFFu, jmax);
-      xv[u] = u < n ? half_hi(e[u]) : 0.0f;
-      const Record rec(packed + (int64_t)j * sh.stride_F, sh.stride_F);
-      if (FMT == SPAX_FMT_FP16) {
-        v[u] = rec.stream128(loffF);
-      } else {
-        c[u] = rec.stream32(loffF);
-        sz[u] = rec.word(szoffF);
-      }
-    }
-  }
-  __device__ __forceinline__ void multiply(float (&acc)[8], float& zsum) const {
-#pragma unroll
-    for (int u = 0; u < P; ++u) {
-      if (FMT == SPAX_FMT_FP16) {
-        fma_fp16x8(acc, xv[u], v[u]);
-      } else {
-        fma_int4x8(acc, group_terms<4>(xv[u], sz[u], zsum), c[u]);
-      }
-    }
-  }
-};
-
 // A lane's byte offsets inside a column record for its rows of the tile.
 template <int FMT, int RPL = 8>
 struct TileOffsets {

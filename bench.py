@@ -264,33 +264,27 @@ def _strip_c_comments(text: str) -> str:
     return " ".join(code.split())
 
 
-def _compiler_id():
-    """The hipcc version banner (the compiler that builds the kernels), or '' if absent."""
-    import subprocess
+def _build_id():
+    """Flags and compiler banner recorded by the build next to the library ('' if absent)."""
+    path = os.path.join(ROOT, "activation_sparse_tiered_amd", "libspax.so.buildinfo")
     try:
-        r = subprocess.run(["hipcc", "--version"], capture_output=True, text=True, timeout=60)
-        return " ".join(r.stdout.split())
-    except (OSError, subprocess.SubprocessError):
+        with open(path, encoding="utf-8") as fh:
+            return " ".join(fh.read().split())
+    except OSError:
         return ""
 
 
 def sources_sha256():
     """sha256 over the fused kernel's sources without their comments (name, then text; in
-    the order of KERNEL_SOURCES), the build flags and the compiler's version banner: the
-    recorded byte counters stay valid only for the same code built the same way."""
+    the order of KERNEL_SOURCES), then the build flags and compiler banner the build recorded:
+    the recorded byte counters stay valid only for the same code built the same way."""
     import hashlib
-    import importlib.util
-    spec = importlib.util.spec_from_file_location(
-        "_spax_build_flags", os.path.join(ROOT, "activation_sparse_tiered_amd", "build.py"))
-    b = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(b)
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         h.update(os.path.basename(f).encode())
         with open(f, encoding="utf-8") as fh:
             h.update(_strip_c_comments(fh.read()).encode())
-    h.update(" ".join(x for x in b.FLAGS if not x.startswith("-I")).encode())
-    h.update(_compiler_id().encode())
+    h.update(_build_id().encode())
     return h.hexdigest()
 
 
