@@ -121,11 +121,15 @@ int check_gemv_args(const spax_layout* L, const void* packed, const uint16_t* x,
 int validate_step(const spax_step* step, bool noalloc) {
   if (!step || !step->phases) return fail(SPAX_ERR_NULL, "step and step->phases are required");
   if (step->n_phases < 1) return fail(SPAX_ERR_SHAPE, "n_phases %d < 1", step->n_phases);
-  if (step->flags & ~(SPAX_STEP_SEPARATE | SPAX_STEP_BATCHED))
+  if (step->flags & ~(SPAX_STEP_SEPARATE | SPAX_STEP_BATCHED | SPAX_STEP_DETERMINISTIC))
     return fail(SPAX_ERR_UNSUPPORTED, "unknown step flags 0x%x", step->flags);
   const bool batched = (step->flags & SPAX_STEP_BATCHED) != 0;
+  const bool deterministic = (step->flags & SPAX_STEP_DETERMINISTIC) != 0;
   if (batched && (step->flags & SPAX_STEP_SEPARATE))
     return fail(SPAX_ERR_PARAM, "SPAX_STEP_BATCHED cannot be combined with SPAX_STEP_SEPARATE");
+  if (deterministic && (batched || noalloc))
+    return fail(SPAX_ERR_UNSUPPORTED, "SPAX_STEP_DETERMINISTIC is not available %s",
+                batched ? "with SPAX_STEP_BATCHED" : "without a workspace");
   // The per-phase GEMV needs no workspace (checked against a size of 0 when none is used).
   const void* ws = noalloc ? nullptr : step->ws;
   const size_t ws_bytes = noalloc ? 0 : step->ws_bytes;
@@ -143,6 +147,15 @@ int validate_step(const spax_step* step, bool noalloc) {
     if (st) return phase_fail(st, i);
     st = check_phase_aliasing(ph);
     if (st) return phase_fail(st, i);
+  }
+  if (deterministic) {
+    const size_t need = deterministic_workspace_bytes(step->phases, step->n_phases);
+    if (need > 0 && (!step->ws || step->ws_bytes < need))
+      return fail(SPAX_ERR_WORKSPACE, "SPAX_STEP_DETERMINISTIC needs a workspace of %zu bytes",
+                  need);
+    for (int i = 0; i < step->n_phases; ++i)
+      if (need > 0 && phase_touches(step->phases[i], step->ws, need))
+        return fail(SPAX_ERR_PARAM, "the workspace overlaps a buffer of phase %d", i);
   }
   if (batched) {
     const size_t need = batched_workspace_bytes(step->n_phases);
@@ -304,7 +317,8 @@ size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases) {
     const size_t b = gemv_plan(phases[i].layout).ws_bytes;
     if (b > mx) mx = b;
   }
-  return mx;
+  const size_t det = deterministic_workspace_bytes(phases, n_phases);
+  return det > mx ? det : mx;
 }
 
 int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {

@@ -129,9 +129,17 @@ int launch_merge_and_gather(const spax_layout* L, const void* host_dev, void* st
 // whenever the plan splits K.
 // compact: the lists hold slot | channel << 16 entries into a compacted staging copy of the
 // records, which `packed` then points to (pinned-host path).
+// partials (deterministic mode): n_chunks x d_out_total floats; the chunks' partial sums are
+// stored there and a second launch adds them in chunk order into y (y is then not cleared).
 int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* packed,
                        const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
                        const int32_t* counts, float* y, bool y_zeroed, hipStream_t s,
-                       bool compact = false);
+                       bool compact = false, float* partials = nullptr);
+// y = sum over the chunks of partials[c][0 .. T), c in increasing order (T a multiple of 4).
+int launch_reduce_chunks(const float* partials, int32_t n_chunks, int64_t T, float* y,
+                         hipStream_t s);
+// Deterministic mode: bytes of the partial sums of the widest phase of a step (0 if none has
+// more than one column chunk).
+size_t deterministic_workspace_bytes(const spax_phase* phases, int32_t n_phases);
 
 }  // namespace spax

@@ -44,6 +44,8 @@ struct FusedArgs {
   int32_t* approx_idx;
   int32_t* counts;
   float* y;
+  float* partials;   // deterministic mode: chunk c's tile goes to partials[c][...] (NULL: atomics)
+  int32_t own_only;  // deterministic mode: each wave streams only its own lists
   float4* y_next;    // cleared as a side job (NULL: none)
   int32_t n_next4;   // float4s of y_next
   int32_t per_next;  // float4s cleared per workgroup
@@ -76,15 +78,17 @@ __device__ __forceinline__ void wave_lds_fence() {
 // or past the length, so the list drops out of the next look, and the loop ends after at
 // most kFusedWaves such misses.  Returns the count (0: no work left) and sets `base`, the
 // entry's index from the start of the lists (wave v's FULL list at 2 v S, its APPROX list at
-// 2 v S + S).  Wave-uniform.
+// 2 v S + S).  Wave-uniform.  own_only: only the wave's own list is looked at, so which
+// wave adds which column (and so the rounding of the tile) does not depend on timing.
 __device__ __forceinline__ int claim_entries(int (*q)[kFusedWaves], int t, int wave, int S,
-                                             int lane, int& base) {
+                                             int lane, int& base, bool own_only) {
 #pragma unroll 1
   for (int miss = 0; miss <= kFusedWaves; ++miss) {
     const int v_l = lane & (kFusedWaves - 1);
     const int c = __hip_atomic_load(&q[2 + t][v_l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const int seen = __hip_atomic_load(&q[t][v_l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint32_t m = (uint32_t)__ballot(lane < kFusedWaves && seen < c);  // wave v: bit v
+    uint32_t m = (uint32_t)__ballot(lane < kFusedWaves && seen < c);  // wave v: bit v
+    if (own_only) m &= 1u << wave;
     if (m == 0u) return 0;
     const uint32_t rot = ((m >> wave) | (m << (kFusedWaves - wave))) & 0xFFFFu;  // own wave first
     const int v = (wave + (int)__builtin_ctz(rot)) & (kFusedWaves - 1);
@@ -138,7 +142,9 @@ __device__ __forceinline__ int ties_between(const uint32_t* xs32, int begin, int
 //      counting the equal keys before its first channel only when it holds such a tie) and
 //      lists its FULL and APPROX columns in LDS;
 //   3. each wave streams its own list and then takes columns from the other waves' lists
-//      until all are done (claim_entries); the tile is reduced across waves and added to y.
+//      until all are done (claim_entries; in deterministic mode a wave keeps to its own
+//      list); the tile is reduced across waves and added to y (deterministic mode: stored
+//      as the chunk's partial sums).
 // (Issuing each wave's first FULL columns as soon as the FULL boundary's coarse bin was known,
 // before the exact boundaries, measured 0.55% slower per token: the selection and the issue
 // lengthened every wave's path to the boundary search more than the early bytes saved.)
@@ -252,6 +258,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     __hip_atomic_store(&u.kh.lists_q[3][wave], nA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   const uint32_t* lists = reinterpret_cast<const uint32_t*>(dyn + a.xs_bytes);
+  const bool own_only = a.own_only != 0;
   const gemv::TileOffsets<FMT> g(sh, row);
   while (nf > 0 || na > 0) {
     gemv::RoundLoads<FMT> r;
@@ -259,8 +266,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
                            gemv::LdsBlock(lists + bA, na, jmax), 0, na, r);
     // the next claims overlap this round's loads
     int nbF = bF, nbA = bA;
-    const int nf2 = claim_entries(u.kh.lists_q, 0, wave, S, lane, nbF);
-    const int na2 = claim_entries(u.kh.lists_q, 1, wave, S, lane, nbA);
+    const int nf2 = claim_entries(u.kh.lists_q, 0, wave, S, lane, nbF, own_only);
+    const int na2 = claim_entries(u.kh.lists_q, 1, wave, S, lane, nbA, own_only);
     gemv::finish_round<FMT>(r, g, nf, na, acc, zsum);
     nf = nf2;
     na = na2;
@@ -268,7 +275,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     bA = nbA;
   }
   __syncthreads();  // every wave is done with the mask scratch that `red` overlays
-  gemv::finish_tile<kFusedWaves>(u.red, acc, zsum, wave, lane, row0, T, sh.n_chunks, a.y);
+  gemv::finish_tile<kFusedWaves>(u.red, acc, zsum, wave, lane, row0, T, sh.n_chunks, a.y,
+                                 a.partials, chunk);
   clear_next(a);
 }
 
@@ -344,12 +352,31 @@ bool fused_phase_ok(const spax_layout* L) {
   return fused_lds(L, fused_plan(L)).bytes <= kFusedMaxDynLds;
 }
 
+size_t deterministic_workspace_bytes(const spax_phase* phases, int32_t n_phases) {
+  size_t mx = 0;
+  for (int i = 0; i < n_phases; ++i) {
+    const spax_layout* L = phases[i].layout;
+    // either launch form may run the phase
+    for (const GemvPlan& p : {gemv_plan(L), fused_phase_ok(L) ? fused_plan(L) : gemv_plan(L)}) {
+      if (p.n_chunks < 2) continue;
+      const size_t b = (size_t)p.n_chunks * (size_t)L->d_out_total * 4;
+      if (b > mx) mx = b;
+    }
+  }
+  return mx;
+}
+
 int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
   if (st->flags & SPAX_STEP_BATCHED)
     return noalloc ? launch_decode_step_batched_static(st, cu_count(), s)
                    : launch_decode_step_batched(st, cu_count(), s);
   const int n = st->n_phases;
   const bool separate = (st->flags & SPAX_STEP_SEPARATE) != 0;
+  // Deterministic mode: every phase's column chunks store their partial sums in the workspace
+  // (reused phase after phase in stream order) and one more launch adds them in chunk order;
+  // y is then never cleared or added to atomically.
+  float* partials =
+      (st->flags & SPAX_STEP_DETERMINISTIC) ? static_cast<float*>(st->ws) : nullptr;
   auto fused_phase_ok = [&](const spax_layout* L) { return !separate && spax::fused_phase_ok(L); };
   auto plan_of = [&](const spax_layout* L) { return fused_phase_ok(L) ? fused_plan(L) : gemv_plan(L); };
   // Launch i clears the y of phase i + 1 as a side job only when phase i is one fused launch,
@@ -358,7 +385,7 @@ int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
   // must not be zeroed while launch i still uses them.  Otherwise phase i + 1 clears its own
   // y with a kernel right before its launch.
   auto clears_next = [&](int i) {
-    if (i + 1 >= n) return false;
+    if (i + 1 >= n || partials) return false;
     const spax_phase& nx = st->phases[i + 1];
     return fused_phase_ok(st->phases[i].layout) && plan_of(nx.layout).n_chunks > 1 &&
            !phase_touches(st->phases[i], nx.y, 4 * (size_t)nx.layout->d_out_total);
@@ -373,8 +400,9 @@ int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
     bool cleared = i > 0 && clears_next(i - 1);
     if (!fused_phase_ok(L)) {
       // Large input vectors: stand-alone mask kernel (which clears y) + GEMV.
-      const bool clear_in_mask = plan.n_chunks > 1 && L->d_out_total <= kMaskClearMax && !cleared;
-      if (plan.n_chunks > 1 && !cleared && !clear_in_mask) {
+      const bool clear_in_mask =
+          plan.n_chunks > 1 && L->d_out_total <= kMaskClearMax && !cleared && !partials;
+      if (plan.n_chunks > 1 && !cleared && !clear_in_mask && !partials) {
         int rc = launch_zero_f32(ph.y, L->d_out_total, s);
         if (rc) return rc;
         cleared = true;
@@ -385,12 +413,12 @@ int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
       if (rc) return rc;
       if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[2 * i], s));
       rc = launch_tiered_gemv(L, plan, ph.packed, ph.x, ph.full_idx, ph.approx_idx, ph.counts,
-                              ph.y, cleared || clear_in_mask, s);
+                              ph.y, cleared || clear_in_mask, s, false, partials);
       if (rc) return rc;
       if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[2 * i + 1], s));
       continue;
     }
-    if (plan.n_chunks > 1 && !cleared) {
+    if (plan.n_chunks > 1 && !cleared && !partials) {
       int rc = launch_zero_f32(ph.y, L->d_out_total, s);
       if (rc) return rc;
     }
@@ -405,6 +433,8 @@ int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
     a.approx_idx = ph.approx_idx;
     a.counts = ph.counts;
     a.y = ph.y;
+    a.partials = plan.n_chunks > 1 ? partials : nullptr;
+    a.own_only = partials != nullptr;
     a.y_next = nullptr;
     a.n_next4 = 0;
     if (clears_next(i)) {
@@ -424,6 +454,10 @@ int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
       hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_INT4, kFusedMaxDin>), grid, blk, f.bytes, s, a);
     SPAX_HIP_CHECK(hipGetLastError());
     if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[2 * i + 1], s));
+    if (a.partials) {
+      int rc = launch_reduce_chunks(partials, plan.n_chunks, L->d_out_total, ph.y, s);
+      if (rc) return rc;
+    }
   }
   return SPAX_OK;
 }

@@ -24,13 +24,31 @@ template <int FMT, bool kCompact>
 __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
     gemv::Shape sh, const uint8_t* __restrict__ packed, const uint32_t* __restrict__ x32,
     const int32_t* __restrict__ full_idx, const int32_t* __restrict__ approx_idx,
-    const int32_t* __restrict__ counts, float* __restrict__ y) {
+    const int32_t* __restrict__ counts, float* __restrict__ y, float* __restrict__ partials) {
   __shared__ float red[kWaves * kTileRows];
   const int item = gemv::xcd_order((int)blockIdx.x, (int)gridDim.x);
   const int tile = (int)((uint32_t)item % (uint32_t)sh.n_tiles);
   const int chunk = (int)((uint32_t)item / (uint32_t)sh.n_tiles);
   gemv::gemv_item<FMT, kCompact>(sh, packed, x32, full_idx, approx_idx, counts, y, tile, chunk,
-                                 red);
+                                 red, partials);
+}
+
+// Deterministic mode: y[r] = sum over c = 0 .. n_chunks - 1, in that order, of
+// partials[c][r] (four rows per thread; T is a multiple of 4).
+__global__ __launch_bounds__(256) void reduce_chunks_kernel(const float4* __restrict__ partials,
+                                                            int32_t n_chunks, int64_t T4,
+                                                            float4* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T4) return;
+  float4 s = partials[i];
+  for (int32_t c = 1; c < n_chunks; ++c) {
+    const float4 v = partials[(int64_t)c * T4 + i];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  y[i] = s;
 }
 
 // Range merging on the device (pinned-host path, gather transfer): workgroup r merges region
@@ -195,11 +213,23 @@ int launch_merge_and_gather(const spax_layout* L, const void* host_dev, void* st
   return SPAX_OK;
 }
 
+int launch_reduce_chunks(const float* partials, int32_t n_chunks, int64_t T, float* y,
+                         hipStream_t s) {
+  const int64_t T4 = T / 4;
+  const int threads = 256;
+  hipLaunchKernelGGL(reduce_chunks_kernel, dim3((unsigned)((T4 + threads - 1) / threads)),
+                     dim3(threads), 0, s, reinterpret_cast<const float4*>(partials), n_chunks,
+                     T4, reinterpret_cast<float4*>(y));
+  SPAX_HIP_CHECK(hipGetLastError());
+  return SPAX_OK;
+}
+
 int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* packed,
                        const uint16_t* x, const int32_t* full_idx, const int32_t* approx_idx,
                        const int32_t* counts, float* y, bool y_zeroed, hipStream_t s,
-                       bool compact) {
-  if (plan.n_chunks > 1 && !y_zeroed) {
+                       bool compact, float* partials) {
+  if (plan.n_chunks == 1) partials = nullptr;  // one chunk: plain stores, already deterministic
+  if (plan.n_chunks > 1 && !y_zeroed && !partials) {
     int st = launch_zero_f32(y, L->d_out_total, s);
     if (st) return st;
   }
@@ -209,7 +239,7 @@ int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* p
   const auto* x32 = reinterpret_cast<const uint32_t*>(x);
 #define SPAX_GEMV_LAUNCH(F, C)                                                              \
   hipLaunchKernelGGL((tiered_gemv_kernel<F, C>), grid, dim3(kGemvThreads), 0, s, sh, pk, x32, \
-                     full_idx, approx_idx, counts, y)
+                     full_idx, approx_idx, counts, y, partials)
   if (L->base_fmt == SPAX_FMT_FP16) {
     if (compact) SPAX_GEMV_LAUNCH(SPAX_FMT_FP16, true);
     else SPAX_GEMV_LAUNCH(SPAX_FMT_FP16, false);
@@ -219,6 +249,7 @@ int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* p
   }
 #undef SPAX_GEMV_LAUNCH
   SPAX_HIP_CHECK(hipGetLastError());
+  if (partials) return launch_reduce_chunks(partials, plan.n_chunks, L->d_out_total, y, s);
   return SPAX_OK;
 }
 

@@ -416,11 +416,15 @@ __device__ __forceinline__ void wave_range(int b, int e, int wave, int& wb, int&
 }
 
 // Reduce the NW waves' partial rows through LDS, then write (one chunk) or atomically add
-// (several chunks, y zeroed beforehand in stream order) the 64 RPL-row tile into y.
+// (several chunks, y zeroed beforehand in stream order) the 64 RPL-row tile into y.  With
+// `partials` (deterministic mode, several chunks) the tile is stored as row block `chunk` of
+// partials[n_chunks][T] instead, for a later pass that adds the chunks in a fixed order.
 template <int NW, int RPL = 8>
 __device__ __forceinline__ void finish_tile(float (*red)[64 * RPL], const float (&acc)[RPL],
                                             float zsum, int wave, int lane, int row0, int T,
-                                            int n_chunks, float* __restrict__ y) {
+                                            int n_chunks, float* __restrict__ y,
+                                            float* __restrict__ partials = nullptr,
+                                            int chunk = 0) {
   constexpr int kRows = 64 * RPL;
   float4* dst = reinterpret_cast<float4*>(&red[wave][lane * RPL]);
 #pragma unroll
@@ -437,6 +441,7 @@ __device__ __forceinline__ void finish_tile(float (*red)[64 * RPL], const float 
       // Several chunks meet through hardware fp32 atomics at device scope; y is read only
       // after the kernel ends, so no device-scope fence is needed.
       if (n_chunks == 1) y[grow] = sum;
+      else if (partials) partials[(size_t)chunk * (size_t)T + (size_t)grow] = sum;
       else unsafeAtomicAdd(&y[grow], sum);
     }
   }
@@ -466,7 +471,7 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
                                           const int32_t* __restrict__ approx_idx,
                                           const int32_t* __restrict__ counts,
                                           float* __restrict__ y, int tile, int chunk,
-                                          float* red) {
+                                          float* red, float* __restrict__ partials = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = sh.T;
@@ -499,7 +504,7 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
                                 acc, zsum);
   }
   finish_tile<kWaves, RPL>(reinterpret_cast<float(*)[64 * RPL]>(red), acc, zsum, wave, lane,
-                           row0, T, sh.n_chunks, y);
+                           row0, T, sh.n_chunks, y, partials, chunk);
 }
 
 }  // namespace gemv

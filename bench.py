@@ -1,7 +1,8 @@
 """Benchmark of the tiered activation-sparse decoding GEMV on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode7b] [--sparsity 0.5]
-                    [--no-cpu-baseline] [--no-batched] [--no-separate] [--control none|full|skip]
+                    [--no-cpu-baseline] [--no-batched] [--no-separate] [--no-deterministic]
+                    [--control none|full|skip]
 
 Default workload (decode7b): one step is one token of a 32-layer 7B-shaped decoder: for each
 layer and each projection group (q|k|v, o, gate|up, down) one TopK-Guided tier mask (s +-
@@ -30,7 +31,8 @@ per launch, over its average launch duration (the timed step's event time over i
 the host cores.  ``batched`` is the same step in the batched launch form (all masks in one
 launch, all GEMVs in one), legal here only because the synthetic inputs are independent.
 ``separate`` is the same step through the two stand-alone kernels per phase, the mask kernel
-of spax_build_tiers and the GEMV kernel of spax_tiered_gemv.
+of spax_build_tiers and the GEMV kernel of spax_tiered_gemv.  ``deterministic`` is the step
+with SPAX_STEP_DETERMINISTIC (y identical bit for bit from run to run).
 ``token_us`` gives the median and 90th percentile over the timed tokens, each timed on its
 own after the timed region.  ``--control full|skip`` replaces the tier rule by all-FULL or
 all-SKIP masks: controls for the hardware byte counters.  ``read_probe`` gives what a plain
@@ -85,6 +87,8 @@ def parse():
                     help="skip timing the batched step form")
     ap.add_argument("--no-separate", action="store_true",
                     help="skip timing the two-launch step form")
+    ap.add_argument("--no-deterministic", action="store_true",
+                    help="skip timing the SPAX_STEP_DETERMINISTIC form")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the plain streaming-read ceiling and floor")
     ap.add_argument("--no-dense", action="store_true",
@@ -591,6 +595,18 @@ def device_bench(args, spax, torch, dev):
         separate["frac"] = round(sgbs / HBM_PEAK_GBS, 4)
         log(f"[bench] two-launch step: {separate['value'] * per_tok:.1f} us, {sgbs:.1f} GB/s")
 
+    # ---- the deterministic form (chunk partial sums in the workspace plus one fixed-order
+    # reduce launch per phase that has several column chunks; waves keep to their own lists)
+    deterministic = None
+    if not args.no_deterministic:
+        dt_ms = time_form(stack, spax.STEP_DETERMINISTIC, args)
+        dgbs = bytes_per_step / (dt_ms * 1e-3) / 1e9
+        deterministic = {"value": round(dt_ms * 1e3 / per_tok, 2), "unit": "us/token",
+                         "achieved_GBps": round(dgbs, 1), "frac": round(dgbs / HBM_PEAK_GBS, 4),
+                         "form": "SPAX_STEP_DETERMINISTIC: y identical bit for bit from run to "
+                                 "run; the fused launch per phase plus a reduce launch"}
+        log(f"[bench] deterministic step: {dt_ms * 1e3:.1f} us, {dgbs:.1f} GB/s")
+
     dense = None
     if not args.no_dense and spec["fmt"] == 0 and args.control == "none":
         dense = dense_baseline(stack)
@@ -648,6 +664,7 @@ def device_bench(args, spax, torch, dev):
         "cpu_baseline": cpu,
         "batched": batched,
         "separate": separate,
+        "deterministic": deterministic,
         "token_us": token_us,
         "read_probe": probe,
         "dense_baseline": dense,

@@ -381,7 +381,14 @@ enum {
    * descriptor tables, copied from a library-owned pinned ring of host buffers, so not
    * capturable in a graph).  events: [0, 1] bracket the mask launch, [2, 3] the GEMV launches
    * (one phase: [0, 1] bracket both).  Cannot be combined with SPAX_STEP_SEPARATE. */
-  SPAX_STEP_BATCHED = 2
+  SPAX_STEP_BATCHED = 2,
+  /* (with SPAX_STEP_DEFAULT or SPAX_STEP_SEPARATE) y identical bit for bit from run to run: a
+   * phase's column chunks store their partial sums in ws instead of adding them into y with
+   * atomics, and one more launch per phase adds the chunks in a fixed order.  Needs ws of
+   * spax_step_workspace_bytes bytes, disjoint from every phase's buffers; y need not be
+   * cleared (it is overwritten).  Not with SPAX_STEP_BATCHED, nor through
+   * spax_decode_step_projections_noalloc (SPAX_ERR_UNSUPPORTED). */
+  SPAX_STEP_DETERMINISTIC = 4
 };
 
 typedef struct spax_step {
@@ -397,9 +404,11 @@ typedef struct spax_step {
   hipEvent_t* events;
 } spax_step;
 
-/* Workspace bytes for spax_decode_step_projections over these phases: the larger of the
- * per-phase GEMV workspaces (currently 0) and the SPAX_STEP_BATCHED descriptor tables
- * (a few hundred bytes per phase).  0 for invalid input. */
+/* Workspace bytes for spax_decode_step_projections over these phases, enough for every
+ * launch form: the largest of the per-phase GEMV workspaces (currently 0), the
+ * SPAX_STEP_BATCHED descriptor tables (a few hundred bytes per phase) and the
+ * SPAX_STEP_DETERMINISTIC partial sums of the widest phase (column chunks x d_out_total
+ * floats, about 2 MB for a 7B decoder layer).  0 for invalid input. */
 size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases);
 
 /*

@@ -226,7 +226,9 @@ def test_decode_step_validates_all_phases_first():
     arr = spax.phase_array([good, good, bad])
     ws = spax.spax_step_workspace_bytes(arr)
     assert spax.spax_gemv_workspace_bytes(L) == 0
-    assert 0 < ws < 3 * 1024  # the batched form's descriptor tables
+    # the larger of the batched form's descriptor tables and the deterministic form's partial
+    # sums (column chunks x 512 rows x 4 bytes)
+    assert 0 < ws <= 64 * 512 * 4 and ws % 4 == 0
     with pytest.raises(spax.SpaxError) as e:
         spax.spax_decode_step_projections(arr, FAKE, ws_bytes=ws, stream=0)
     assert e.value.status == _lib.SPAX_ERR_PARAM and "phase 2" in str(e.value)
@@ -258,7 +260,7 @@ def test_batched_step_validation():
         spax.spax_decode_step_projections(arr, None, ws_bytes=0, flags=2, stream=0)
     assert e.value.status == _lib.SPAX_ERR_WORKSPACE
     with pytest.raises(spax.SpaxError) as e:
-        spax.spax_decode_step_projections(arr, FAKE + 512 * MB, ws_bytes=ws - 1, flags=2, stream=0)
+        spax.spax_decode_step_projections(arr, FAKE + 512 * MB, ws_bytes=64, flags=2, stream=0)
     assert e.value.status == _lib.SPAX_ERR_WORKSPACE
     shared_y = spax.phase_array([phase(0, y=FAKE + 100 * MB), phase(1, y=FAKE + 100 * MB)])
     with pytest.raises(spax.SpaxError) as e:
@@ -268,6 +270,36 @@ def test_batched_step_validation():
     with pytest.raises(spax.SpaxError) as e:
         spax.spax_decode_step_projections(y_on_x, FAKE + 512 * MB, ws_bytes=ws, flags=2, stream=0)
     assert e.value.status == _lib.SPAX_ERR_PARAM
+
+
+@needs_no_gpu
+def test_deterministic_step_validation():
+    """SPAX_STEP_DETERMINISTIC: the partial sums need the workspace, apart from every phase's
+    buffers; the flag is refused with SPAX_STEP_BATCHED and by the no-alloc call."""
+    L = spax.spax_layout_init(64, [512], 0, 128, 64)
+    arr = spax.phase_array([_fake_phase(L, spax.topk_params(4, 4), i) for i in range(2)])
+    ws = spax.spax_step_workspace_bytes(arr)
+    MB = 1 << 20
+    det = spax.STEP_DETERMINISTIC
+    for flags in (det, det | spax.STEP_SEPARATE):
+        with pytest.raises(spax.SpaxError) as e:
+            spax.spax_decode_step_projections(arr, None, ws_bytes=0, flags=flags, stream=0)
+        assert e.value.status == _lib.SPAX_ERR_WORKSPACE
+        with pytest.raises(spax.SpaxError) as e:
+            spax.spax_decode_step_projections(arr, FAKE + 512 * MB, ws_bytes=ws - 4, flags=flags,
+                                              stream=0)
+        assert e.value.status == _lib.SPAX_ERR_WORKSPACE
+        with pytest.raises(spax.SpaxError) as e:  # the workspace on phase 1's y
+            spax.spax_decode_step_projections(arr, FAKE + 22 * MB, ws_bytes=ws, flags=flags,
+                                              stream=0)
+        assert e.value.status == _lib.SPAX_ERR_PARAM and "overlap" in str(e.value)
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections(arr, FAKE + 512 * MB, ws_bytes=ws,
+                                          flags=det | spax.STEP_BATCHED, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_UNSUPPORTED
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_decode_step_projections_noalloc(arr, flags=det, stream=0)
+    assert e.value.status == _lib.SPAX_ERR_UNSUPPORTED
 
 
 @needs_no_gpu
