@@ -87,7 +87,13 @@ int spax_greedy_allocation(const double* params, int32_t n_mats, double alpha, d
   }
   const double fmean = fsum / n_mats;
   std::vector<double> step(n_mats), p(n_mats, 0.0), trial(n_mats);
-  for (int m = 0; m < n_mats; ++m) step[m] = alpha * fmean / params[m];
+  double walk = 0.0;  // increments until every matrix is at sparsity 1
+  for (int m = 0; m < n_mats; ++m) {
+    step[m] = alpha * fmean / params[m];
+    walk += 1.0 / step[m];
+  }
+  if (walk > 1e7) return fail(SPAX_ERR_PARAM, "alpha %g is too small: the walk could take %.3g "
+                              "increments (limit 1e7)", alpha, walk);
   int32_t count = 0;
   auto record = [&]() {
     if (count < cap) {
@@ -106,6 +112,10 @@ int spax_greedy_allocation(const double* params, int32_t n_mats, double alpha, d
       trial = p;
       trial[m] += step[m];
       const double e = block_error(trial.data(), n_mats, user);
+      if (!std::isfinite(e)) {
+        *n_rows = count;
+        return fail(SPAX_ERR_PARAM, "block_error returned %g for a trial of matrix %d", e, m);
+      }
       if (best < 0 || e < best_err) {
         best = m;
         best_err = e;

@@ -508,8 +508,10 @@ typedef double (*spax_block_error_fn)(const double* p, int32_t n_mats, void* use
  * layer the units are the projection groups (q|k|v, o, gate|up, down).
  *   rows   : host, cap rows of (1 + n_mats) doubles; n_rows receives the rows recorded.
  * Errors: SPAX_ERR_NULL, SPAX_ERR_PARAM (n_mats outside 1..64, alpha <= 0, P_max > 1, a
- * parameter count not finite and positive), SPAX_ERR_WORKSPACE (more rows than cap;
- * *n_rows then holds the number needed).
+ * parameter count not finite and positive, alpha so small that taking every matrix to 1
+ * would need more than 1e7 increments, or a block_error value that is not finite: *n_rows
+ * then holds the rows recorded before it), SPAX_ERR_WORKSPACE (more rows than cap; *n_rows
+ * then holds the number needed).
  */
 int spax_greedy_allocation(const double* params, int32_t n_mats, double alpha, double P_max,
                            spax_block_error_fn block_error, void* user, double* rows,

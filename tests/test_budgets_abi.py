@@ -78,3 +78,13 @@ def test_budget_errors():
     st = _lib.lib.spax_greedy_allocation(f.ctypes.data, 2, 0.1, 0.3, cb, None, rows.ctypes.data,
                                          2, C.byref(nr))
     assert st == _lib.SPAX_ERR_WORKSPACE and nr.value == 7
+
+
+def test_greedy_rejects_tiny_alpha_and_nonfinite_errors():
+    with pytest.raises(spax.SpaxError) as e:  # 2e8 increments to take both matrices to 1
+        spax.spax_greedy_allocation([100.0, 100.0], 1e-8, 0.3, lambda p: 0.0)
+    assert e.value.status == _lib.SPAX_ERR_PARAM and "too small" in str(e.value)
+    with pytest.raises(spax.SpaxError) as e:
+        spax.spax_greedy_allocation([100.0, 400.0], 0.1, 0.3,
+                                    lambda p: float("nan") if p[1] > 0 else 0.0)
+    assert e.value.status == _lib.SPAX_ERR_PARAM and "block_error" in str(e.value)
