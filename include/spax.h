@@ -300,9 +300,11 @@ enum {
    * nothing waits for the host, so the call is asynchronous unless `stats` is requested */
   SPAX_PINNED_GATHER = 1,
   /* the lists come back to the host (the call synchronizes `stream`), which merges the
-   * ranges; host threads copy the records of every range from the pinned blob into one
-   * library-owned pinned staging buffer (FULL records, then APPROX records, back to back) and
-   * one hipMemcpyAsync moves them (CPU gather, single DMA) */
+   * ranges; a pool of host threads (up to 16, started on first use) copies the records of
+   * every range from the pinned blob into one library-owned pinned staging buffer (FULL
+   * records, then APPROX records, back to back), which moves to the device in 8 MiB
+   * hipMemcpyAsync chunks, each issued as soon as it is filled (CPU gather, one DMA stream
+   * that overlaps the gathering) */
   SPAX_PINNED_HOSTGATHER = 2
 };
 
