@@ -16,7 +16,7 @@ output error, and records the allocation against the block's compute-weighted sp
 P = sum_m f_m p_m / sum_m f_m (f_m: parameter count).  A matrix's increment is inversely
 proportional to its parameter count, so every increment moves P by the same amount.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 1. Block targets: u_b = s + lambda * (mean(sigma) - sigma_b) / mean(sigma), then
    s_b = clamp(u_b + c, lo, hi) with the one shift c that makes the mean of the s_b equal

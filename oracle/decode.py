@@ -7,7 +7,7 @@ paragraphs: selection applies per generated token during batch-one decoding; the
 measured unit is bytes moved per token.  A 7B-shaped decoder layer has four groups of
 projections that each share one input vector: q|k|v, o, gate|up, down.
 
-Reading (listed in the design doc): the step is, for each layer and each group in that order,
+Reading: the step is, for each layer and each group in that order,
 one tier mask from that group's activation vector followed by one tiered GEMV of the
 fused group.  Attention and norms are not part of the path; each group's activation
 vector is an independent seeded input.

@@ -5,7 +5,7 @@ Oracle (test infrastructure only; see ``oracle/__init__.py``).
 Pages: the eigenradar commentary on SpAx, "The route outside GPU memory", third
 paragraph (jointly accessed columns are placed together; adjacent read ranges are
 merged), first paragraph (each weight column has an original and a two-bit approximate
-form).  The pages give no byte format.  Reading taken (listed in the design doc):
+form).  The pages give no byte format.  Reading taken:
 
 * Matrices that multiply the same activation vector (q|k|v; gate|up) are fused: each
   column record holds that column of every matrix, concatenated along rows.  One read

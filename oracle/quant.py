@@ -5,7 +5,7 @@ Oracle (test infrastructure only; see ``oracle/__init__.py``).
 The pages fix that the approximate tier reads a two-bit form of each weight column
 (eigenradar commentary on SpAx, "The route outside GPU memory": first and third
 paragraphs) and that it needs fewer bytes than the original (SpAx Abstract).  They do
-not give the quantizer.  Reading taken (listed in the design doc): asymmetric min-max
+not give the quantizer.  Reading taken: asymmetric min-max
 round-to-nearest per group of G consecutive rows of one column, reconstructed as
 w_hat = s*q + z with z = the group minimum and fp16 s, z.  With L = 2**bits - 1 levels:
 

@@ -7,13 +7,13 @@ accessed columns are placed together and adjacent read ranges are merged, and co
 granularity can move more bytes than the selected columns need; the last paragraph asks
 that bytes selected and bytes physically moved be counted apart.
 
-Reading (listed in the design doc): a range is a maximal run of consecutive selected channels
+Reading: a range is a maximal run of consecutive selected channels
 of one tier, in the packed (channel) order; two runs whose gap is at most ``gap``
 unselected channels are merged, and the gap columns are moved too.
 
 Storage granularity (same paragraph: coarse storage granularity can move more bytes than a
 selected column needs; last paragraph: for NVMe, selected bytes and bytes physically read
-are separate entries).  Reading (listed in the design doc): the blob sits on a device read in
+are separate entries).  Reading: the blob sits on a device read in
 blocks of ``block`` bytes, the blob starting on a block boundary; each merged range is one
 read request, and a request reads every block its bytes touch.  Two requests that touch one
 block each read it.
@@ -79,7 +79,7 @@ def storage_ledger(full_idx, approx_idx, stride_F: int, stride_A: int, off_A: in
 
 def placement_order(calib_tiers, stride_F: int, stride_A: int):
     """Offline placement of the column records (same paragraph: jointly accessed columns are
-    placed together).  Reading (listed in the design doc): from calibration masks (one tier array
+    placed together).  Reading: from calibration masks (one tier array
     per calibration token: 2 FULL, 1 APPROX, 0 SKIP), each channel scores the bytes it made
     selected (stride_F per FULL, stride_A per APPROX); records are placed by descending score,
     equal scores by channel index.  Returns ``order``: position p of the placed blob holds

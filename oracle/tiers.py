@@ -16,7 +16,7 @@ Definitions followed:
   calibrated threshold, clipped to a band of +-delta around the target, and TopK is
   then applied with that count; realised sparsity stays within +-delta.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 1. Magnitude is compared on fp16 bit patterns: ``key = bits(x) & 0x7FFF``.  For
    non-NaN values this order equals the order of ``|x|``; NaN keys (0x7C01..0x7FFF)
