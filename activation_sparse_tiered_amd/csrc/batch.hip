@@ -54,7 +54,7 @@ struct GemvDesc {
 };
 
 __global__ __launch_bounds__(kMaskThreads) void batched_mask_kernel(const MaskDesc* __restrict__ md) {
-  __shared__ mask::Shared<kMaskThreads> sh;
+  __shared__ mask::KeyHist<kMaskThreads> sh;
   __shared__ uint32_t xs32[SPAX_MAX_DIN / 2];
   const MaskDesc& m = md[blockIdx.x];
   mask::tiers_to_global<kMaskThreads, SPAX_MAX_DIN>(sh, xs32, m.ta, m.x, m.tier, m.full_idx,

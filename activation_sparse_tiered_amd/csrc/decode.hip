@@ -134,7 +134,7 @@ __device__ __forceinline__ int ties_between(const uint32_t* xs32, int begin, int
 }
 
 // One group: mask and GEMV.  Workgroup gridDim.x - 1 only writes the outputs of the mask
-// (build_plan + emit, as the stand-alone mask kernel).  Every other workgroup owns one
+// (tiers_to_global, as the stand-alone mask kernel).  Every other workgroup owns one
 // 512-row tile and one contiguous range of input channels, split over its 16 waves:
 //   1. the exact boundaries from a per-key histogram (select_begin / select_finish: one pass
 //      over the keys);
@@ -153,7 +153,6 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   extern __shared__ __align__(16) uint8_t dyn[];
   // The mask's scratch and the GEMV's cross-wave reduction are never live together.
   __shared__ union {
-    mask::Shared<kFusedThreads> msh;
     mask::KeyHist<kFusedThreads> kh;
     float red[kFusedWaves][kTileRows];
   } u;
@@ -169,7 +168,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
 
   if (blockIdx.x == gridDim.x - 1) {
     // ---- writer: tier bytes, ascending lists, counts
-    mask::tiers_to_global<kFusedThreads, MAXD>(u.msh, xs32, a.ta, a.x, a.tier, a.full_idx,
+    mask::tiers_to_global<kFusedThreads, MAXD>(u.kh, xs32, a.ta, a.x, a.tier, a.full_idx,
                                                a.approx_idx, a.counts);
     clear_next(a);
     return;

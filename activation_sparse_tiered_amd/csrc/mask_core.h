@@ -12,15 +12,15 @@
 //
 // x is copied to LDS once; wave w owns the contiguous channels [w*C, (w+1)*C), C a multiple
 // of 128.  Passes over the wave's channels:
-//   1. 256-bin histogram of the high key bits (LDS atomics into lane-group copies) and
-//      per-lane counters, summed once per wave;
-//   2. (TopK boundaries) per-wave 128-bin histograms of the low bits inside the boundary
-//      buckets, from which each wave gets its own "greater" / "equal" counts;
-//   3. emit: ranks from ballots plus per-wave bases that wave 0 derives with one scan.
+//   1. the per-key histogram (select_begin), after which two waves find the exact boundaries
+//      (select_finish);
+//   2. (tiers_to_global) per-wave counts of the keys above and equal to each boundary, from
+//      which every wave derives its list and tie bases with scans over the waves;
+//   3. emit: ranks from ballots plus those bases.
 // The kernels are issue-bound inside one CU (every wave instruction competes with those of
-// the other waves), so fixed per-wave work is kept small and is not repeated by each wave:
-// two 16-bit counts share one 32-bit lane sum (a wave holds at most 32768 channels), and a
-// step without boundary keys skips the tie ranking.
+// the other waves), so fixed per-wave work is kept small: two 16-bit counts share one 32-bit
+// lane sum (a wave holds at most 2048 channels), and a step without boundary keys skips the
+// tie ranking.
 #pragma once
 
 #include <climits>
@@ -33,26 +33,6 @@ namespace mask {
 struct Select {
   int32_t kb;  // boundary key
   int32_t m;   // channels with key == kb that are selected (lowest indices first)
-};
-
-template <int NT>
-struct Shared {
-  static constexpr int W = NT / 64;
-  // Level-1 histogram in 8 copies (one per lane & 7, odd stride so the copies of a bin sit
-  // in different banks): lanes whose keys share a bin mostly hit different addresses.
-  static constexpr int kCopies = 8, kStride = 257;
-  static constexpr int kRep = (kCopies * kStride + 3) / 4 * 4;
-  alignas(16) int hist_rep[kRep];
-  alignas(16) int wave_hist[2][W][128];
-  int hist_hi[256];
-  int wave_cnt[W][2];   // (gt | eq << 16) against the FULL and the kept boundary
-  int wave_nat[W];      // natural count (keys below K(tau))
-  int wave_base[W + 1][4];  // FULL rank base, APPROX rank base, ties before (FULL, kept);
-                            // row W holds the totals
-  int totals[2];        // n_full, n_kept
-  int R[2];
-  int sel_b[2], sel_above[2];
-  Select sel[2];
 };
 
 // Channel layout: wave w owns channels [j0, j0 + n), j0 = w*C; at step s, lane l handles
@@ -127,239 +107,11 @@ struct Plan {
   int n_full, n_kept;
 };
 
-// Stage 1: load x into LDS (xs32: roundup(d, 2) halves), pass 1 and level 1.  Afterwards
-// sh.sel holds the exact boundaries for THRESHOLD; otherwise sh.R holds the rank targets and
-// sh.sel_b / sh.sel_above the level-1 buckets (-1: R == 0).  Ends with a barrier.  d <= MAXD.
-template <int NT, int MAXD>
-__device__ __forceinline__ void plan_stage1(Shared<NT>& sh, Keys& k, uint32_t* xs32,
-                                            const uint16_t* __restrict__ x, const TierArgs& a) {
-  constexpr int W = NT / 64;
-  using S = Shared<NT>;
-  static_assert(MAXD <= 32768 && NT >= 256, "per-wave counts are packed in 16 bits");
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int d = a.d;
-  k.xs32 = xs32;
-  k.C = ((d + W - 1) / W + 127) / 128 * 128;
-  k.j0 = min(wave * k.C, d);
-  k.n = min(k.j0 + k.C, d) - k.j0;
-  k.steps = (k.n + 127) / 128;
-  const bool thresholds = a.mode == SPAX_MODE_THRESHOLD;
-
-  // ---- x into LDS, four loads in flight per thread and iteration.  For odd d the last
-  // dword also holds the two bytes past x (same dword, never used as a channel).
-  {
-    const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
-    const int ndw = (d + 1) >> 1;
-    for (int i = tid; i < ndw; i += 4 * NT) {
-      uint32_t v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = i + q * NT < ndw ? x32[i + q * NT] : 0u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (i + q * NT < ndw) xs32[i + q * NT] = v[q];
-    }
-    // Every load has landed: say so to the compiler's wait tracking, so that loads issued
-    // after the mask passes are not made to wait for these conditional ones.
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  if (!thresholds) {
-    const int4 z = make_int4(0, 0, 0, 0);
-    int4* hr = reinterpret_cast<int4*>(sh.hist_rep);
-    for (int i = tid; i < S::kRep / 4; i += NT) hr[i] = z;
-    int4* wh = reinterpret_cast<int4*>(&sh.wave_hist[0][0][0]);
-    for (int i = tid; i < 2 * W * 128 / 4; i += NT) wh[i] = z;
-  }
-  __syncthreads();
-
-  // ---- pass 1: high-bit histogram and natural count, or the threshold counts
-  if (thresholds) {
-    int c0 = 0, c1 = 0;  // gt | eq << 16
-    for (int s = 0; s < k.steps; ++s) {
-      const uint32_t wd = k.word(s, lane);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int key = k.valid(s, lane, e) ? (int)((e ? wd >> 16 : wd) & 0x7FFFu) : -1;
-        c0 += key > a.k_full ? 1 : key == a.k_full ? 0x10000 : 0;
-        c1 += key > a.k_skip ? 1 : key == a.k_skip ? 0x10000 : 0;
-      }
-    }
-    c0 = wave_sum(c0);
-    c1 = wave_sum(c1);
-    if (lane == 0) {
-      sh.wave_cnt[wave][0] = c0;
-      sh.wave_cnt[wave][1] = c1;
-    }
-    if (tid == 0) {
-      sh.sel[0] = Select{a.k_full, d};
-      sh.sel[1] = Select{a.k_skip, d};
-    }
-  } else {
-    int nat = 0;
-    for (int s = 0; s < k.steps; ++s) {
-      const uint32_t wd = k.word(s, lane);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const bool valid = k.valid(s, lane, e);
-        const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
-        // unconditional (zero past the range): see select_begin
-        atomicAdd(&sh.hist_rep[(lane & (S::kCopies - 1)) * S::kStride + (key >> 7)], valid ? 1 : 0);
-        nat += valid && key < a.k_tau;
-      }
-    }
-    nat = wave_sum(nat);
-    if (lane == 0) sh.wave_nat[wave] = nat;
-  }
-  __syncthreads();
-
-  if (!thresholds) {
-    // ---- rank targets (wave 0) and the folded level-1 histogram (threads < 256)
-    if (wave == 0) {
-      int R0, R1;
-      if (a.mode == SPAX_MODE_TOPK) {
-        R0 = a.n_full;
-        R1 = a.n_full + a.n_approx;
-      } else {
-        const int natural = wave_sum(lane < W ? sh.wave_nat[lane] : 0);
-        const int n_skip = min(max(natural, a.n_lo), a.n_hi);
-        const int kept = d - n_skip;
-        // num <= den <= 65535 and kept <= 32768: fits 32 bits
-        const int n_approx = (int)(((uint32_t)a.num * (uint32_t)kept + (uint32_t)(a.den / 2)) /
-                                   (uint32_t)a.den);
-        R0 = kept - n_approx;
-        R1 = kept;
-      }
-      if (lane == 0) {
-        sh.R[0] = R0;
-        sh.R[1] = R1;
-      }
-    }
-    for (int b = tid; b < 256; b += NT) {
-      int t = 0;
-#pragma unroll
-      for (int c = 0; c < S::kCopies; ++c) t += sh.hist_rep[c * S::kStride + b];
-      sh.hist_hi[b] = t;
-    }
-    __syncthreads();
-    const int R[2] = {sh.R[0], sh.R[1]};
-    // ---- level 1: bucket of each boundary (waves 0 and 1)
-    if (wave < 2) {
-      int local[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) local[i] = sh.hist_hi[lane * 4 + i];
-      int b = -1, ab = 0;
-      if (R[wave] > 0) suffix_find<4>(local, R[wave], 0, lane, &b, &ab);
-      if (lane == 0) {
-        sh.sel_b[wave] = R[wave] > 0 ? b : -1;
-        sh.sel_above[wave] = ab;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// Stage 2: pass 2 and level 2 (TopK boundaries), then every wave's rank bases
-// (sh.wave_base).  Returns the plan on every thread; ends with a barrier.
-template <int NT>
-__device__ __forceinline__ Plan plan_stage2(Shared<NT>& sh, const Keys& k, const TierArgs& a) {
-  constexpr int W = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (a.mode != SPAX_MODE_THRESHOLD) {
-    const int R[2] = {sh.R[0], sh.R[1]};
-    const int b0 = sh.sel_b[0], b1 = sh.sel_b[1];
-    // ---- pass 2: per-wave low-bit histograms inside the buckets; keys above the buckets
-    // (above0 | above1 << 16)
-    int above = 0;
-    for (int s = 0; s < k.steps; ++s) {
-      const uint32_t wd = k.word(s, lane);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const bool valid = k.valid(s, lane, e);
-        const int key = (int)((e ? wd >> 16 : wd) & 0x7FFFu);
-        const int hi = valid ? key >> 7 : -2;
-        atomicAdd(&sh.wave_hist[0][wave][key & 127], hi == b0 ? 1 : 0);  // see select_begin
-        atomicAdd(&sh.wave_hist[1][wave][key & 127], hi == b1 ? 1 : 0);
-        above += (b0 >= 0 && hi > b0 ? 1 : 0) + (b1 >= 0 && hi > b1 ? 0x10000 : 0);
-      }
-    }
-    above = wave_sum(above);
-    __syncthreads();
-    // ---- level 2: exact boundary keys (waves 0 and 1 sum the per-wave histograms)
-    if (wave < 2) {
-      int local[2] = {0, 0};
-      for (int w = 0; w < W; ++w) {
-        const int2 h = *reinterpret_cast<const int2*>(&sh.wave_hist[wave][w][lane * 2]);
-        local[0] += h.x;
-        local[1] += h.y;
-      }
-      int v = -1, ab = 0;
-      if (R[wave] > 0) suffix_find<2>(local, R[wave], sh.sel_above[wave], lane, &v, &ab);
-      if (lane == 0)
-        sh.sel[wave] =
-            R[wave] > 0 ? Select{(sh.sel_b[wave] << 7) | v, R[wave] - ab} : Select{0x8000, 0};
-    }
-    __syncthreads();
-    // ---- this wave's (gt | eq << 16) against the boundaries, from its own histograms
-    const int low0 = sh.sel[0].kb & 127, low1 = sh.sel[1].kb & 127;
-    const int2 h0 = *reinterpret_cast<const int2*>(&sh.wave_hist[0][wave][lane * 2]);
-    const int2 h1 = *reinterpret_cast<const int2*>(&sh.wave_hist[1][wave][lane * 2]);
-    auto ge = [&](int bin, int c, int low) { return bin > low ? c : bin == low ? c << 16 : 0; };
-    const int c0 = wave_sum(ge(lane * 2, h0.x, low0) + ge(lane * 2 + 1, h0.y, low0));
-    const int c1 = wave_sum(ge(lane * 2, h1.x, low1) + ge(lane * 2 + 1, h1.y, low1));
-    if (lane == 0) {
-      // R == 0: boundary above every key, nothing greater or equal
-      sh.wave_cnt[wave][0] = R[0] > 0 ? c0 + (above & 0xFFFF) : 0;
-      sh.wave_cnt[wave][1] = R[1] > 0 ? c1 + (above >> 16) : 0;
-    }
-    __syncthreads();
-  }
-
-  // ---- rank bases of every wave (wave 0, lane w <-> wave w).  Ties are taken in index
-  // order, so a wave's selected ties are clamp(m - ties before it, 0, its ties).
-  Plan p;
-  p.s0 = sh.sel[0];
-  p.s1 = sh.sel[1];
-  if (wave == 0) {
-    const bool on = lane < W;
-    const int w0 = on ? sh.wave_cnt[lane][0] : 0, w1 = on ? sh.wave_cnt[lane][1] : 0;  // lane W: 0
-    const int g0 = w0 & 0xFFFF, e0 = w0 >> 16, g1 = w1 & 0xFFFF, e1 = w1 >> 16;
-    const int eb0 = wave_scan(e0) - e0, eb1 = wave_scan(e1) - e1;  // up to 32768 each
-    const int f = g0 + min(max(p.s0.m - eb0, 0), e0);
-    const int kk = g1 + min(max(p.s1.m - eb1, 0), e1);
-    const int fs = wave_scan(f), ks = wave_scan(kk);
-    if (lane <= W) {
-      sh.wave_base[lane][0] = fs - f;
-      sh.wave_base[lane][1] = (ks - kk) - (fs - f);  // FULL is a subset of kept
-      sh.wave_base[lane][2] = eb0;
-      sh.wave_base[lane][3] = eb1;
-    }
-    if (lane == 0) {
-      sh.totals[0] = __builtin_amdgcn_readlane(fs, 63);
-      sh.totals[1] = __builtin_amdgcn_readlane(ks, 63);
-    }
-  }
-  __syncthreads();
-  p.n_full = sh.totals[0];
-  p.n_kept = sh.totals[1];
-  return p;
-}
-
-// Both stages: boundaries, totals and rank bases.
-template <int NT, int MAXD>
-__device__ __forceinline__ Plan build_plan(Shared<NT>& sh, Keys& k, uint32_t* xs32,
-                                           const uint16_t* __restrict__ x, const TierArgs& a) {
-  plan_stage1<NT, MAXD>(sh, k, xs32, x, a);
-  return plan_stage2<NT>(sh, k, a);
-}
-
-// Exact selection from a per-key histogram (used by the fused decode kernel, which needs the
-// boundaries but no ranks): one pass of LDS atomics into 32768 16-bit counters (two keys per
-// dword; a count never exceeds 32768, so it cannot carry into its neighbour), 1024 partial
-// sums of 32 keys each, then one wave finds each boundary with two suffix scans (partial
-// sums, then the 32 keys of the chosen partial sum).  Compared with the two-level radix
-// select above there is no second pass over the keys, and far fewer lanes collide in one
-// counter (equal keys only).
+// Exact selection from a per-key histogram: one pass of LDS atomics into 32768 16-bit
+// counters (two keys per dword; a count never exceeds 32768, so it cannot carry into its
+// neighbour) and 1024 partial sums of 32 keys each, then one wave finds each boundary with
+// two suffix scans (partial sums, then the 32 keys of the chosen partial sum).  Lanes
+// collide in a fine counter only on equal keys.
 template <int NT>
 struct KeyHist {
   static constexpr int W = NT / 64;
@@ -370,13 +122,15 @@ struct KeyHist {
   // the next unclaimed FULL / APPROX entry ([0], [1]) and the published list lengths ([2],
   // [3]); zeroed by select_begin before its first barrier.
   int lists_q[4][W];
+  // For tiers_to_global: per wave, (keys above | keys equal) << 16 for each boundary.
+  int wave_cnt[W][2];
   Select sel[2];
   int E[2];
 };
 
 // Exact boundaries from a per-key histogram, in two parts (a caller may do other work in
-// between).  select_begin loads x into LDS (xs32: roundup(d, 2) halves), sets k like
-// build_plan, builds the per-key histogram and the coarse one (32 keys per bin), and gives
+// between).  select_begin loads x into LDS (xs32: roundup(d, 2) halves), sets k (the wave's
+// channel range), builds the per-key histogram and the coarse one (32 keys per bin), and gives
 // every wave the two target ranks R (FULL, kept; counted from the largest key).  For
 // THRESHOLD the boundaries are the given keys: sel and E are set and false is returned.
 // Both histograms are complete on return (its last barrier follows the last atomic).
@@ -413,7 +167,9 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
 #pragma unroll
     for (int q = 0; q < PER; ++q)
       if (tid + q * NT < ndw) xs32[tid + q * NT] = v[q];
-    __builtin_amdgcn_s_waitcnt(0);  // see plan_stage1
+    // Every load has landed: say so to the compiler's wait tracking, so that loads issued
+    // after the mask passes are not made to wait for these conditional ones.
+    __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
   if (thresholds) {
@@ -514,22 +270,25 @@ __device__ __forceinline__ void select_finish(KeyHist<NT>& h, const int (&R)[2],
   E[1] = h.E[1];
 }
 
+// A wave's first FULL and APPROX list positions, the ties at each boundary key before its
+// first channel, and the end of its FULL and APPROX positions.
+struct WaveBases {
+  int fpos, apos, eqb0, eqb1, f_end, a_end;
+};
+
 // Pass 3: FULL / APPROX channels go to emit_list(tier, rank, j, raw) with their rank in the
 // ascending list; emit_tier(j, t_even, t_odd, n) sees each lane's pair of channels (j even,
 // n = 2, or 1 when j + 1 is past the wave's range).  Only ranks in [f_lo, f_hi) (FULL) and
 // [a_lo, a_hi) (APPROX) are wanted.  Unless every channel must reach emit_tier
 // (all_channels), a wave whose rank ranges miss both windows does nothing, and a wave stops
-// once it is past both (ranks grow with the channel index).  Uses build_plan's bases; no
-// barrier.
-template <int NT, class EmitList, class EmitTier>
-__device__ __forceinline__ void emit(const Shared<NT>& sh, const Keys& k, const Plan& p,
+// once it is past both (ranks grow with the channel index).  No barrier.
+template <class EmitList, class EmitTier>
+__device__ __forceinline__ void emit(const WaveBases& b, const Keys& k, const Plan& p,
                                      bool all_channels, int f_lo, int f_hi, int a_lo, int a_hi,
                                      EmitList emit_list, EmitTier emit_tier) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int fpos = sh.wave_base[wave][0], apos = sh.wave_base[wave][1];
-  int eqb0 = sh.wave_base[wave][2], eqb1 = sh.wave_base[wave][3];
-  const int f_end = sh.wave_base[wave + 1][0], a_end = sh.wave_base[wave + 1][1];
+  int fpos = b.fpos, apos = b.apos, eqb0 = b.eqb0, eqb1 = b.eqb1;
+  const int f_end = b.f_end, a_end = b.a_end;
   const bool wantF = fpos < f_hi && f_end > f_lo && f_lo < f_hi;
   const bool wantA = apos < a_hi && a_end > a_lo && a_lo < a_hi;
   if (!all_channels && !wantF && !wantA) return;
@@ -586,27 +345,77 @@ __device__ __forceinline__ void emit(const Shared<NT>& sh, const Keys& k, const 
 // A whole mask in one workgroup with its outputs in global memory: tier bytes (tier may be
 // NULL), both ascending lists and the counts {n_full, n_approx, n_skip}.  Used by the
 // stand-alone mask kernel, the writer workgroup of the fused decode kernel and the batched
-// mask launch.  d <= MAXD.
+// mask launch.  d <= MAXD.  The boundaries come from the per-key histogram (select_begin /
+// select_finish); one counting pass gives every wave its keys above and equal to each
+// boundary, one barrier publishes them, and every wave derives its list and tie bases with
+// two scans over the waves before emit writes the lists.
 template <int NT, int MAXD>
-__device__ __forceinline__ void tiers_to_global(Shared<NT>& sh, uint32_t* xs32, const TierArgs& a,
+__device__ __forceinline__ void tiers_to_global(KeyHist<NT>& h, uint32_t* xs32, const TierArgs& a,
                                                 const uint16_t* __restrict__ x, uint8_t* tier,
                                                 int32_t* full_idx, int32_t* approx_idx,
                                                 int32_t* counts) {
+  constexpr int W = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Keys k;
-  const Plan p = build_plan<NT, MAXD>(sh, k, xs32, x, a);
+  int R[2], E[2];
+  Select sel[2];
+  if (select_begin<NT, MAXD>(h, k, xs32, x, a, R, sel, E)) select_finish<NT>(h, R, sel, E);
+  const Select s0 = sel[0], s1 = sel[1];
+  // counts of this wave's channels: (above | equal << 16) per boundary (a wave holds at most
+  // 32768 / W channels, so each half fits 16 bits)
+  uint32_t c0 = 0, c1 = 0;
+  for (int s = 0; s < k.steps; ++s) {
+    const uint32_t wd = k.word(s, lane);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = k.valid(s, lane, e) ? (int)((e ? wd >> 16 : wd) & 0x7FFFu) : -1;
+      c0 += (key > s0.kb ? 1u : 0u) + (key == s0.kb ? 0x10000u : 0u);
+      c1 += (key > s1.kb ? 1u : 0u) + (key == s1.kb ? 0x10000u : 0u);
+    }
+  }
+  c0 = (uint32_t)wave_sum((int)c0);
+  c1 = (uint32_t)wave_sum((int)c1);
+  if (lane == 0) {
+    h.wave_cnt[wave][0] = (int)c0;
+    h.wave_cnt[wave][1] = (int)c1;
+  }
+  __syncthreads();
+  // lane u < W holds wave u's counts; exclusive scans over the waves give the ties before
+  // wave u, its FULL and kept counts, then its first list positions
+  const uint32_t w0 = lane < W ? (uint32_t)h.wave_cnt[lane][0] : 0u;
+  const uint32_t w1 = lane < W ? (uint32_t)h.wave_cnt[lane][1] : 0u;
+  const int g0 = (int)(w0 & 0xFFFFu), e0 = (int)(w0 >> 16);
+  const int g1 = (int)(w1 & 0xFFFFu), e1 = (int)(w1 >> 16);
+  const int t0 = wave_scan(e0) - e0, t1 = wave_scan(e1) - e1;  // ties before wave u
+  const int nf = g0 + min(max(s0.m - t0, 0), e0);
+  const int nk = g1 + min(max(s1.m - t1, 0), e1);
+  const int fb = wave_scan(nf) - nf, ab = wave_scan(nk - nf) - (nk - nf);
+  WaveBases b;
+  b.fpos = __builtin_amdgcn_readlane(fb, wave);
+  b.apos = __builtin_amdgcn_readlane(ab, wave);
+  b.eqb0 = __builtin_amdgcn_readlane(t0, wave);
+  b.eqb1 = __builtin_amdgcn_readlane(t1, wave);
+  b.f_end = b.fpos + __builtin_amdgcn_readlane(nf, wave);
+  b.a_end = b.apos + __builtin_amdgcn_readlane(nk - nf, wave);
+  Plan p;
+  p.s0 = s0;
+  p.s1 = s1;
+  p.n_full = __builtin_amdgcn_readlane(fb + nf, W - 1);
+  p.n_kept = p.n_full + __builtin_amdgcn_readlane(ab + nk - nf, W - 1);
   const bool tier_even = ((uintptr_t)tier & 1) == 0;  // channel pairs start at even j
-  emit<NT>(
-      sh, k, p, true, 0, INT_MAX, 0, INT_MAX,
+  emit(
+      b, k, p, true, 0, INT_MAX, 0, INT_MAX,
       [&](int t, int rank, int j, uint32_t) {
         if (t == SPAX_TIER_FULL) full_idx[rank] = j;
         else approx_idx[rank] = j;
       },
-      [&](int j, uint32_t t0, uint32_t t1, int n) {
+      [&](int j, uint32_t t0_, uint32_t t1_, int n) {
         if (!tier) return;
-        if (n == 2 && tier_even) *reinterpret_cast<uint16_t*>(tier + j) = (uint16_t)(t0 | t1 << 8);
+        if (n == 2 && tier_even) *reinterpret_cast<uint16_t*>(tier + j) = (uint16_t)(t0_ | t1_ << 8);
         else {
-          tier[j] = (uint8_t)t0;
-          if (n == 2) tier[j + 1] = (uint8_t)t1;
+          tier[j] = (uint8_t)t0_;
+          if (n == 2) tier[j + 1] = (uint8_t)t1_;
         }
       });
   if (threadIdx.x == 0) {

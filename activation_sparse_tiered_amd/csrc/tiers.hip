@@ -19,7 +19,7 @@ __global__ __launch_bounds__(NT) void build_tiers_kernel(
     TierArgs a, const uint16_t* __restrict__ x, uint8_t* __restrict__ tier,
     int32_t* __restrict__ full_idx, int32_t* __restrict__ approx_idx,
     int32_t* __restrict__ counts, float4* __restrict__ y_zero, int32_t n_zero4) {
-  __shared__ mask::Shared<NT> sh;
+  __shared__ mask::KeyHist<NT> sh;
   __shared__ uint32_t xs32[SPAX_MAX_DIN / 2];
   mask::tiers_to_global<NT, SPAX_MAX_DIN>(sh, xs32, a, x, tier, full_idx, approx_idx, counts);
   // Side job: clear the fp32 output the following GEMV accumulates into.  Issued last, so
