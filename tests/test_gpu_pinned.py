@@ -192,3 +192,48 @@ def test_pinned_gather_malformed_lists_stay_inside(env):
         y, st = run_pinned(env, L, host, b, gap, transfer=1)
         assert np.isfinite(y).all()
         assert 0 <= st.moved_bytes <= d_in * (L.stride_F + L.stride_A)
+
+
+def test_pinned_calls_from_several_host_threads(env):
+    """Four host threads, each with its own stream, workspace and output, call the pinned path
+    at once on one shared blob in all three transfers (the host-merged transfers share the
+    library's per-device pinned scratch and the host-gather thread pool): every call gives the
+    single-threaded result, and the byte accounts agree."""
+    import threading
+    torch, spax, dev = env
+    d_in, d_out = 4096, [2048, 1024]
+    nF, nA = spax.spax_counts_from_fractions(d_in, 0.2, 0.3)
+    L, O, Ws, x16, packed, host, b = setup(env, d_in, d_out, 0, 128, 77, nF, nA)
+    want = {t: run_pinned(env, L, host, b, 2, t) for t in (0, 1, 2)}
+    _, wf, wa, _ = otiers.build_tiers(x16, otiers.MODE_TOPK, n_full=nF, n_approx=nA)
+    for t, (y, _) in want.items():
+        check_y_oracle(y, O, Ws, x16, wf, wa, f"single-threaded transfer {t}")
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream(device=dev)
+            y = torch.empty(int(L.d_out_total), dtype=torch.float32, device=dev)
+            ws = torch.empty(spax.spax_pinned_workspace_bytes(L), dtype=torch.uint8, device=dev)
+            for rep in range(6):
+                t = (k + rep) % 3
+                y.fill_(float("nan"))
+                s.wait_stream(torch.cuda.current_stream(dev))
+                st = spax.spax_tiered_gemv_pinned(L, host, b["x"], b["f"], b["a"], b["c"], y, 2,
+                                                  ws, transfer=t, stream=s)
+                s.synchronize()
+                got = y.cpu().numpy()
+                if rel_l2(got, want[t][0]) > 1e-6 or not np.all(np.isfinite(got)):
+                    errors.append((k, rep, t, "y"))
+                if st.moved_bytes != want[t][1].moved_bytes or st.n_ranges != want[t][1].n_ranges:
+                    errors.append((k, rep, t, "account"))
+        except Exception as e:  # reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads), "a host thread did not finish"
+    assert not errors, errors
