@@ -379,3 +379,82 @@ def test_step_next_y_reuses_previous_phase_buffer(env, flags, what):
         if not (i == 0 and what == "a"):
             assert np.array_equal(b["a"].cpu().numpy()[:wc[1]], wa), i
         check_y_oracle(b["y"].cpu().numpy(), O, Ws, x16, wf, wa, f"phase {i} over {what}")
+
+
+def test_step_from_several_host_threads(env):
+    """Four host threads, each with its own stream and its own copy of every output buffer and
+    workspace, enqueue decode steps at once in the default, batched and deterministic forms
+    (the batched form stages its descriptor tables through the library's pinned ring, shared
+    by all callers on a device): every call gives the single-threaded masks bit for bit and
+    the same form's single-threaded y within the atomics' reordering (the deterministic form
+    bit for bit)."""
+    import threading
+    torch, spax, dev = env
+    specs = [(4096, [1024, 512, 512], 0, 128, ("guided", 0.5, 0.01)),
+             (2048, [2048], 1, 128, ("topk", 0.25, 0.35)),
+             (3000, [1024], 0, 64, ("threshold", 0.6, 1.4))]
+    keep = run_step(env, specs, 4242, flags=0)
+    check(keep)
+    want = [dict((k, b[k].cpu().numpy().copy()) for k in ("tier", "f", "a", "c"))
+            for *_, b in keep]
+    # each form's own single-threaded y (the forms sum in different orders)
+    arr0 = spax.phase_array([spax.make_phase(L, packed, b["x"], _params(spax, oa), b["tier"],
+                                             b["f"], b["a"], b["c"], b["y"])
+                             for (L, O, Ws, x16, oa, packed, b) in keep])
+    ws0 = torch.zeros(spax.spax_step_workspace_bytes(arr0), dtype=torch.uint8, device=dev)
+    forms = (0, spax.STEP_BATCHED, spax.STEP_DETERMINISTIC)
+    want_y = {}
+    for flags in forms:
+        spax.spax_decode_step_projections(arr0, ws0, flags=flags)
+        torch.cuda.synchronize()
+        want_y[flags] = [b["y"].cpu().numpy().copy() for *_, b in keep]
+        for (L, O, Ws, x16, oa, packed, b), yv in zip(keep, want_y[flags]):
+            args = dict(oa)
+            mode = args.pop("mode")
+            _, wf, wa, _ = otiers.build_tiers(x16, mode, **args)
+            check_y_oracle(yv, O, Ws, x16, wf, wa, f"single-threaded flags {flags}")
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream(device=dev)
+            bufs, phases = [], []
+            for (L, O, Ws, x16, oa, packed, b) in keep:
+                nb = dict(tier=torch.empty_like(b["tier"]), f=torch.empty_like(b["f"]),
+                          a=torch.empty_like(b["a"]), c=torch.empty_like(b["c"]),
+                          y=torch.empty_like(b["y"]))
+                bufs.append(nb)
+                phases.append(spax.make_phase(L, packed, b["x"], _params(spax, oa), nb["tier"],
+                                              nb["f"], nb["a"], nb["c"], nb["y"]))
+            arr = spax.phase_array(phases)
+            ws = torch.zeros(spax.spax_step_workspace_bytes(arr), dtype=torch.uint8, device=dev)
+            s.wait_stream(torch.cuda.current_stream(dev))
+            for rep in range(6):
+                flags = forms[(k + rep) % 3]
+                spax.spax_decode_step_projections(arr, ws, flags=flags, stream=s)
+                s.synchronize()
+                for i, (nb, w) in enumerate(zip(bufs, want)):
+                    c = w["c"]
+                    if not (np.array_equal(nb["c"].cpu().numpy(), c)
+                            and np.array_equal(nb["tier"].cpu().numpy(), w["tier"])
+                            and np.array_equal(nb["f"].cpu().numpy()[:c[0]], w["f"][:c[0]])
+                            and np.array_equal(nb["a"].cpu().numpy()[:c[1]], w["a"][:c[1]])):
+                        errors.append((k, rep, flags, i, "mask"))
+                    y = nb["y"].cpu().numpy()
+                    ref = want_y[flags][i]
+                    if flags == spax.STEP_DETERMINISTIC:
+                        ok = np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+                    else:
+                        ok = np.all(np.isfinite(y)) and rel_l2(y, ref) <= 1e-6
+                    if not ok:
+                        errors.append((k, rep, flags, i, "y", float(rel_l2(y, ref))))
+        except Exception as e:  # reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads), "a host thread did not finish"
+    assert not errors, errors
