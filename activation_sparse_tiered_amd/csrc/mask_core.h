@@ -107,11 +107,12 @@ struct Plan {
   int n_full, n_kept;
 };
 
-// Exact selection from a per-key histogram: one pass of LDS atomics into 32768 16-bit
-// counters (two keys per dword; a count never exceeds 32768, so it cannot carry into its
-// neighbour) and 1024 partial sums of 32 keys each, then one wave finds each boundary with
-// two suffix scans (partial sums, then the 32 keys of the chosen partial sum).  Lanes
-// collide in a fine counter only on equal keys.
+// Exact selection: a radix select over the 15-bit keys with two digits (the high 10 bits,
+// then the low 5), both digit histograms built in one pass of LDS atomics: 1024 counters of
+// the high digit and 32768 16-bit per-key counters (two keys per dword; a count never exceeds
+// 32768, so it cannot carry into its neighbour), the low-digit histogram of a high digit
+// being its 32 key counters.  Then one wave finds each boundary with two suffix scans (high
+// digit, then low digit).  Lanes collide in a per-key counter only on equal keys.
 template <int NT>
 struct KeyHist {
   static constexpr int W = NT / 64;
