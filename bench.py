@@ -42,6 +42,8 @@ when every launch only reads its selected byte count (a floor for the layer-seri
 For linear512 and mlp7b ``cpu_baseline`` also holds a one-thread run of the oracle.
 ``dense_baseline`` (fp16 workloads) times the same step without tiers through torch's fp16
 matrix-vector product on the same weights, as context for the speedup over dense decoding.
+``--fit`` (decode7b) adds ``fixed_cost_fit``: the layer-serial step at s = 0.3, 0.5 and 0.7 and
+the line t = a + b * MB per fused launch through them.
 """
 
 from __future__ import annotations
@@ -87,6 +89,9 @@ def parse():
                     help="skip timing the batched step form")
     ap.add_argument("--no-separate", action="store_true",
                     help="skip timing the two-launch step form")
+    ap.add_argument("--fit", action="store_true",
+                    help="decode7b: also time the layer-serial step at s = 0.3, 0.5 and 0.7 and "
+                         "fit the per-launch time against the bytes per launch")
     ap.add_argument("--no-deterministic", action="store_true",
                     help="skip timing the SPAX_STEP_DETERMINISTIC form")
     ap.add_argument("--no-read-probe", action="store_true",
@@ -475,6 +480,59 @@ def dense_baseline(stack, reps=10):
                     "dense weights in HBM, same shapes and weights, phases in order"}
 
 
+def layer_serial_point(spax, torch, dev, spec, args):
+    """One layer-serial measurement of a workload: (µs per launch, algorithmic MB per launch)
+    over `args.steps` timed steps after `args.warmup`, bytes from the device counts of the
+    timed tokens."""
+    stack = Stack(spax, torch, dev, spec["layers"], args.tokens, spec=spec)
+    for t in range(args.warmup):
+        stack.step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(args.steps):
+        stack.step(args.warmup + t)
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.steps
+    tok_bytes = {}
+    for t in range(args.warmup, args.warmup + args.steps):
+        key = t % stack.tokens
+        if key not in tok_bytes:
+            _, counts = stack.timed_kernels(t)
+            tok_bytes[key] = sum(stack.algorithmic_bytes(i, c) for i, c in enumerate(counts))
+    n = len(stack.layouts)
+    step_bytes = float(np.mean([tok_bytes[t % stack.tokens]
+                                for t in range(args.warmup, args.warmup + args.steps)]))
+    del stack
+    torch.cuda.empty_cache()
+    return step_ms * 1e3 / n, step_bytes / n / 1e6
+
+
+def fixed_cost_fit(spax, torch, dev, args, main_point):
+    """The layer-serial decode7b step at s = 0.3, 0.5 and 0.7 (the timed run's point reused
+    for its own s) and the least-squares line t = a + b * MB per launch."""
+    points = []
+    for s in (0.3, 0.5, 0.7):
+        if abs(s - args.sparsity) < 1e-9:
+            points.append((s,) + main_point)
+            continue
+        a2 = argparse.Namespace(**vars(args))
+        a2.sparsity = s
+        us, mb = layer_serial_point(spax, torch, dev, workload_spec(a2), args)
+        log(f"[bench] fit point s={s}: {us:.3f} us, {mb:.3f} MB per launch")
+        points.append((s, us, mb))
+    mbs = np.array([p[2] for p in points])
+    uss = np.array([p[1] for p in points])
+    b, a = np.polyfit(mbs, uss, 1)
+    return {"points": [{"s": p[0], "us_per_launch": round(p[1], 3), "MB_per_launch": round(p[2], 3)}
+                       for p in points],
+            "intercept_us": round(float(a), 3), "slope_us_per_MB": round(float(b), 5),
+            "marginal_TBps": round(1.0 / float(b), 3) if b > 0 else None,  # MB/us = TB/s
+            "what": "layer-serial fused launches: t = intercept + slope x algorithmic MB per "
+                    "launch over the three skip targets"}
+
+
 def device_bench(args, spax, torch, dev):
     spec = workload_spec(args)
     per_tok = spec["tokens_per_step"]
@@ -622,6 +680,11 @@ def device_bench(args, spax, torch, dev):
         log(f"[bench] read probe {probe}")
 
     cpu = None
+    fit = None
+    if args.fit and args.workload == "decode7b" and args.control == "none":
+        fit = fixed_cost_fit(spax, torch, dev, args, (avg_launch_ms * 1e3, avg_bytes / 1e6))
+        log(f"[bench] fixed-cost fit {fit}")
+
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(stack, spec["cpu_layers"])
         if args.workload in ("linear512", "mlp7b"):
@@ -669,6 +732,7 @@ def device_bench(args, spax, torch, dev):
         "read_probe": probe,
         "dense_baseline": dense,
         "storage_4KiB": storage,
+        "fixed_cost_fit": fit,
     }
 
 
