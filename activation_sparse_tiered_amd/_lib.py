@@ -15,9 +15,9 @@ LIB_PATH = os.path.join(_HERE, "libspax.so")
 SPAX_OK = 0
 STATUS_NAMES = {0: "SPAX_OK", -1: "SPAX_ERR_NULL", -2: "SPAX_ERR_SHAPE", -3: "SPAX_ERR_PARAM",
                 -4: "SPAX_ERR_ALIGN", -5: "SPAX_ERR_WORKSPACE", -6: "SPAX_ERR_HIP",
-                -7: "SPAX_ERR_UNSUPPORTED"}
+                -7: "SPAX_ERR_UNSUPPORTED", -8: "SPAX_ERR_HOST"}
 SPAX_ERR_NULL, SPAX_ERR_SHAPE, SPAX_ERR_PARAM, SPAX_ERR_ALIGN = -1, -2, -3, -4
-SPAX_ERR_WORKSPACE, SPAX_ERR_HIP, SPAX_ERR_UNSUPPORTED = -5, -6, -7
+SPAX_ERR_WORKSPACE, SPAX_ERR_HIP, SPAX_ERR_UNSUPPORTED, SPAX_ERR_HOST = -5, -6, -7, -8
 
 FMT_FP16, FMT_INT4 = 0, 1
 MODE_TOPK, MODE_THRESHOLD, MODE_TOPK_GUIDED = 0, 1, 2

@@ -1,6 +1,7 @@
 // Entry points of libspax: argument validation, then kernel launches.
 // Every check runs before anything is enqueued; on error no output is touched.
 #include <algorithm>
+#include <mutex>
 #include <vector>
 #include <cstdio>
 #include <cstring>
@@ -31,18 +32,20 @@ int check_tier_outputs(const uint16_t* x, int32_t d_in, const int32_t* full_idx,
 
 // SPAX_STEP_BATCHED runs all phases at once: no output may overlap another output or any
 // input x.
-int check_independent(const spax_step* st) {
-  struct Range {
-    uintptr_t b, e;
-    int phase;
-    bool out;
-  };
-  std::vector<Range> r;
+struct Range {
+  uintptr_t b, e;
+  int phase;
+  bool out;
+};
+constexpr int kRangesPerPhase = 7;
+// The check over a caller-provided buffer of kRangesPerPhase ranges per phase.
+int check_independent_in(const spax_step* st, Range* buf) {
+  Range* end = buf;
   for (int i = 0; i < st->n_phases; ++i) {
     const spax_phase& ph = st->phases[i];
     const spax_layout* L = ph.layout;
     const auto add = [&](const void* p, size_t n, bool out) {
-      if (p && n) r.push_back(Range{(uintptr_t)p, (uintptr_t)p + n, i, out});
+      if (p && n) *end++ = Range{(uintptr_t)p, (uintptr_t)p + n, i, out};
     };
     add(ph.x, 2 * (size_t)L->d_in, false);
     add(ph.packed, (size_t)L->total_bytes, false);
@@ -52,17 +55,36 @@ int check_independent(const spax_step* st) {
     add(ph.counts, 12, true);
     add(ph.y, 4 * (size_t)L->d_out_total, true);
   }
-  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.b < b.b; });
+  std::sort(buf, end, [](const Range& a, const Range& b) { return a.b < b.b; });
   // any overlap involving an output is an error (two inputs may share memory)
   uintptr_t end_out = 0, end_any = 0;
   int ph_out = -1, ph_any = -1;
-  for (const Range& x : r) {
+  for (const Range* px = buf; px != end; ++px) {
+    const Range& x = *px;
     if (x.b < end_out) return fail(SPAX_ERR_PARAM, "batched step: phase %d overlaps an output of phase %d", x.phase, ph_out);
     if (x.out && x.b < end_any) return fail(SPAX_ERR_PARAM, "batched step: an output of phase %d overlaps phase %d", x.phase, ph_any);
     if (x.out && x.e > end_out) { end_out = x.e; ph_out = x.phase; }
     if (x.e > end_any) { end_any = x.e; ph_any = x.phase; }
   }
   return SPAX_OK;
+}
+
+// noalloc: the ranges go to a static buffer (the no-alloc step holds at most
+// kNoallocMaxPhases phases: its descriptor tables must fit the static device scratch), taken
+// under a lock, so the check allocates nothing.
+constexpr int kNoallocMaxPhases = 2048;
+int check_independent(const spax_step* st, bool noalloc) {
+  if (noalloc) {
+    if (st->n_phases > kNoallocMaxPhases)
+      return fail(SPAX_ERR_WORKSPACE, "%d phases: the no-alloc step takes at most %d",
+                  st->n_phases, kNoallocMaxPhases);
+    static std::mutex mu;
+    static Range buf[kRangesPerPhase * kNoallocMaxPhases];
+    std::lock_guard<std::mutex> lock(mu);
+    return check_independent_in(st, buf);
+  }
+  std::vector<Range> r((size_t)kRangesPerPhase * (size_t)st->n_phases);
+  return check_independent_in(st, r.data());
 }
 
 // Within one phase of a step, no output (tier bytes, lists, counts, y) shares a byte with
@@ -167,7 +189,7 @@ int validate_step(const spax_step* step, bool noalloc) {
     } else if (!step->ws || step->ws_bytes < need) {
       return fail(SPAX_ERR_WORKSPACE, "SPAX_STEP_BATCHED needs a workspace of %zu bytes", need);
     }
-    int st = check_independent(step);
+    int st = check_independent(step, noalloc);
     if (st) return st;
   }
   return SPAX_OK;
@@ -215,7 +237,7 @@ int spax_placement_order(const spax_layout* L, const uint8_t* tiers, int32_t n_t
     return fail(SPAX_ERR_NULL, "layout, tiers and order are required");
   if (!layout_ok(L)) return fail(SPAX_ERR_SHAPE, "layout not initialised by spax_layout_init");
   if (n_tokens < 0) return fail(SPAX_ERR_PARAM, "n_tokens %d < 0", n_tokens);
-  return placement_order(L, tiers, n_tokens, order);
+  return no_throw([&] { return placement_order(L, tiers, n_tokens, order); });
 }
 
 int spax_build_tiers(const uint16_t* x, int32_t d_in, const spax_tier_params* p, uint8_t* tier,
@@ -305,8 +327,10 @@ int spax_tiered_gemv_pinned(const spax_layout* L, const void* packed_host, const
     (void)hipGetLastError();
     return fail(SPAX_ERR_PARAM, "packed_host is not pinned host memory mapped for the device");
   }
-  return tiered_gemv_pinned(L, packed_host, attr.devicePointer, x, full_idx, approx_idx, counts,
-                            y, gap, transfer, ws, stats, stream);
+  return no_throw([&] {
+    return tiered_gemv_pinned(L, packed_host, attr.devicePointer, x, full_idx, approx_idx,
+                              counts, y, gap, transfer, ws, stats, stream);
+  });
 }
 
 size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases) {
@@ -323,16 +347,20 @@ size_t spax_step_workspace_bytes(const spax_phase* phases, int32_t n_phases) {
 
 int spax_decode_step_projections(const spax_step* step, hipStream_t stream) {
   clear_error();
-  int st = validate_step(step, false);
-  if (st) return st;
-  return launch_decode_step(step, stream, false);
+  return no_throw([&] {
+    int st = validate_step(step, false);
+    if (st) return st;
+    return launch_decode_step(step, stream, false);
+  });
 }
 
 int spax_decode_step_projections_noalloc(const spax_step* step, hipStream_t stream) {
   clear_error();
-  int st = validate_step(step, true);
-  if (st) return st;
-  return launch_decode_step(step, stream, true);
+  return no_throw([&] {
+    int st = validate_step(step, true);
+    if (st) return st;
+    return launch_decode_step(step, stream, true);
+  });
 }
 
 }  // extern "C"

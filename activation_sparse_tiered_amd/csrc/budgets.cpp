@@ -27,13 +27,8 @@ double compute_weighted(const double* f, const double* p, int n) {
   return num / den;
 }
 
-}  // namespace
-
-extern "C" {
-
-int spax_block_sparsity(const double* sens, int32_t n_blocks, double s, double lambda,
+int block_sparsity_impl(const double* sens, int32_t n_blocks, double s, double lambda,
                         double s_min, double s_max, double* s_block) {
-  clear_error();
   if (!sens || !s_block) return fail(SPAX_ERR_NULL, "sens and s_block are required");
   if (n_blocks < 1) return fail(SPAX_ERR_PARAM, "n_blocks %d < 1", n_blocks);
   if (!std::isfinite(s) || !std::isfinite(lambda) || !std::isfinite(s_min) ||
@@ -70,10 +65,9 @@ int spax_block_sparsity(const double* sens, int32_t n_blocks, double s, double l
   return SPAX_OK;
 }
 
-int spax_greedy_allocation(const double* params, int32_t n_mats, double alpha, double P_max,
+int greedy_allocation_impl(const double* params, int32_t n_mats, double alpha, double P_max,
                            spax_block_error_fn block_error, void* user, double* rows,
                            int32_t cap, int32_t* n_rows) {
-  clear_error();
   if (!params || !block_error || !n_rows) return fail(SPAX_ERR_NULL, "params, block_error and n_rows are required");
   if (n_mats < 1 || n_mats > 64) return fail(SPAX_ERR_PARAM, "n_mats %d outside 1..64", n_mats);
   if (!(alpha > 0) || !std::isfinite(alpha) || !std::isfinite(P_max) || P_max > 1.0)
@@ -129,6 +123,26 @@ int spax_greedy_allocation(const double* params, int32_t n_mats, double alpha, d
   if (count > cap)
     return fail(SPAX_ERR_WORKSPACE, "the walk recorded %d rows; rows holds %d", count, cap);
   return SPAX_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int spax_block_sparsity(const double* sens, int32_t n_blocks, double s, double lambda,
+                        double s_min, double s_max, double* s_block) {
+  clear_error();
+  return no_throw(
+      [&] { return block_sparsity_impl(sens, n_blocks, s, lambda, s_min, s_max, s_block); });
+}
+
+int spax_greedy_allocation(const double* params, int32_t n_mats, double alpha, double P_max,
+                           spax_block_error_fn block_error, void* user, double* rows,
+                           int32_t cap, int32_t* n_rows) {
+  clear_error();
+  return no_throw([&] {
+    return greedy_allocation_impl(params, n_mats, alpha, P_max, block_error, user, rows, cap,
+                                  n_rows);
+  });
 }
 
 int spax_allocation_at(const double* rows, int32_t n_rows, int32_t n_mats, double target,

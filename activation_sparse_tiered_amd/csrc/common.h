@@ -5,6 +5,8 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <exception>
+#include <new>
 
 #include "spax.h"
 
@@ -21,6 +23,22 @@ int hip_fail(hipError_t e, const char* what);
     hipError_t e_ = (expr);                                    \
     if (e_ != hipSuccess) return ::spax::hip_fail(e_, #expr);  \
   } while (0)
+
+// Runs f() (an entry point's body) and turns a C++ exception -- a host allocation or a host
+// thread that could not be obtained -- into SPAX_ERR_HOST, so that no exception crosses the
+// C ABI.
+template <class F>
+int no_throw(F&& f) noexcept {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return fail(SPAX_ERR_HOST, "host memory allocation failed");
+  } catch (const std::exception& e) {
+    return fail(SPAX_ERR_HOST, "host-side failure: %s", e.what());
+  } catch (...) {
+    return fail(SPAX_ERR_HOST, "host-side failure");
+  }
+}
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -183,6 +183,7 @@ const char* spax_status_string(int status) {
     case SPAX_ERR_WORKSPACE: return "SPAX_ERR_WORKSPACE";
     case SPAX_ERR_HIP: return "SPAX_ERR_HIP";
     case SPAX_ERR_UNSUPPORTED: return "SPAX_ERR_UNSUPPORTED";
+    case SPAX_ERR_HOST: return "SPAX_ERR_HOST";
     default: return "SPAX_ERR_UNKNOWN";
   }
 }

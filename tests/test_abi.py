@@ -456,3 +456,12 @@ def test_header_compiles_as_c():
                         f"-I{os.path.join(ROOT, 'include')}", src],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
+
+
+def test_status_strings_name_every_status():
+    lib = _lib.lib
+    lib.spax_status_string.restype = C.c_char_p
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.spax_status_string(code).decode() == name
+    assert _lib.STATUS_NAMES[_lib.SPAX_ERR_HOST] == "SPAX_ERR_HOST"
+    assert lib.spax_status_string(-99).decode() == "SPAX_ERR_UNKNOWN"
