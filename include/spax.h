@@ -430,12 +430,13 @@ int spax_decode_step_projections(const spax_step* step, hipStream_t stream);
  * spax_decode_step_projections without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation).  Same phases, flags, validation and results as spax_decode_step_projections;
- * step->ws and step->ws_bytes are ignored.  The only form that needs a workspace,
- * SPAX_STEP_BATCHED, keeps its descriptor tables in a static device array of the library
- * (256 KiB per GPU, held until the process ends; about 208 bytes per phase, so at most
- * 1257 phases, else SPAX_ERR_WORKSPACE), filled from a static host buffer by one copy on
- * `stream`.  The call makes no hipMalloc, hipHostMalloc or hipFree call (its first call on a
- * device looks up the array's address and creates one event).  Every call on one GPU shares
+ * step->ws and step->ws_bytes are ignored.  SPAX_STEP_BATCHED keeps its descriptor tables
+ * in a static device array of the library (256 KiB per GPU, held until the process ends;
+ * about 208 bytes per phase, so at most 1257 phases, else SPAX_ERR_WORKSPACE), filled from a
+ * static host buffer by one copy on `stream`; SPAX_STEP_DETERMINISTIC, whose partial sums
+ * need a workspace, is refused (SPAX_ERR_UNSUPPORTED).  The call makes no hipMalloc,
+ * hipHostMalloc or hipFree call and no host heap allocation (its first call on a device looks
+ * up the array's address and creates one event).  Every call on one GPU shares
  * that array: calls that overlap on one GPU (different streams, or host threads on one
  * device) race, so callers serialize them, e.g. on one stream.  A call waits on the host
  * until the previous call's table copy has left the host buffer.
