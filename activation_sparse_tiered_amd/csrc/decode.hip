@@ -156,6 +156,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     mask::KeyHist<kFusedThreads> kh;
     float red[kFusedWaves][kTileRows];
   } u;
+  static_assert(sizeof(float) * kFusedWaves * kTileRows <= sizeof(u.kh.fine),
+                "the reduction buffer must lie inside the per-key counters");
   uint32_t* xs32 = reinterpret_cast<uint32_t*>(dyn);
   const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(dyn);
 
@@ -273,7 +275,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     bF = nbF;
     bA = nbA;
   }
-  __syncthreads();  // every wave is done with the mask scratch that `red` overlays
+  // `red` overlays only the per-key counters, which no wave reads after select_finish's last
+  // barrier (the claim counters lie past them), so no barrier is needed before it is written.
   gemv::finish_tile<kFusedWaves>(u.red, acc, zsum, wave, lane, row0, T, sh.n_chunks, a.y,
                                  a.partials, chunk);
   clear_next(a);
