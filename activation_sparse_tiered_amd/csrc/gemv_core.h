@@ -187,10 +187,10 @@ struct Record {
 };
 
 // A block of up to 64 entries of a column list held in registers, one per lane: entry =
-// channel | (fp16 bits of x_j) << 16, for list positions [base, base + 64).  Loaded with one
-// vector load of the indices and one gather of the activations (load_blocks: two dependent
-// round trips per 64 columns instead of two per column); get() broadcasts one entry with
-// readlane.  Indices are clamped to [0, d_in), so malformed lists cannot address outside the
+// channel | (fp16 bits of x_j) << 16, for a wave's list positions [base, base + 64).  Loaded
+// with one vector load of the indices and one gather of the activations (load_index,
+// finish_blocks: two dependent round trips per 64 columns instead of two per column); get()
+// broadcasts one entry with readlane.  Indices are clamped to [0, d_in), so malformed lists cannot address outside the
 // blob.
 struct RegBlock {
   uint32_t e;
@@ -202,31 +202,33 @@ struct RegBlock {
   }
 };
 
-// The FULL and the APPROX block of one step of 64 list positions, [fi, fend) and [ai, aend),
-// with their loads overlapped: both index loads, then both activation gathers (two dependent
-// round trips for the pair instead of four).  The loads are unconditional: a lane past its
-// tier's end reads the tier's last entry (or entry 0 of an empty list, whose buffer still
-// holds d_in entries) and keeps a zero entry.  kCompact: the lists hold staging slot |
-// channel << 16 (pinned-host path) and the returned entry holds the slot and x of the
-// channel.
+// Strided list blocks (stand-alone and batched GEMV): a wave's list entries are
+// first + stride * p for p = 0, 1, ...; lane l of block p0 holds p = p0 + l.  The entry
+// indices are fixed before the counts are known, so a block's index loads can be issued
+// before (or with) the counts load; an entry index is clamped into the list's capacity
+// (d_in entries), so a lane past the wave's count reads a stale but in-bounds entry, which
+// finish_blocks drops.
+__device__ __forceinline__ uint32_t load_index(const void* __restrict__ idx, int first,
+                                               int stride, int p, uint32_t jmax) {
+  const int entry = min(first + stride * p, (int)jmax);  // < 2^31: stride * p <= 2^29
+  return load_global<uint32_t>(reinterpret_cast<const uint32_t*>(idx) + entry);
+}
+
+// The FULL and APPROX blocks from raw index words rF / rA: lanes below nf / na (wave-uniform,
+// may be <= 0) keep their entry and gather their activation; the others hold a zero entry.
+// kCompact: the words are staging slot | channel << 16.
 template <bool kCompact>
-__device__ __forceinline__ void load_blocks(const void* __restrict__ idxF,
-                                            const void* __restrict__ idxA,
-                                            const uint16_t* __restrict__ x16, int fi, int fend,
-                                            int ai, int aend, uint32_t jmax, RegBlock& bf,
-                                            RegBlock& ba) {
+__device__ __forceinline__ void finish_blocks(uint32_t rF, uint32_t rA,
+                                              const uint16_t* __restrict__ x16, int nf, int na,
+                                              uint32_t jmax, int p0, RegBlock& bf,
+                                              RegBlock& ba) {
   const int lane = threadIdx.x & 63;
-  const int iF = fi + lane, iA = ai + lane;
-  const uint32_t rF =
-      load_global<uint32_t>(reinterpret_cast<const uint32_t*>(idxF) + min(iF, max(fend - 1, 0)));
-  const uint32_t rA =
-      load_global<uint32_t>(reinterpret_cast<const uint32_t*>(idxA) + min(iA, max(aend - 1, 0)));
   const uint32_t jF = min(kCompact ? rF >> 16 : rF, jmax), jA = min(kCompact ? rA >> 16 : rA, jmax);
   const uint32_t sF = kCompact ? min(rF & 0xFFFFu, jmax) : jF;
   const uint32_t sA = kCompact ? min(rA & 0xFFFFu, jmax) : jA;
   const uint32_t xF = load_global<uint16_t>(x16 + jF), xA = load_global<uint16_t>(x16 + jA);
-  bf = RegBlock{iF < fend ? sF | (xF << 16) : 0u, fi};
-  ba = RegBlock{iA < aend ? sA | (xA << 16) : 0u, ai};
+  bf = RegBlock{lane < nf ? sF | (xF << 16) : 0u, p0};
+  ba = RegBlock{lane < na ? sA | (xA << 16) : 0u, p0};
 }
 
 // Column lists in LDS (fused kernel): entry = channel | (fp16 bits of x_j) << 16.  Up to 64
@@ -408,13 +410,6 @@ __device__ __forceinline__ int xcd_order(int b, int n) {
   return b < (n8 << 3) ? (b & 7) * n8 + (b >> 3) : b;
 }
 
-// Split [b, e) evenly over the workgroup's NW waves.
-template <int NW>
-__device__ __forceinline__ void wave_range(int b, int e, int wave, int& wb, int& we) {
-  wb = b + (e - b) * wave / NW;
-  we = b + (e - b) * (wave + 1) / NW;
-}
-
 // Reduce the NW waves' partial rows through LDS, then write (one chunk) or atomically add
 // (several chunks, y zeroed beforehand in stream order) the 64 RPL-row tile into y.  With
 // `partials` (deterministic mode, several chunks) the tile is stored as row block `chunk` of
@@ -458,9 +453,9 @@ struct ItemRows {
   static constexpr int unroll = kUnroll;
 };
 
-// One work item of the stand-alone GEMV: row tile `tile`, column chunk `chunk` of the lists
-// in global memory (counts and indices clamped to [0, d_in], so malformed lists cannot
-// address outside the blob).  kCompact: the lists hold slot | channel << 16 entries into a
+// One work item of the stand-alone (and batched) GEMV: row tile `tile`, column chunk `chunk`
+// of the lists in global memory -- the entries chunk, chunk + n_chunks, ... -- (counts and
+// indices clamped to [0, d_in], so malformed lists cannot address outside the blob).  kCompact: the lists hold slot | channel << 16 entries into a
 // compacted staging copy of the records (`packed` is then the staging buffer).  A workgroup
 // of kWaves waves; RPL rows per lane (a 64 RPL-row tile), U columns per round; ends after the
 // tile's atomics.  red: kWaves x 64 RPL floats.
@@ -480,28 +475,35 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
   // is always in bounds; their sums land in rows >= T and are never stored.  Every matrix
   // height is a multiple of 64, so a lane's rows are all inside or all past T.
   const int row = row0 + lane * RPL < T ? row0 + lane * RPL : 0;
+  const uint32_t jmax = (uint32_t)sh.d_in - 1u;
+  // Chunk c takes the list entries c, c + n_chunks, c + 2 n_chunks, ... and wave w of the
+  // workgroup every kWaves-th of those, so this wave's entries are first + stride * p.  The
+  // first block's index loads go out with the counts load; the counts only fix how many of
+  // the entries are valid.  Every chunk and every wave gets the same count within one.
+  const int stride = sh.n_chunks * kWaves;
+  const int first = chunk + sh.n_chunks * wave;
+  uint32_t rF = load_index(full_idx, first, stride, lane, jmax);
+  uint32_t rA = load_index(approx_idx, first, stride, lane, jmax);
   const int nF = uniform(min(max(load_global<int32_t>(counts), 0), sh.d_in));
   const int nA = uniform(min(max(load_global<int32_t>(counts + 1), 0), sh.d_in));
-  const uint32_t jmax = (uint32_t)sh.d_in - 1u;
-  const int fb = split_at(nF, chunk, sh.n_chunks);
-  const int fe = split_at(nF, chunk + 1, sh.n_chunks);
-  const int ab = split_at(nA, chunk, sh.n_chunks);
-  const int ae = split_at(nA, chunk + 1, sh.n_chunks);
-  int wfb, wfe, wab, wae;
-  wave_range<kWaves>(fb, fe, wave, wfb, wfe);
-  wave_range<kWaves>(ab, ae, wave, wab, wae);
+  const int cF = nF > first ? (nF - first + stride - 1) / stride : 0;  // this wave's entries
+  const int cA = nA > first ? (nA - first + stride - 1) / stride : 0;
   float acc[RPL];
 #pragma unroll
   for (int h = 0; h < RPL; ++h) acc[h] = 0.0f;
   float zsum = 0.0f;
   const uint16_t* x16 = reinterpret_cast<const uint16_t*>(x32);
   // 64 list entries per tier and block; the channels fit the 16-bit entry field (d_in <= 32768)
-  for (int fi = wfb, ai = wab; fi < wfe || ai < wae; fi += 64, ai += 64) {
-    const int fend = min(fi + 64, wfe), aend = min(ai + 64, wae);
+  for (int p0 = 0; p0 < cF || p0 < cA; p0 += 64) {
+    if (p0 > 0) {
+      rF = load_index(full_idx, first, stride, p0 + lane, jmax);
+      rA = load_index(approx_idx, first, stride, p0 + lane, jmax);
+    }
+    const int nf = min(cF - p0, 64), na = min(cA - p0, 64);  // may be <= 0
     RegBlock bf, ba;
-    load_blocks<kCompact>(full_idx, approx_idx, x16, fi, fend, ai, aend, jmax, bf, ba);
-    stream_columns<FMT, RPL, U>(sh, packed, row, fi, max(fi, fend), bf, ai, max(ai, aend), ba,
-                                acc, zsum);
+    finish_blocks<kCompact>(rF, rA, x16, nf, na, jmax, p0, bf, ba);
+    stream_columns<FMT, RPL, U>(sh, packed, row, p0, p0 + max(nf, 0), bf, p0, p0 + max(na, 0),
+                                ba, acc, zsum);
   }
   finish_tile<kWaves, RPL>(reinterpret_cast<float(*)[64 * RPL]>(red), acc, zsum, wave, lane,
                            row0, T, sh.n_chunks, y, partials, chunk);
