@@ -101,7 +101,7 @@ __device__ __forceinline__ GemvDesc uniform_desc(const GemvDesc& g) {
 
 // The work items of the phases whose base format is FMT (one launch per format present, so
 // each format gets its own register and LDS budget).
-template <int FMT>
+template <int FMT, class Blob>
 __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDesc* __restrict__ gd,
                                                                     int n_phases, int n_items) {
   __shared__ float red[gemv::kWaves * gemv::ItemRows<FMT>::tile];
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kGemvThreads) void batched_gemv_kernel(const GemvDe
     const int local = item - g.item0;
     const int tile = (int)((uint32_t)local % (uint32_t)g.sh.n_tiles);
     const int chunk = (int)((uint32_t)local / (uint32_t)g.sh.n_tiles);
-    gemv::gemv_item<FMT, false, gemv::ItemRows<FMT>::rpl, gemv::ItemRows<FMT>::unroll>(
+    gemv::gemv_item<FMT, Blob, false, gemv::ItemRows<FMT>::rpl, gemv::ItemRows<FMT>::unroll>(
         g.sh, g.packed, g.x32, g.full_idx, g.approx_idx, g.counts, g.y, tile, chunk, red);
     __syncthreads();  // red is reused by the next item
   }
@@ -189,6 +189,7 @@ int stage_and_copy(const void* src, size_t bytes, void* dst, hipStream_t s) {
 struct BatchItems {
   int32_t n_phases[2];  // phases per base format (their descriptors: fp16 first, then int4)
   int64_t items[2];     // work items per base format
+  bool narrow[2];       // every blob of that format has both regions below 2 GiB
 };
 
 // The descriptor tables of a batched step, written into `table` (table_bytes(n) bytes): the
@@ -200,7 +201,13 @@ bool build_tables(const spax_step* st, char* table, BatchItems* bi) {
   MaskDesc* md = reinterpret_cast<MaskDesc*>(table);
   GemvDesc* gd = reinterpret_cast<GemvDesc*>(table + aligned_size((size_t)n * sizeof(MaskDesc)));
   *bi = BatchItems{};
-  for (int i = 0; i < n; ++i) bi->n_phases[st->phases[i].layout->base_fmt == SPAX_FMT_INT4]++;
+  bi->narrow[0] = bi->narrow[1] = true;
+  for (int i = 0; i < n; ++i) {
+    const spax_layout* L = st->phases[i].layout;
+    const int f = L->base_fmt == SPAX_FMT_INT4;
+    bi->n_phases[f]++;
+    bi->narrow[f] = bi->narrow[f] && narrow_regions(L);
+  }
   int slot[2] = {0, bi->n_phases[0]};
   for (int i = 0; i < n; ++i) {
     const spax_phase& ph = st->phases[i];
@@ -237,12 +244,12 @@ bool build_tables(const spax_step* st, char* table, BatchItems* bi) {
   return true;
 }
 
-template <int FMT>
+template <int FMT, class Blob>
 int launch_gemvs(const GemvDesc* dgd, int n_phases, int64_t items, int n_cu, hipStream_t s) {
   // as many workgroups as can be resident at once
   static const int per_cu = [] {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, batched_gemv_kernel<FMT>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, batched_gemv_kernel<FMT, Blob>,
                                                      kGemvThreads, 0) != hipSuccess || occ < 1)
       occ = 2;
     return occ;
@@ -250,8 +257,8 @@ int launch_gemvs(const GemvDesc* dgd, int n_phases, int64_t items, int n_cu, hip
   const int64_t cap = (int64_t)n_cu * per_cu;
   const int64_t grid = items < cap ? items : cap;
   if (grid > 0) {
-    hipLaunchKernelGGL(batched_gemv_kernel<FMT>, dim3((unsigned)grid), dim3(kGemvThreads), 0, s,
-                       dgd, n_phases, (int)items);
+    hipLaunchKernelGGL((batched_gemv_kernel<FMT, Blob>), dim3((unsigned)grid), dim3(kGemvThreads),
+                       0, s, dgd, n_phases, (int)items);
     SPAX_HIP_CHECK(hipGetLastError());
   }
   return SPAX_OK;
@@ -275,9 +282,14 @@ int launch_from_tables(const spax_step* st, int n_cu, const void* dtables, const
     SPAX_HIP_CHECK(hipEventRecord(st->events[1], s));
     SPAX_HIP_CHECK(hipEventRecord(st->events[2], s));
   }
-  int rc = launch_gemvs<SPAX_FMT_FP16>(dgd, bi.n_phases[0], bi.items[0], n_cu, s);
+  const GemvDesc* dgd4 = dgd + bi.n_phases[0];
+  int rc = bi.narrow[0]
+               ? launch_gemvs<SPAX_FMT_FP16, gemv::RegionBlob>(dgd, bi.n_phases[0], bi.items[0], n_cu, s)
+               : launch_gemvs<SPAX_FMT_FP16, gemv::RecordBlob>(dgd, bi.n_phases[0], bi.items[0], n_cu, s);
   if (rc) return rc;
-  rc = launch_gemvs<SPAX_FMT_INT4>(dgd + bi.n_phases[0], bi.n_phases[1], bi.items[1], n_cu, s);
+  rc = bi.narrow[1]
+           ? launch_gemvs<SPAX_FMT_INT4, gemv::RegionBlob>(dgd4, bi.n_phases[1], bi.items[1], n_cu, s)
+           : launch_gemvs<SPAX_FMT_INT4, gemv::RecordBlob>(dgd4, bi.n_phases[1], bi.items[1], n_cu, s);
   if (rc) return rc;
   if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[four ? 3 : 1], s));
   return SPAX_OK;

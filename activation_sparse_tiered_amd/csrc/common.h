@@ -83,6 +83,14 @@ inline int batched_tile_rows(const spax_layout* L) {
 constexpr int kGemvThreads = SPAX_GEMV_THREADS;  // waves that share one tile, split the columns
 constexpr int64_t kMaxRowsTotal = (int64_t)1 << 24;  // largest d_out_total of a layout
 
+// Both regions of the layout's blob (FULL records, APPROX records) below 2 GiB: the GEMV kernels
+// then address a column record from one buffer descriptor per region with a 32-bit offset
+// (gemv::RegionBlob) instead of building a descriptor per record (gemv::RecordBlob).
+inline bool narrow_regions(const spax_layout* L) {
+  constexpr int64_t k2GiB = (int64_t)1 << 31;
+  return L->off_A < k2GiB && (int64_t)L->d_in * L->stride_A < k2GiB;
+}
+
 struct GemvPlan {
   int32_t n_tiles;   // ceil(d_out_total / tile rows)
   int32_t n_chunks;  // split-K factor over the selected column lists

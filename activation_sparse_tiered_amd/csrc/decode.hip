@@ -148,7 +148,7 @@ __device__ __forceinline__ int ties_between(const uint32_t* xs32, int begin, int
 // (Issuing each wave's first FULL columns as soon as the FULL boundary's coarse bin was known,
 // before the exact boundaries, measured 0.55% slower per token: the selection and the issue
 // lengthened every wave's path to the boundary search more than the early bytes saved.)
-template <int FMT, int MAXD>
+template <int FMT, int MAXD, class Blob>
 __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t dyn[];
   // The mask's scratch and the GEMV's cross-wave reduction are never live together.
@@ -261,9 +261,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   const uint32_t* lists = reinterpret_cast<const uint32_t*>(dyn + a.xs_bytes);
   const bool own_only = a.own_only != 0;
   const gemv::TileOffsets<FMT> g(sh, row);
+  const Blob blob(sh, a.packed);
   while (nf > 0 || na > 0) {
     gemv::RoundLoads<FMT> r;
-    gemv::issue_round<FMT>(sh, a.packed, g, gemv::LdsBlock(lists + bF, nf, jmax), 0, nf,
+    gemv::issue_round<FMT>(blob, g, gemv::LdsBlock(lists + bF, nf, jmax), 0, nf,
                            gemv::LdsBlock(lists + bA, na, jmax), 0, na, r);
     // the next claims overlap this round's loads
     int nbF = bF, nbA = bA;
@@ -450,10 +451,22 @@ int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
     const dim3 grid((unsigned)(plan.n_tiles * plan.n_chunks + 1));  // + the writer
     a.per_next = (a.n_next4 + (int32_t)grid.x - 1) / (int32_t)grid.x;
     const dim3 blk(kFusedThreads);
-    if (L->base_fmt == SPAX_FMT_FP16)
-      hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_FP16, kFusedMaxDin>), grid, blk, f.bytes, s, a);
-    else
-      hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_INT4, kFusedMaxDin>), grid, blk, f.bytes, s, a);
+    const bool fp16 = L->base_fmt == SPAX_FMT_FP16;
+    if (narrow_regions(L)) {
+      if (fp16)
+        hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_FP16, kFusedMaxDin, gemv::RegionBlob>),
+                           grid, blk, f.bytes, s, a);
+      else
+        hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_INT4, kFusedMaxDin, gemv::RegionBlob>),
+                           grid, blk, f.bytes, s, a);
+    } else {
+      if (fp16)
+        hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_FP16, kFusedMaxDin, gemv::RecordBlob>),
+                           grid, blk, f.bytes, s, a);
+      else
+        hipLaunchKernelGGL((fused_phase_kernel<SPAX_FMT_INT4, kFusedMaxDin, gemv::RecordBlob>),
+                           grid, blk, f.bytes, s, a);
+    }
     SPAX_HIP_CHECK(hipGetLastError());
     if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[2 * i + 1], s));
     if (a.partials) {

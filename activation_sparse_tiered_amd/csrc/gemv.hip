@@ -20,7 +20,7 @@ namespace {
 
 using gemv::kWaves;
 
-template <int FMT, bool kCompact>
+template <int FMT, bool kCompact, class Blob>
 __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
     gemv::Shape sh, const uint8_t* __restrict__ packed, const uint32_t* __restrict__ x32,
     const int32_t* __restrict__ full_idx, const int32_t* __restrict__ approx_idx,
@@ -29,8 +29,8 @@ __global__ __launch_bounds__(kGemvThreads) void tiered_gemv_kernel(
   const int item = gemv::xcd_order((int)blockIdx.x, (int)gridDim.x);
   const int tile = (int)((uint32_t)item % (uint32_t)sh.n_tiles);
   const int chunk = (int)((uint32_t)item / (uint32_t)sh.n_tiles);
-  gemv::gemv_item<FMT, kCompact>(sh, packed, x32, full_idx, approx_idx, counts, y, tile, chunk,
-                                 red, partials);
+  gemv::gemv_item<FMT, Blob, kCompact>(sh, packed, x32, full_idx, approx_idx, counts, y, tile,
+                                       chunk, red, partials);
 }
 
 // Deterministic mode: y[r] = sum over c = 0 .. n_chunks - 1, in that order, of
@@ -237,16 +237,22 @@ int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* p
   const dim3 grid((unsigned)(plan.n_tiles * plan.n_chunks));
   const auto* pk = static_cast<const uint8_t*>(packed);
   const auto* x32 = reinterpret_cast<const uint32_t*>(x);
-#define SPAX_GEMV_LAUNCH(F, C)                                                              \
-  hipLaunchKernelGGL((tiered_gemv_kernel<F, C>), grid, dim3(kGemvThreads), 0, s, sh, pk, x32, \
-                     full_idx, approx_idx, counts, y, partials)
+  // The compacted staging copy has the blob's layout (record slots in place of channels).
+  const bool narrow = narrow_regions(L);
+#define SPAX_GEMV_LAUNCH(F, C, B)                                                             \
+  hipLaunchKernelGGL((tiered_gemv_kernel<F, C, gemv::B>), grid, dim3(kGemvThreads), 0, s, sh, \
+                     pk, x32, full_idx, approx_idx, counts, y, partials)
+#define SPAX_GEMV_LAUNCH_FMT(F)                        \
+  if (compact && narrow) SPAX_GEMV_LAUNCH(F, true, RegionBlob);    \
+  else if (compact) SPAX_GEMV_LAUNCH(F, true, RecordBlob);         \
+  else if (narrow) SPAX_GEMV_LAUNCH(F, false, RegionBlob);         \
+  else SPAX_GEMV_LAUNCH(F, false, RecordBlob)
   if (L->base_fmt == SPAX_FMT_FP16) {
-    if (compact) SPAX_GEMV_LAUNCH(SPAX_FMT_FP16, true);
-    else SPAX_GEMV_LAUNCH(SPAX_FMT_FP16, false);
+    SPAX_GEMV_LAUNCH_FMT(SPAX_FMT_FP16);
   } else {
-    if (compact) SPAX_GEMV_LAUNCH(SPAX_FMT_INT4, true);
-    else SPAX_GEMV_LAUNCH(SPAX_FMT_INT4, false);
+    SPAX_GEMV_LAUNCH_FMT(SPAX_FMT_INT4);
   }
+#undef SPAX_GEMV_LAUNCH_FMT
 #undef SPAX_GEMV_LAUNCH
   SPAX_HIP_CHECK(hipGetLastError());
   if (partials) return launch_reduce_chunks(partials, plan.n_chunks, L->d_out_total, y, s);

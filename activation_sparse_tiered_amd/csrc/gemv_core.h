@@ -158,31 +158,65 @@ __device__ __forceinline__ T* uniform(T* p) {
 #define SPAX_NT_LOADS 1
 #endif
 
-// Loads from one column record through a buffer descriptor built on the record's (uniform)
-// base: the record base stays in scalar registers and the lane's byte offset, the same for
-// every column, is the only vector operand, so no 64-bit address is added per column and
-// load.  The descriptor's size is the record's, so a load past it reads zero.
-struct Record {
+// Loads from one column record: a buffer descriptor in scalar registers plus a scalar byte
+// offset, so the lane's byte offset inside the record, the same for every column, is the only
+// vector operand and no 64-bit address is formed per load.  A load past the descriptor's
+// size reads zero.
+struct Column {
   __amdgpu_buffer_rsrc_t r;
-  __device__ __forceinline__ Record(const uint8_t* base, int64_t bytes)
-      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
-                                            0x00020000)) {}
+  uint32_t so;
   // cache policy 2: non-temporal (weight codes are read once per token)
   __device__ __forceinline__ uint32_t stream32(uint32_t off) const {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, SPAX_NT_LOADS ? 2 : 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, (int)so, SPAX_NT_LOADS ? 2 : 0);
   }
   __device__ __forceinline__ uint32_t word(uint32_t off) const {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, (int)so, 0);
   }
   __device__ __forceinline__ uint2 stream64(uint32_t off) const {
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, SPAX_NT_LOADS ? 2 : 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, (int)so, SPAX_NT_LOADS ? 2 : 0);
     return make_uint2(v.x, v.y);
   }
   __device__ __forceinline__ uint4 stream128(uint32_t off) const {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SPAX_NT_LOADS ? 2 : 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, (int)so, SPAX_NT_LOADS ? 2 : 0);
     return make_uint4(v.x, v.y, v.z, v.w);
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Column records of a blob through one descriptor per region (the FULL records, then the
+// APPROX records): record j lies at scalar offset j * stride, one scalar multiply per column.
+// Only for blobs whose two regions are each below 2 GiB (narrow_regions on the host), so every
+// offset fits 32 bits.
+struct RegionBlob {
+  __amdgpu_buffer_rsrc_t rF, rA;
+  uint32_t sF, sA;
+  __device__ __forceinline__ RegionBlob(const Shape& sh, const uint8_t* packed)
+      : rF(buffer_rsrc(packed, sh.off_A)),
+        rA(buffer_rsrc(packed + sh.off_A, (int64_t)sh.d_in * sh.stride_A)),
+        sF((uint32_t)sh.stride_F),
+        sA((uint32_t)sh.stride_A) {}
+  __device__ __forceinline__ Column full(int j) const { return Column{rF, (uint32_t)j * sF}; }
+  __device__ __forceinline__ Column approx(int j) const { return Column{rA, (uint32_t)j * sA}; }
+};
+
+// Any blob size: a descriptor built per column record on its 64-bit base (five more scalar
+// instructions per column).
+struct RecordBlob {
+  const uint8_t* packed;
+  int64_t sF, sA, offA;
+  __device__ __forceinline__ RecordBlob(const Shape& sh, const uint8_t* p)
+      : packed(p), sF(sh.stride_F), sA(sh.stride_A), offA(sh.off_A) {}
+  __device__ __forceinline__ Column full(int j) const {
+    return Column{buffer_rsrc(packed + (int64_t)j * sF, sF), 0u};
+  }
+  __device__ __forceinline__ Column approx(int j) const {
+    return Column{buffer_rsrc(packed + offA + (int64_t)j * sA, sA), 0u};
   }
 };
 
@@ -281,14 +315,12 @@ struct RoundLoads {
 };
 
 // Issues the loads of FULL columns [fi, fi + nf) of srcF and APPROX columns [ai, ai + na) of
-// srcA (counts wave-uniform, at most U, may be <= 0).  Slots past a count keep zero data and
-// a zero activation.
-template <int FMT, int RPL = 8, int U = kUnroll, class SrcF, class SrcA>
-__device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __restrict__ packed,
-                                            const TileOffsets<FMT, RPL>& g, const SrcF& srcF,
-                                            int fi, int nf, const SrcA& srcA, int ai, int na,
-                                            RoundLoads<FMT, RPL, U>& r) {
-  const uint8_t* regionA = packed + sh.off_A;
+// srcA (counts wave-uniform, at most U, may be <= 0) from blob b (RegionBlob or RecordBlob).
+// Slots past a count keep zero data and a zero activation.
+template <int FMT, int RPL = 8, int U = kUnroll, class Blob, class SrcF, class SrcA>
+__device__ __forceinline__ void issue_round(const Blob& b, const TileOffsets<FMT, RPL>& g,
+                                            const SrcF& srcF, int fi, int nf, const SrcA& srcA,
+                                            int ai, int na, RoundLoads<FMT, RPL, U>& r) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     r.xf[u] = 0.0f;
@@ -302,7 +334,7 @@ __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __re
     if (u < nf) {
       int j;
       srcF.get(fi + u, j, r.xf[u]);
-      const Record rec(packed + (int64_t)j * sh.stride_F, sh.stride_F);
+      const Column rec = b.full(j);
       if (FMT == SPAX_FMT_FP16 || RPL == 32) {
         r.vf[u] = rec.stream128(g.loffF);
       } else {
@@ -316,7 +348,7 @@ __device__ __forceinline__ void issue_round(const Shape& sh, const uint8_t* __re
     if (u < na) {
       int j;
       srcA.get(ai + u, j, r.xa[u]);
-      const Record rec(regionA + (int64_t)j * sh.stride_A, sh.stride_A);
+      const Column rec = b.approx(j);
       if (RPL == 32) r.va[u] = rec.stream64(g.loffA);
       else r.ca[u] = rec.stream32(g.loffA);
       r.sa[u] = rec.word(g.szoffA);
@@ -375,17 +407,17 @@ __device__ __forceinline__ void finish_round(const RoundLoads<FMT, RPL, U>& r,
 // the previous round are still in flight and makes every load wait for all earlier ones.
 // `row` is the lane's first row (or 0 for lanes past the last row, which read valid memory
 // and are never stored).
-template <int FMT, int RPL = 8, int U = kUnroll, class SrcF, class SrcA>
-__device__ __forceinline__ void stream_columns(const Shape& sh, const uint8_t* __restrict__ packed,
-                                               int row, int fb, int fe, const SrcF& srcF, int ab,
-                                               int ae, const SrcA& srcA, float (&acc)[RPL],
+template <int FMT, int RPL = 8, int U = kUnroll, class Blob, class SrcF, class SrcA>
+__device__ __forceinline__ void stream_columns(const Shape& sh, const Blob& b, int row, int fb,
+                                               int fe, const SrcF& srcF, int ab, int ae,
+                                               const SrcA& srcA, float (&acc)[RPL],
                                                float& zsum) {
   const TileOffsets<FMT, RPL> g(sh, row);
   int fi = fb, ai = ab;
   while (fi < fe || ai < ae) {
     const int nf = min(fe - fi, U), na = min(ae - ai, U);  // may be <= 0
     RoundLoads<FMT, RPL, U> r;
-    issue_round<FMT, RPL, U>(sh, packed, g, srcF, fi, nf, srcA, ai, na, r);
+    issue_round<FMT, RPL, U>(b, g, srcF, fi, nf, srcA, ai, na, r);
     finish_round<FMT, RPL, U>(r, g, nf, na, acc, zsum);
     fi += max(nf, 0);
     ai += max(na, 0);
@@ -458,8 +490,8 @@ struct ItemRows {
 // indices clamped to [0, d_in], so malformed lists cannot address outside the blob).  kCompact: the lists hold slot | channel << 16 entries into a
 // compacted staging copy of the records (`packed` is then the staging buffer).  A workgroup
 // of kWaves waves; RPL rows per lane (a 64 RPL-row tile), U columns per round; ends after the
-// tile's atomics.  red: kWaves x 64 RPL floats.
-template <int FMT, bool kCompact = false, int RPL = 8, int U = kUnroll>
+// tile's atomics.  red: kWaves x 64 RPL floats.  Blob: RegionBlob or RecordBlob.
+template <int FMT, class Blob, bool kCompact = false, int RPL = 8, int U = kUnroll>
 __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __restrict__ packed,
                                           const uint32_t* __restrict__ x32,
                                           const int32_t* __restrict__ full_idx,
@@ -493,6 +525,7 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
   for (int h = 0; h < RPL; ++h) acc[h] = 0.0f;
   float zsum = 0.0f;
   const uint16_t* x16 = reinterpret_cast<const uint16_t*>(x32);
+  const Blob b(sh, packed);
   // 64 list entries per tier and block; the channels fit the 16-bit entry field (d_in <= 32768)
   for (int p0 = 0; p0 < cF || p0 < cA; p0 += 64) {
     if (p0 > 0) {
@@ -502,8 +535,8 @@ __device__ __forceinline__ void gemv_item(const Shape& sh, const uint8_t* __rest
     const int nf = min(cF - p0, 64), na = min(cA - p0, 64);  // may be <= 0
     RegBlock bf, ba;
     finish_blocks<kCompact>(rF, rA, x16, nf, na, jmax, p0, bf, ba);
-    stream_columns<FMT, RPL, U>(sh, packed, row, p0, p0 + max(nf, 0), bf, p0, p0 + max(na, 0),
-                                ba, acc, zsum);
+    stream_columns<FMT, RPL, U>(sh, b, row, p0, p0 + max(nf, 0), bf, p0, p0 + max(na, 0), ba,
+                                acc, zsum);
   }
   finish_tile<kWaves, RPL>(reinterpret_cast<float(*)[64 * RPL]>(red), acc, zsum, wave, lane,
                            row0, T, sh.n_chunks, y, partials, chunk);
