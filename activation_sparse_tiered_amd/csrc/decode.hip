@@ -189,6 +189,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   const int row0 = tile * kTileRows;
   const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
   const uint32_t jmax = (uint32_t)d - 1u;
+  const gemv::TileOffsets<FMT> g(sh, row);
 
   // ---- 1. boundaries
   mask::Select sel[2];
@@ -260,7 +261,6 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   }
   const uint32_t* lists = reinterpret_cast<const uint32_t*>(dyn + a.xs_bytes);
   const bool own_only = a.own_only != 0;
-  const gemv::TileOffsets<FMT> g(sh, row);
   const Blob blob(sh, a.packed);
   while (nf > 0 || na > 0) {
     gemv::RoundLoads<FMT> r;

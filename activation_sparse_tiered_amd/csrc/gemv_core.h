@@ -284,6 +284,11 @@ struct LdsBlock {
   }
 };
 
+// log2 of a group size (a power of two: 64 or 128 rows), so that a row's group is a shift
+// rather than a division by a runtime value (some forty instructions on the path to the first
+// column loads).
+__device__ __forceinline__ uint32_t log2_group(int32_t g) { return (uint32_t)__builtin_ctz((uint32_t)g); }
+
 // A lane's byte offsets inside a column record for its rows of the tile.
 template <int FMT, int RPL = 8>
 struct TileOffsets {
@@ -298,9 +303,9 @@ struct TileOffsets {
   __device__ __forceinline__ TileOffsets(const Shape& sh, int row)
       : loffA(RPL == 8 ? (((uint32_t)row / 4u) & ~3u) : (uint32_t)row / 4u),
         selA(spread_sel(((uint32_t)row / 4u) & 2u)),
-        szoffA((uint32_t)(sh.T / 4) + (uint32_t)(row / sh.approx_group) * 4u),
+        szoffA((uint32_t)sh.T / 4u + ((uint32_t)row >> log2_group(sh.approx_group)) * 4u),
         loffF(FMT == SPAX_FMT_FP16 ? (uint32_t)row * 2u : (uint32_t)row / 2u),
-        szoffF((uint32_t)(sh.T / 2) + (uint32_t)(row / sh.base_group) * 4u) {}
+        szoffF((uint32_t)sh.T / 2u + ((uint32_t)row >> log2_group(sh.base_group)) * 4u) {}
 };
 
 // The registers of one round: up to U FULL and U APPROX columns.  RPL 8: vf holds a fp16

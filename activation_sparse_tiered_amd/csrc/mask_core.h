@@ -70,6 +70,15 @@ __device__ __forceinline__ int wave_scan(int x) {
   return x;
 }
 
+// Inclusive prefix sum within each row of 16 lanes (row shifts only).
+__device__ __forceinline__ int row_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  return x;
+}
+
 // Sum over the 64 lanes, as a wave-uniform value.
 __device__ __forceinline__ int wave_sum(int x) {
   return __builtin_amdgcn_readlane(wave_scan(x), 63);
@@ -217,23 +226,30 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
 
 // The coarse bin cb (keys [32 cb, 32 cb + 32)) that holds the R-th largest key, R >= 1, and
 // the number of keys above it.  One wave, after select_begin; the result is wave-uniform.
+// Lane l sums bins 16 l .. 16 l + 15; a scan over the lanes and one ballot find the lane whose
+// bins hold rank R; then lanes 0..15 take that lane's bins, highest first, and a scan within
+// the row of 16 and one more ballot find the bin.
 template <int NT>
 __device__ __forceinline__ void coarse_find(const KeyHist<NT>& h, int R, int lane, int& cb,
                                             int& above) {
-  int local[16];
   const int4* c4 = reinterpret_cast<const int4*>(h.coarse) + 4 * lane;
+  int sum = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int4 v = c4[q];
-    local[4 * q] = v.x;
-    local[4 * q + 1] = v.y;
-    local[4 * q + 2] = v.z;
-    local[4 * q + 3] = v.w;
+    sum += v.x + v.y + v.z + v.w;
   }
-  cb = 0;
-  above = 0;
-  suffix_find<16>(local, R, 0, lane, &cb, &above);
-  cb = min(max(cb, 0), 1023);  // R <= d: always found
+  const int pre = wave_scan(sum);
+  const int run = __builtin_amdgcn_readlane(pre, 63) - pre;  // keys in the lanes above
+  const uint64_t hit = __ballot(run < R && run + sum >= R);  // one lane: R <= d
+  const int L = hit ? (int)__builtin_ctzll(hit) : 0;
+  const int runL = __builtin_amdgcn_readlane(run, L);
+  const int v = lane < 16 ? h.coarse[16 * L + 15 - lane] : 0;
+  const int cum = row_scan(v);  // lane i: bins 16 L + 15 - i .. 16 L + 15
+  const uint64_t in = __ballot(lane < 16 && runL + cum >= R);
+  const int i = in ? (int)__builtin_ctzll(in) : 15;
+  cb = 16 * L + 15 - i;
+  above = runL + __builtin_amdgcn_readlane(cum - v, i);
 }
 
 // Second part: waves 0 and 1 each find one boundary inside its coarse bin; every wave gets
