@@ -107,30 +107,64 @@ __device__ __forceinline__ int claim_entries(int (*q)[kFusedWaves], int t, int w
   return 0;
 }
 
-// How many of the two fp16 halves of an LDS word of x have key (bits & 0x7FFF) kb, where
-// kb2 = kb in both halves; only the first nv (0, 1 or 2) halves count.  XOR with kb2 leaves
-// a half zero exactly where the key equals kb (a key never has its top bit set).
-__device__ __forceinline__ int equal_halves(uint32_t wd, uint32_t kb2, int nv) {
-  const uint32_t t = (wd & 0x7FFF7FFFu) ^ kb2;
-  return (nv > 0 && (t & 0xFFFFu) == 0u ? 1 : 0) + (nv > 1 && t < 0x10000u ? 1 : 0);
+// Bit 15 of each half of the result set where that half of w (two fp16 activations) has key
+// (bits & 0x7FFF) kb, with kb2 = kb in both halves.  t = key ^ kb leaves a half zero exactly
+// where the key equals kb, and since both lie below 0x8000 a half h of t is zero exactly when
+// h - 1 (a packed 16-bit subtract: no borrow between the halves) has bit 15 set.
+__device__ __forceinline__ uint32_t equal_bits(uint32_t w, uint32_t kb2) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t t = (w & 0x7FFF7FFFu) ^ kb2;
+  const u16x2 one = {1, 1};
+  const uint32_t dm = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, t) - one);
+  return dm & ~t & 0x80008000u;
 }
 
-// Channels j in [begin, end) whose key is kb (begin even; eight keys per lane and LDS read).
-// One wave; the result is wave-uniform.
-__device__ __forceinline__ int ties_between(const uint32_t* xs32, int begin, int end, int kb,
-                                            int lane) {
-  const uint32_t kb2 = (uint32_t)kb * 0x10001u;
-  int c = 0;
+// Eight activations (a 16-byte LDS read): how many have key kb0 (bits 0..15 of the result)
+// and kb1 (bits 16..31).  keep: the halves that count (bit 15 of each).
+__device__ __forceinline__ uint32_t equal8(const uint4& v, uint32_t kb2_0, uint32_t kb2_1,
+                                           const uint4& keep) {
+  return (uint32_t)(__builtin_popcount(equal_bits(v.x, kb2_0) & keep.x) +
+                    __builtin_popcount(equal_bits(v.y, kb2_0) & keep.y) +
+                    __builtin_popcount(equal_bits(v.z, kb2_0) & keep.z) +
+                    __builtin_popcount(equal_bits(v.w, kb2_0) & keep.w)) +
+         ((uint32_t)(__builtin_popcount(equal_bits(v.x, kb2_1) & keep.x) +
+                     __builtin_popcount(equal_bits(v.y, kb2_1) & keep.y) +
+                     __builtin_popcount(equal_bits(v.z, kb2_1) & keep.z) +
+                     __builtin_popcount(equal_bits(v.w, kb2_1) & keep.w))
+          << 16);
+}
+
+// Channels j in [0, end) whose key is kb0, and those whose key is kb1 (eight keys per lane and
+// LDS read; whole 512-channel blocks read four at a time with no bounds, so four reads are
+// in flight).  One wave; the results are wave-uniform.
+__device__ __forceinline__ void ties_before(const uint32_t* xs32, int end, int kb0, int kb1,
+                                            int lane, int& t0, int& t1) {
+  const uint32_t k0 = (uint32_t)kb0 * 0x10001u, k1 = (uint32_t)kb1 * 0x10001u;
+  const uint4 all = make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u);
   const uint4* x4 = reinterpret_cast<const uint4*>(xs32);
-  for (int base = begin; base < end; base += 512) {
-    const int j = base + 8 * lane;
-    if (j < end) {
-      const uint4 v = x4[j >> 3];
-      c += equal_halves(v.x, kb2, end - j) + equal_halves(v.y, kb2, end - j - 2) +
-           equal_halves(v.z, kb2, end - j - 4) + equal_halves(v.w, kb2, end - j - 6);
-    }
+  const int full = end & ~511;
+  uint32_t c = 0;  // kb0 in bits 0..15, kb1 in 16..31: each count is at most 16384
+  int base = 0;
+  for (; base + 2048 <= full; base += 2048) {
+    uint4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = x4[(base >> 3) + 64 * q + lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c += equal8(v[q], k0, k1, all);
   }
-  return mask::wave_sum(c);
+  for (; base < full; base += 512) c += equal8(x4[(base >> 3) + lane], k0, k1, all);
+  const int j = base + 8 * lane;
+  if (j < end) {  // the last, partial block: only the first end - j halves count
+    const int n = end - j;
+    const uint4 keep = make_uint4((n > 0 ? 0x8000u : 0u) | (n > 1 ? 0x80000000u : 0u),
+                                  (n > 2 ? 0x8000u : 0u) | (n > 3 ? 0x80000000u : 0u),
+                                  (n > 4 ? 0x8000u : 0u) | (n > 5 ? 0x80000000u : 0u),
+                                  (n > 6 ? 0x8000u : 0u) | (n > 7 ? 0x80000000u : 0u));
+    c += equal8(x4[j >> 3], k0, k1, keep);
+  }
+  c = (uint32_t)mask::wave_sum((int)c);
+  t0 = (int)(c & 0xFFFFu);
+  t1 = (int)(c >> 16);
 }
 
 // One group: mask and GEMV.  Workgroup gridDim.x - 1 only writes the outputs of the mask
@@ -213,8 +247,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   }
   // Channels before ws at a split boundary key: counted by the few waves that hold such a
   // channel, each over x[0, ws) in LDS, so the others go on with no barrier.
-  int ties0 = need0 ? ties_between(xs32, 0, ws, s0.kb, lane) : 0;
-  int ties1 = need1 ? ties_between(xs32, 0, ws, s1.kb, lane) : 0;
+  int ties0 = 0, ties1 = 0;
+  if (need0 || need1) ties_before(xs32, ws, s0.kb, s1.kb, lane, ties0, ties1);
   int nF = 0, nA = 0;
   for (int j0 = ws; j0 < we; j0 += 64) {
     const int j = j0 + lane;
