@@ -49,6 +49,7 @@ struct FusedArgs {
   float4* y_next;    // cleared as a side job (NULL: none)
   int32_t n_next4;   // float4s of y_next
   int32_t per_next;  // float4s cleared per workgroup
+  int32_t n_spec;    // FULL columns per wave loaded before the mask is known (0..kUnroll)
   int32_t wave_cap;  // LDS list entries per wave and tier (>= its channels)
   int32_t xs_bytes;  // LDS bytes of the activations (lists follow)
 };
@@ -167,14 +168,29 @@ __device__ __forceinline__ void ties_before(const uint32_t* xs32, int end, int k
   t1 = (int)(c >> 16);
 }
 
+// Multiplies the speculatively loaded FULL fp16 columns of r whose slot bit is set in ok (the
+// others proved not to be FULL and are dropped unread).  Waits for every load first.
+template <int FMT>
+__device__ __forceinline__ void finish_spec(const gemv::RoundLoads<FMT>& r, uint32_t ok,
+                                            float (&acc)[8]) {
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int u = 0; u < gemv::kUnroll; ++u)
+    if ((ok >> u) & 1u) gemv::fma_fp16x8(acc, r.xf[u], r.vf[u]);
+}
+
 // One group: mask and GEMV.  Workgroup gridDim.x - 1 only writes the outputs of the mask
 // (tiers_to_global, as the stand-alone mask kernel).  Every other workgroup owns one
 // 512-row tile and one contiguous range of input channels, split over its 16 waves:
 //   1. the exact boundaries from a per-key histogram (select_begin / select_finish: one pass
 //      over the keys);
+//   1a. (fp16 bases) while the histogram is built, each wave already loads the FULL records
+//      of the n_spec largest keys among its first 64 channels (the memory system is otherwise
+//      idle until the boundaries are known); they are multiplied only once the mask confirms
+//      them FULL;
 //   2. each wave decides the tiers of its channels (ties at a boundary key by channel order,
 //      counting the equal keys before its first channel only when it holds such a tie) and
-//      lists its FULL and APPROX columns in LDS;
+//      lists its FULL and APPROX columns in LDS, leaving out the confirmed speculative ones;
 //   3. each wave streams its own list and then takes columns from the other waves' lists
 //      until all are done (claim_entries; in deterministic mode a wave keeps to its own
 //      list); the tile is reduced across waves and added to y (deterministic mode: stored
@@ -224,11 +240,39 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   const int row = row0 + lane * 8 < T ? row0 + lane * 8 : 0;
   const uint32_t jmax = (uint32_t)d - 1u;
   const gemv::TileOffsets<FMT> g(sh, row);
+  const Blob blob(sh, a.packed);
 
   // ---- 1. boundaries
   mask::Select sel[2];
   int E[2], R[2];
-  const bool search = mask::select_begin<kFusedThreads, MAXD>(u.kh, k, xs32, a.x, a.ta, R, sel, E);
+  // ---- 1a. speculative FULL columns: slot i holds channel ws + sl[i]
+  gemv::RoundLoads<FMT> r0;
+  int sl[gemv::kUnroll] = {};
+  int n_sp = 0;
+  uint64_t picked = 0;  // lanes of the first 64 channels whose column was loaded
+  auto speculate = [&]() {
+    if (FMT != SPAX_FMT_FP16 || a.n_spec <= 0 || ws >= we) return;
+    const int j = ws + lane;
+    int key = j < we ? (int)(xs16[j] & 0x7FFFu) : -1;
+#pragma unroll
+    for (int i = 0; i < gemv::kUnroll; ++i) {
+      sl[i] = 0;
+      r0.xf[i] = 0.0f;
+      if (i >= a.n_spec) continue;
+      const int m = mask::wave_max(key);
+      if (m < 0) continue;
+      const int l = (int)__builtin_ctzll(__ballot(key == m));
+      if (lane == l) key = -1;
+      sl[i] = l;
+      picked |= 1ull << l;
+      n_sp = i + 1;
+      const int jc = ws + l;
+      r0.xf[i] = gemv::half_lo((uint32_t)xs16[jc]);
+      r0.vf[i] = blob.full(jc).stream128(g.loffF);
+    }
+  };
+  const bool search =
+      mask::select_begin<kFusedThreads, MAXD>(u.kh, k, xs32, a.x, a.ta, R, sel, E, speculate);
   if (search) mask::select_finish<kFusedThreads>(u.kh, R, sel, E);
   const mask::Select s0 = sel[0], s1 = sel[1];
 
@@ -250,6 +294,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   int ties0 = 0, ties1 = 0;
   if (need0 || need1) ties_before(xs32, ws, s0.kb, s1.kb, lane, ties0, ties1);
   int nF = 0, nA = 0;
+  uint64_t spec_full = 0;  // lanes whose speculatively loaded column is FULL
   for (int j0 = ws; j0 < we; j0 += 64) {
     const int j = j0 + lane;
     const bool v = j < we;
@@ -257,19 +302,26 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     const int key = v ? (int)(raw & 0x7FFFu) : -1;
     const bool t0 = key == s0.kb, t1 = key == s1.kb;
     const uint64_t b0 = __ballot(t0), b1 = __ballot(t1);
-    const int r0 = ties0 + (int)mask::lanes_below(b0), r1 = ties1 + (int)mask::lanes_below(b1);
-    const bool full = key > s0.kb || (t0 && (!need0 || r0 < s0.m));
-    const bool kept = key > s1.kb || (t1 && (!need1 || r1 < s1.m));
+    const int rk0 = ties0 + (int)mask::lanes_below(b0), rk1 = ties1 + (int)mask::lanes_below(b1);
+    const bool full = key > s0.kb || (t0 && (!need0 || rk0 < s0.m));
+    const bool kept = key > s1.kb || (t1 && (!need1 || rk1 < s1.m));
     const bool apx = kept && !full;
+    const bool sp = j0 == ws && ((picked >> lane) & 1u);
+    if (j0 == ws) spec_full = __ballot(sp && full);
+    const bool listF = full && !sp;
     ties0 += mask::popc(b0);
     ties1 += mask::popc(b1);
     const uint32_t e = (uint32_t)j | (raw << 16);
-    const uint64_t bf = __ballot(full), ba = __ballot(apx);
-    if (full) lF[nF + (int)mask::lanes_below(bf)] = e;
+    const uint64_t bf = __ballot(listF), ba = __ballot(apx);
+    if (listF) lF[nF + (int)mask::lanes_below(bf)] = e;
     if (apx) lA[nA + (int)mask::lanes_below(ba)] = e;
     nF += mask::popc(bf);
     nA += mask::popc(ba);
   }
+  uint32_t spec_ok = 0;  // slots to multiply
+#pragma unroll
+  for (int i = 0; i < gemv::kUnroll; ++i)
+    if (i < n_sp && ((spec_full >> sl[i]) & 1u)) spec_ok |= 1u << i;
   wave_lds_fence();
 
   // ---- 3. stream, reduce
@@ -295,7 +347,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   }
   const uint32_t* lists = reinterpret_cast<const uint32_t*>(dyn + a.xs_bytes);
   const bool own_only = a.own_only != 0;
-  const Blob blob(sh, a.packed);
+  bool spec_pending = n_sp > 0;
   while (nf > 0 || na > 0) {
     gemv::RoundLoads<FMT> r;
     gemv::issue_round<FMT>(blob, g, gemv::LdsBlock(lists + bF, nf, jmax), 0, nf,
@@ -305,11 +357,16 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
     const int nf2 = claim_entries(u.kh.lists_q, 0, wave, S, lane, nbF, own_only);
     const int na2 = claim_entries(u.kh.lists_q, 1, wave, S, lane, nbA, own_only);
     gemv::finish_round<FMT>(r, g, nf, na, acc, zsum);
+    if (spec_pending) {  // landed long ago; multiplied after the first round's wait
+      finish_spec<FMT>(r0, spec_ok, acc);
+      spec_pending = false;
+    }
     nf = nf2;
     na = na2;
     bF = nbF;
     bA = nbA;
   }
+  if (spec_pending) finish_spec<FMT>(r0, spec_ok, acc);
   // `red` overlays only the per-key counters, which no wave reads after select_finish's last
   // barrier (the claim counters lie past them), so no barrier is needed before it is written.
   gemv::finish_tile<kFusedWaves>(u.red, acc, zsum, wave, lane, row0, T, sh.n_chunks, a.y,
@@ -358,6 +415,26 @@ GemvPlan fused_plan(const spax_layout* L) {
 // Dynamic LDS: the activations (d_in halves rounded up to whole dwords, in bytes, rounded
 // to 16), then for each wave a FULL and an APPROX list of wave_cap entries; wave_cap * 16 >=
 // the channels of one chunk.
+// Speculative FULL columns per wave: half the FULL channels the fewest a mask can select would
+// put among a wave's first 64 channels, at most kUnroll (so the largest keys there are almost
+// always FULL); none for threshold masks, whose boundaries need no search, and none for int4
+// bases, whose 4-byte code loads per lane save less time than choosing the columns costs
+// (measured 4.9% slower per token).
+int spec_columns(const TierArgs& ta, int wave_cap, int32_t base_fmt) {
+  if (base_fmt != SPAX_FMT_FP16) return 0;
+  int64_t fmin = 0;
+  if (ta.mode == SPAX_MODE_TOPK) {
+    fmin = ta.n_full;
+  } else if (ta.mode == SPAX_MODE_TOPK_GUIDED) {
+    const int64_t kept = (int64_t)ta.d - ta.n_hi;
+    fmin = kept - ((int64_t)ta.num * kept + ta.den / 2) / ta.den;
+  } else {
+    return 0;
+  }
+  const int64_t n = fmin * (wave_cap < 64 ? wave_cap : 64) / (2 * (int64_t)ta.d);
+  return n < 0 ? 0 : (n > gemv::kUnroll ? gemv::kUnroll : (int)n);
+}
+
 FusedLds fused_lds(const spax_layout* L, const GemvPlan& plan) {
   FusedLds f;
   const int range = (L->d_in + plan.n_chunks - 1) / plan.n_chunks;
@@ -482,6 +559,7 @@ int launch_decode_step(const spax_step* st, hipStream_t s, bool noalloc) {
     const FusedLds f = fused_lds(L, plan);
     a.wave_cap = f.wave_cap;
     a.xs_bytes = f.xs_bytes;
+    a.n_spec = spec_columns(ta, f.wave_cap, L->base_fmt);
     const dim3 grid((unsigned)(plan.n_tiles * plan.n_chunks + 1));  // + the writer
     a.per_next = (a.n_next4 + (int32_t)grid.x - 1) / (int32_t)grid.x;
     const dim3 blk(kFusedThreads);

@@ -59,6 +59,15 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 }
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
+// Workgroup barrier for LDS traffic: the fences order LDS operations only, so global loads
+// still in flight stay in flight (a plain __syncthreads() also waits for every one of them).
+// Every barrier of the mask code guards LDS data only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive prefix sum over the 64 lanes with DPP (row shifts, then row broadcasts); no LDS.
 __device__ __forceinline__ int wave_scan(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
@@ -77,6 +86,17 @@ __device__ __forceinline__ int row_scan(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
   x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
   return x;
+}
+
+// Largest value over the 64 lanes, as a wave-uniform value.
+__device__ __forceinline__ int wave_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x111, 0xF, 0xF, false));  // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x112, 0xF, 0xF, false));  // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x114, 0xF, 0xF, false));  // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x118, 0xF, 0xF, false));  // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
 }
 
 // Sum over the 64 lanes, as a wave-uniform value.
@@ -144,10 +164,16 @@ struct KeyHist {
 // every wave the two target ranks R (FULL, kept; counted from the largest key).  For
 // THRESHOLD the boundaries are the given keys: sel and E are set and false is returned.
 // Both histograms are complete on return (its last barrier follows the last atomic).
-template <int NT, int MAXD>
+// after_x(): called by every thread once x is in LDS, before the histogram pass (not for
+// THRESHOLD masks, whose boundaries are known at once).
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <int NT, int MAXD, class AfterX = NoHook>
 __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* xs32,
                                              const uint16_t* __restrict__ x, const TierArgs& a,
-                                             int (&R)[2], Select (&sel)[2], int (&E)[2]) {
+                                             int (&R)[2], Select (&sel)[2], int (&E)[2],
+                                             AfterX after_x = AfterX()) {
   constexpr int W = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,7 +207,7 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
     // after the mask passes are not made to wait for these conditional ones.
     __builtin_amdgcn_s_waitcnt(0);
   }
-  __syncthreads();
+  lds_barrier();
   if (thresholds) {
     sel[0] = Select{a.k_full, d};
     sel[1] = Select{a.k_skip, d};
@@ -189,6 +215,7 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
     R[0] = R[1] = 0;
     return false;
   }
+  after_x();
   int nat = 0;
   for (int s = 0; s < k.steps; ++s) {
     const uint32_t wd = k.word(s, lane);
@@ -207,7 +234,7 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
   }
   nat = wave_sum(nat);
   if (lane == 0) h.wave_nat[wave] = nat;
-  __syncthreads();
+  lds_barrier();
   if (a.mode == SPAX_MODE_TOPK) {
     R[0] = a.n_full;
     R[1] = a.n_full + a.n_approx;
@@ -280,7 +307,7 @@ __device__ __forceinline__ void select_finish(KeyHist<NT>& h, const int (&R)[2],
       h.E[b] = eb;
     }
   }
-  __syncthreads();
+  lds_barrier();
   sel[0] = h.sel[0];
   sel[1] = h.sel[1];
   E[0] = h.E[0];
@@ -397,7 +424,7 @@ __device__ __forceinline__ void tiers_to_global(KeyHist<NT>& h, uint32_t* xs32, 
     h.wave_cnt[wave][0] = (int)c0;
     h.wave_cnt[wave][1] = (int)c1;
   }
-  __syncthreads();
+  lds_barrier();
   // lane u < W holds wave u's counts; exclusive scans over the waves give the ties before
   // wave u, its FULL and kept counts, then its first list positions
   const uint32_t w0 = lane < W ? (uint32_t)h.wave_cnt[lane][0] : 0u;

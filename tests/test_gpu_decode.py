@@ -216,6 +216,28 @@ def test_step_ties(env, flags):
     check(run_step(env, specs, 808, flags=flags, xs=_tie_inputs(808)))
 
 
+@pytest.mark.parametrize("flags", [0, 4], ids=["fused", "deterministic"])
+def test_step_ties_speculative(env, flags):
+    """Ties at the boundaries in fp16 phases wide enough (12288 and 4096 rows: tens of channels
+    per wave) that the fused kernel loads each wave's largest-key FULL columns before the mask
+    is known: speculated columns that the mask then puts in APPROX or SKIP (a tie key past the
+    boundary's share, one key for every channel) must be dropped, and confirmed ones must not
+    be streamed twice."""
+    r = np.random.default_rng(4242)
+    x0 = r.laplace(0, 1, 4096).astype(np.float16)
+    x0[r.random(4096) < 0.6] = 0
+    x1 = r.choice(np.array([-2, -1, -0.5, -0.25, 0.25, 0.5, 1, 2], np.float16), 4096)
+    x2 = np.full(4096, 0.75, np.float16)
+    x2[::7] = -0.75
+    x3 = r.laplace(0, 1, 11008).astype(np.float16)
+    x3[r.random(11008) < 0.1] = 1.5
+    specs = [(4096, [4096, 4096, 4096], 0, 128, ("guided", 0.5, 0.01)),
+             (4096, [4096, 4096, 4096], 0, 128, ("topk", 0.3, 0.3)),
+             (4096, [4096, 4096, 4096], 0, 128, ("topk", 0.2, 0.3)),
+             (11008, [4096], 0, 128, ("guided", 0.5, 0.01))]
+    check(run_step(env, specs, 4242, flags=flags, xs={0: x0, 1: x1, 2: x2, 3: x3}))
+
+
 @pytest.mark.parametrize("flags", [0, 1, 2])
 def test_step_special_values(env, flags):
     """-0, subnormals, infinities and NaN order by their key; masks and lists stay exact
