@@ -250,10 +250,20 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
   int sl[gemv::kUnroll] = {};
   int n_sp = 0;
   uint64_t picked = 0;  // lanes of the first 64 channels whose column was loaded
+  // this lane's channel of the wave's first 64, read before the histogram pass (LDS reads
+  // after it would queue behind the atomics)
+  int key = -1;
+  uint32_t raw = 0;
+  auto spec_keys = [&]() {
+    if (FMT != SPAX_FMT_FP16 || a.n_spec <= 0) return;
+    const int j = ws + lane;
+    raw = j < we ? (uint32_t)xs16[j] : 0u;
+    key = j < we ? (int)(raw & 0x7FFFu) : -1;
+  };
+  // Chosen and issued once the wave's histogram atomics are issued: the LDS works through
+  // those meanwhile.
   auto speculate = [&]() {
     if (FMT != SPAX_FMT_FP16 || a.n_spec <= 0 || ws >= we) return;
-    const int j = ws + lane;
-    int key = j < we ? (int)(xs16[j] & 0x7FFFu) : -1;
 #pragma unroll
     for (int i = 0; i < gemv::kUnroll; ++i) {
       sl[i] = 0;
@@ -267,12 +277,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_phase_kernel(FusedArgs a)
       picked |= 1ull << l;
       n_sp = i + 1;
       const int jc = ws + l;
-      r0.xf[i] = gemv::half_lo((uint32_t)xs16[jc]);
+      r0.xf[i] = gemv::half_lo((uint32_t)__builtin_amdgcn_readlane((int)raw, l));
       r0.vf[i] = blob.full(jc).stream128(g.loffF);
     }
   };
   const bool search =
-      mask::select_begin<kFusedThreads, MAXD>(u.kh, k, xs32, a.x, a.ta, R, sel, E, speculate);
+      mask::select_begin<kFusedThreads, MAXD>(u.kh, k, xs32, a.x, a.ta, R, sel, E, spec_keys,
+                                              speculate);
   if (search) mask::select_finish<kFusedThreads>(u.kh, R, sel, E);
   const mask::Select s0 = sel[0], s1 = sel[1];
 

@@ -164,16 +164,18 @@ struct KeyHist {
 // every wave the two target ranks R (FULL, kept; counted from the largest key).  For
 // THRESHOLD the boundaries are the given keys: sel and E are set and false is returned.
 // Both histograms are complete on return (its last barrier follows the last atomic).
-// after_x(): called by every thread once x is in LDS, before the histogram pass (not for
-// THRESHOLD masks, whose boundaries are known at once).
+// after_x(): called by every thread once x is in LDS, before the histogram pass; after_hist():
+// once the thread has issued its histogram atomics, which the LDS then works through while the
+// thread goes on (neither is called for THRESHOLD masks, whose boundaries are known at once).
 struct NoHook {
   __device__ __forceinline__ void operator()() const {}
 };
-template <int NT, int MAXD, class AfterX = NoHook>
+template <int NT, int MAXD, class AfterX = NoHook, class AfterHist = NoHook>
 __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* xs32,
                                              const uint16_t* __restrict__ x, const TierArgs& a,
                                              int (&R)[2], Select (&sel)[2], int (&E)[2],
-                                             AfterX after_x = AfterX()) {
+                                             AfterX after_x = AfterX(),
+                                             AfterHist after_hist = AfterHist()) {
   constexpr int W = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -232,6 +234,7 @@ __device__ __forceinline__ bool select_begin(KeyHist<NT>& h, Keys& k, uint32_t* 
       nat += valid && key < a.k_tau;
     }
   }
+  after_hist();
   nat = wave_sum(nat);
   if (lane == 0) h.wave_nat[wave] = nat;
   lds_barrier();
