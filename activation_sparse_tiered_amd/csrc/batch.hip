@@ -283,13 +283,14 @@ int launch_from_tables(const spax_step* st, int n_cu, const void* dtables, const
     SPAX_HIP_CHECK(hipEventRecord(st->events[2], s));
   }
   const GemvDesc* dgd4 = dgd + bi.n_phases[0];
+  const int n16 = bi.n_phases[0], n4 = bi.n_phases[1];
   int rc = bi.narrow[0]
-               ? launch_gemvs<SPAX_FMT_FP16, gemv::RegionBlob>(dgd, bi.n_phases[0], bi.items[0], n_cu, s)
-               : launch_gemvs<SPAX_FMT_FP16, gemv::RecordBlob>(dgd, bi.n_phases[0], bi.items[0], n_cu, s);
+               ? launch_gemvs<SPAX_FMT_FP16, gemv::RegionBlob>(dgd, n16, bi.items[0], n_cu, s)
+               : launch_gemvs<SPAX_FMT_FP16, gemv::RecordBlob>(dgd, n16, bi.items[0], n_cu, s);
   if (rc) return rc;
   rc = bi.narrow[1]
-           ? launch_gemvs<SPAX_FMT_INT4, gemv::RegionBlob>(dgd4, bi.n_phases[1], bi.items[1], n_cu, s)
-           : launch_gemvs<SPAX_FMT_INT4, gemv::RecordBlob>(dgd4, bi.n_phases[1], bi.items[1], n_cu, s);
+           ? launch_gemvs<SPAX_FMT_INT4, gemv::RegionBlob>(dgd4, n4, bi.items[1], n_cu, s)
+           : launch_gemvs<SPAX_FMT_INT4, gemv::RecordBlob>(dgd4, n4, bi.items[1], n_cu, s);
   if (rc) return rc;
   if (st->events) SPAX_HIP_CHECK(hipEventRecord(st->events[four ? 3 : 1], s));
   return SPAX_OK;

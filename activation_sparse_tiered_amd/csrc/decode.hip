@@ -423,9 +423,6 @@ GemvPlan fused_plan(const spax_layout* L) {
   return p;
 }
 
-// Dynamic LDS: the activations (d_in halves rounded up to whole dwords, in bytes, rounded
-// to 16), then for each wave a FULL and an APPROX list of wave_cap entries; wave_cap * 16 >=
-// the channels of one chunk.
 // Speculative FULL columns per wave: half the FULL channels the fewest a mask can select would
 // put among a wave's first 64 channels, at most kUnroll (so the largest keys there are almost
 // always FULL); none for threshold masks, whose boundaries need no search, and none for int4
@@ -446,6 +443,9 @@ int spec_columns(const TierArgs& ta, int wave_cap, int32_t base_fmt) {
   return n < 0 ? 0 : (n > gemv::kUnroll ? gemv::kUnroll : (int)n);
 }
 
+// Dynamic LDS: the activations (d_in halves rounded up to whole dwords, in bytes, rounded
+// to 16), then for each wave a FULL and an APPROX list of wave_cap entries; wave_cap * 16 >=
+// the channels of one chunk.
 FusedLds fused_lds(const spax_layout* L, const GemvPlan& plan) {
   FusedLds f;
   const int range = (L->d_in + plan.n_chunks - 1) / plan.n_chunks;

@@ -242,7 +242,7 @@ int launch_tiered_gemv(const spax_layout* L, const GemvPlan& plan, const void* p
 #define SPAX_GEMV_LAUNCH(F, C, B)                                                             \
   hipLaunchKernelGGL((tiered_gemv_kernel<F, C, gemv::B>), grid, dim3(kGemvThreads), 0, s, sh, \
                      pk, x32, full_idx, approx_idx, counts, y, partials)
-#define SPAX_GEMV_LAUNCH_FMT(F)                        \
+#define SPAX_GEMV_LAUNCH_FMT(F)                                    \
   if (compact && narrow) SPAX_GEMV_LAUNCH(F, true, RegionBlob);    \
   else if (compact) SPAX_GEMV_LAUNCH(F, true, RecordBlob);         \
   else if (narrow) SPAX_GEMV_LAUNCH(F, false, RegionBlob);         \

@@ -160,8 +160,9 @@ __device__ __forceinline__ T* uniform(T* p) {
 
 // Loads from one column record: a buffer descriptor in scalar registers plus a scalar byte
 // offset, so the lane's byte offset inside the record, the same for every column, is the only
-// vector operand and no 64-bit address is formed per load.  A load past the descriptor's
-// size reads zero.
+// vector operand and no 64-bit address is formed per load.  Callers keep every offset inside
+// the record (lanes past a tile's last row read row 0), so no load relies on the hardware's
+// range check.
 struct Column {
   __amdgpu_buffer_rsrc_t r;
   uint32_t so;
@@ -491,9 +492,10 @@ struct ItemRows {
 };
 
 // One work item of the stand-alone (and batched) GEMV: row tile `tile`, column chunk `chunk`
-// of the lists in global memory -- the entries chunk, chunk + n_chunks, ... -- (counts and
-// indices clamped to [0, d_in], so malformed lists cannot address outside the blob).  kCompact: the lists hold slot | channel << 16 entries into a
-// compacted staging copy of the records (`packed` is then the staging buffer).  A workgroup
+// of the lists in global memory -- the entries chunk, chunk + n_chunks, ... -- (counts
+// clamped to [0, d_in] and channels to [0, d_in), so malformed lists cannot address outside
+// the blob).  kCompact: the lists hold slot | channel << 16 entries into a compacted
+// staging copy of the records (`packed` is then the staging buffer).  A workgroup
 // of kWaves waves; RPL rows per lane (a 64 RPL-row tile), U columns per round; ends after the
 // tile's atomics.  red: kWaves x 64 RPL floats.  Blob: RegionBlob or RecordBlob.
 template <int FMT, class Blob, bool kCompact = false, int RPL = 8, int U = kUnroll>
