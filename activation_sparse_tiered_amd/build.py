@@ -65,22 +65,21 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
-    write_buildinfo()
+    write_buildinfo(LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB
 
 
-BUILDINFO = LIB + ".buildinfo"
-
-
-def write_buildinfo() -> None:
-    """Record how the library was built (flags without include paths, compiler banner) next to
-    it, so that measurements can be tied to the build without running the compiler later."""
+def write_buildinfo(lib: str) -> None:
+    """Record how the library `lib` was built (flags without include paths, compiler banner) in
+    `lib`.buildinfo, so that measurements can be tied to the build without running the compiler
+    later.  The path follows the library actually written, so a build elsewhere leaves the
+    package's record alone."""
     r = subprocess.run([hipcc(), "--version"], capture_output=True, text=True)
     banner = " ".join(r.stdout.split())
     flags = " ".join(f for f in FLAGS if not f.startswith("-I"))
-    with open(BUILDINFO, "w") as fh:
+    with open(lib + ".buildinfo", "w") as fh:
         fh.write(f"flags: {flags}\ncompiler: {banner}\n")
 
 

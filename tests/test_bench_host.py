@@ -81,3 +81,26 @@ def test_comment_edits_leave_the_sources_hash_alone():
     assert strip(a) == strip(b) == strip(d)
     assert strip(a) != strip(c)
     assert '"/* kept */"' in strip(a)
+
+
+def test_build_record_follows_the_library_written(tmp_path):
+    """The flags and compiler that the traffic record is tied to are written next to the
+    library that a build produces, so building a copy elsewhere (other flags, other path)
+    leaves the package's record as it was."""
+    import importlib.util
+    import shutil
+    if not (shutil.which("hipcc") or os.path.exists("/opt/rocm/bin/hipcc")):
+        pytest.skip("hipcc not installed")
+    spec = importlib.util.spec_from_file_location(
+        "spax_build_copy", os.path.join(ROOT, "activation_sparse_tiered_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    pkg_record = b.LIB + ".buildinfo"
+    before = open(pkg_record).read() if os.path.exists(pkg_record) else None
+    b.FLAGS = b.FLAGS + ["-DSOME_OTHER_FLAG=1"]
+    lib = str(tmp_path / "copy.so")
+    b.write_buildinfo(lib)
+    text = open(lib + ".buildinfo").read()
+    assert "-DSOME_OTHER_FLAG=1" in text and "compiler:" in text
+    after = open(pkg_record).read() if os.path.exists(pkg_record) else None
+    assert after == before
