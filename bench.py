@@ -43,7 +43,9 @@ For linear512 and mlp7b ``cpu_baseline`` also holds a one-thread run of the orac
 ``dense_baseline`` (fp16 workloads) times the same step without tiers through torch's fp16
 matrix-vector product on the same weights, as context for the speedup over dense decoding.
 ``--fit`` (decode7b) adds ``fixed_cost_fit``: the layer-serial step at s = 0.3, 0.5 and 0.7 and
-the line t = a + b * MB per fused launch through them.
+the line t = a + b * MB per fused launch through them.  ``--tier-fit`` (decode workloads) adds
+``tier_fit``: the step with FULL-only and with APPROX-only masks at three sizes each, and per
+tier the line through the time against the bytes, so the cost of each tier's bytes shows apart.
 """
 
 from __future__ import annotations
@@ -92,6 +94,10 @@ def parse():
     ap.add_argument("--fit", action="store_true",
                     help="decode7b: also time the layer-serial step at s = 0.3, 0.5 and 0.7 and "
                          "fit the per-launch time against the bytes per launch")
+    ap.add_argument("--tier-fit", action="store_true",
+                    help="decode workloads: also time the step with FULL-only and APPROX-only "
+                         "masks at three sizes each and fit the time against the bytes, per "
+                         "tier (layer-serial and, unless --no-batched, batched form)")
     ap.add_argument("--no-deterministic", action="store_true",
                     help="skip timing the SPAX_STEP_DETERMINISTIC form")
     ap.add_argument("--no-read-probe", action="store_true",
@@ -533,6 +539,60 @@ def fixed_cost_fit(spax, torch, dev, args, main_point):
                     "launch over the three skip targets"}
 
 
+# One tier at a time: TopK masks that select only FULL columns, or only APPROX columns, for
+# these fractions of the channels (the rest skipped).
+TIER_FIT_POINTS = (("FULL", ((0.1, 0.0), (0.3, 0.0), (0.6, 0.0))),
+                   ("APPROX", ((0.0, 0.2), (0.0, 0.4), (0.0, 0.7))))
+
+
+def _line(xs, ys):
+    b, a = np.polyfit(np.array(xs), np.array(ys), 1)
+    return float(a), float(b)
+
+
+def tier_fit(spax, torch, dev, args, spec):
+    """The workload's step with one tier only, at three sizes per tier, and per tier the
+    least-squares lines t = a + b * MB per fused launch (layer-serial form) and, unless
+    --no-batched, t = a + b * GB per step (batched form): what each tier's bytes cost at the
+    margin.  Bytes are the algorithmic ones, from the device counts of every token."""
+    out = {}
+    for tier, pts in TIER_FIT_POINTS:
+        rows = []
+        for f, a in pts:
+            stack = Stack(spax, torch, dev, spec["layers"], args.tokens,
+                          spec=dict(spec, tiers=("topk", f, a)))
+            n = len(stack.layouts)
+            ls_ms = time_form(stack, 0, args)
+            bt_ms = None if args.no_batched else time_form(stack, spax.STEP_BATCHED, args)
+            step_bytes = 0.0
+            for t in range(stack.tokens):
+                _, counts = stack.timed_kernels(t)
+                step_bytes += sum(stack.algorithmic_bytes(i, c) for i, c in enumerate(counts))
+            step_bytes /= stack.tokens
+            del stack
+            torch.cuda.empty_cache()
+            row = {"full": f, "approx": a, "us_per_launch": round(ls_ms * 1e3 / n, 3),
+                   "MB_per_launch": round(step_bytes / n / 1e6, 3),
+                   "GB_per_step": round(step_bytes / 1e9, 4)}
+            if bt_ms is not None:
+                row["batched_us_per_step"] = round(bt_ms * 1e3, 1)
+            log(f"[bench] tier fit {tier} {row}")
+            rows.append(row)
+        a0, b = _line([r["MB_per_launch"] for r in rows], [r["us_per_launch"] for r in rows])
+        entry = {"points": rows,
+                 "layer_serial": {"intercept_us": round(a0, 3), "slope_us_per_MB": round(b, 5),
+                                  "marginal_TBps": round(1.0 / b, 3) if b > 0 else None}}
+        if not args.no_batched:
+            a1, b1 = _line([r["GB_per_step"] for r in rows],
+                           [r["batched_us_per_step"] for r in rows])
+            entry["batched"] = {"intercept_us": round(a1, 1), "slope_us_per_GB": round(b1, 2),
+                                "marginal_TBps": round(1e3 / b1, 3) if b1 > 0 else None}
+        out[tier] = entry
+    out["what"] = ("the step with FULL-only or APPROX-only TopK masks: per tier, time against "
+                   "algorithmic bytes (MB per fused launch, layer-serial; GB per step, batched)")
+    return out
+
+
 def device_bench(args, spax, torch, dev):
     spec = workload_spec(args)
     per_tok = spec["tokens_per_step"]
@@ -685,6 +745,10 @@ def device_bench(args, spax, torch, dev):
         fit = fixed_cost_fit(spax, torch, dev, args, (avg_launch_ms * 1e3, avg_bytes / 1e6))
         log(f"[bench] fixed-cost fit {fit}")
 
+    tfit = None
+    if args.tier_fit and args.workload in ("decode7b", "decode7b-int4") and args.control == "none":
+        tfit = tier_fit(spax, torch, dev, args, spec)
+
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(stack, spec["cpu_layers"])
         if args.workload in ("linear512", "mlp7b"):
@@ -733,6 +797,7 @@ def device_bench(args, spax, torch, dev):
         "dense_baseline": dense,
         "storage_4KiB": storage,
         "fixed_cost_fit": fit,
+        "tier_fit": tfit,
     }
 
 

@@ -104,3 +104,16 @@ def test_build_record_follows_the_library_written(tmp_path):
     assert "-DSOME_OTHER_FLAG=1" in text and "compiler:" in text
     after = open(pkg_record).read() if os.path.exists(pkg_record) else None
     assert after == before
+
+
+def test_tier_fit_points_select_one_tier_each():
+    """--tier-fit times masks that select one tier only, at three sizes per tier, and fits a
+    line through each tier's points."""
+    assert args_for("--tier-fit").tier_fit and not args_for().tier_fit
+    tiers = dict(bench.TIER_FIT_POINTS)
+    assert set(tiers) == {"FULL", "APPROX"}
+    assert all(a == 0.0 and 0.0 < f < 1.0 for f, a in tiers["FULL"])
+    assert all(f == 0.0 and 0.0 < a < 1.0 for f, a in tiers["APPROX"])
+    assert all(len(set(p)) == 3 for p in tiers.values())
+    a, b = bench._line([1.0, 2.0, 4.0], [7.0, 7.5, 8.5])
+    assert abs(a - 6.5) < 1e-9 and abs(b - 0.5) < 1e-9
