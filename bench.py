@@ -161,6 +161,7 @@ def workload_spec(args):
         spec["desc"] += f"; CONTROL: all channels {args.control.upper()} (TopK " + \
             ("d/0/0)" if args.control == "full" else "0/0/d)")
     if args.layers is not None:
+        spec["desc"] = spec["desc"].replace(f"{spec['layers']} layers", f"{args.layers} layers", 1)
         spec["layers"] = args.layers
         if args.workload == "mlp7b":
             spec["tokens_per_step"] = args.layers

@@ -117,3 +117,11 @@ def test_tier_fit_points_select_one_tier_each():
     assert all(len(set(p)) == 3 for p in tiers.values())
     a, b = bench._line([1.0, 2.0, 4.0], [7.0, 7.5, 8.5])
     assert abs(a - 6.5) < 1e-9 and abs(b - 0.5) < 1e-9
+
+
+def test_layers_override_is_named_in_the_workload():
+    spec = bench.workload_spec(args_for("--layers", "4"))
+    assert spec["layers"] == 4 and spec["desc"].startswith("decode7b: 4 layers")
+    spec = bench.workload_spec(args_for("--workload", "decode7b-int4", "--layers", "3"))
+    assert spec["layers"] == 3 and "3 layers" in spec["desc"] and "32 layers" not in spec["desc"]
+    assert "32 layers" in bench.workload_spec(args_for())["desc"]
