@@ -51,3 +51,27 @@ def test_bench_json_line(workload):
     assert cpu["unit"] == "us/token" and cpu["sample"]
 
     assert j["batched"] is not None and j["batched"]["value"] > 0
+
+
+def test_bench_tier_fit():
+    """--tier-fit at two layers: three FULL-only and three APPROX-only points per tier, the
+    bytes growing with the fraction of channels selected, and a finite line per tier for both
+    the layer-serial and the batched form."""
+    cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--layers", "2", "--tokens", "2",
+           "--steps", "2", "--warmup", "1", "--tier-fit", "--no-cpu-baseline", "--no-dense",
+           "--no-read-probe", "--no-separate", "--no-deterministic"]
+    print("bench:", " ".join(cmd[2:]), flush=True)
+    r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    tf = json.loads(r.stdout.strip().splitlines()[-1])["tier_fit"]
+    for tier, col in (("FULL", "full"), ("APPROX", "approx")):
+        pts = tf[tier]["points"]
+        assert len(pts) == 3
+        assert all(p[col] > 0 and p["approx" if col == "full" else "full"] == 0 for p in pts)
+        mb = [p["MB_per_launch"] for p in pts]
+        assert mb == sorted(mb) and mb[0] > 0
+        assert all(p["us_per_launch"] > 0 and p["batched_us_per_step"] > 0 for p in pts)
+        for form in ("layer_serial", "batched"):
+            line = tf[tier][form]
+            assert all(isinstance(v, float) and v == v for k, v in line.items()
+                       if k != "marginal_TBps"), line
