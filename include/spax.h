@@ -47,7 +47,7 @@ typedef enum spax_status {
   SPAX_ERR_ALIGN = -4,       /* a pointer is not aligned as required                 */
   SPAX_ERR_WORKSPACE = -5,   /* workspace too small                                  */
   SPAX_ERR_HIP = -6,         /* a HIP runtime call failed (message has the details)  */
-  SPAX_ERR_UNSUPPORTED = -7, /* valid request this build does not implement          */
+  SPAX_ERR_UNSUPPORTED = -7, /* valid request the library does not implement         */
   SPAX_ERR_HOST = -8         /* host memory or a host thread could not be obtained   */
 } spax_status;
 
