@@ -9,7 +9,9 @@
 // from a per-key histogram (mask_core.h, select_begin / select_finish), decides the tiers of
 // its own range of input channels, lists those columns in LDS (channel | fp16 x_j << 16 per
 // entry, one list per wave and tier, shared out among the waves) and streams them for its
-// 512-row tile (gemv_core.h).  One extra workgroup writes the tier bytes, the ascending
+// 512-row tile (gemv_core.h).  With fp16 bases each wave also loads the FULL records of its
+// largest-key channels while the histogram is being built, and multiplies them only if the
+// mask makes them FULL.  One extra workgroup writes the tier bytes, the ascending
 // lists and the counts with the rank-producing mask code, so the outputs equal
 // those of spax_build_tiers.  Repeating the boundary search in every workgroup costs no time
 // (it runs in parallel on separate compute units) and removes the second launch and the
